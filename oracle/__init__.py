@@ -1,0 +1,10 @@
+"""CPU oracle for the fused AWQ W4A16 linear (test infrastructure only).
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The HIP library and its Python binding never do.
+"""
+from .awq_ref import (  # noqa: F401
+    AWQ_ORDER, AWQ_REVERSE, AwqFormatError, resolve_groups, validate_pack,
+    pack_awq, unpack_awq, unpack_awq_gather, dequant_ref, dequant_ref_T,
+    gemm_ref, gemm_ref_entries, fp16_rne,
+)

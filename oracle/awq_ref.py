@@ -1,0 +1,236 @@
+"""Plain CPU oracle for the fused AWQ W4A16 linear  y = x . dequant(W) + bias.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this module.  The HIP library
+never imports, links or calls it, and it shares no code, table or helper with
+the HIP sources: the two sides meet only through the seeded input generator,
+which holds none of the method's arithmetic.
+
+Everything here is deliberately slow and literal: numpy integer ops for the
+bit work, float32 for the dequantised weights (where the product is exact, see
+`dequant_ref`) and float64 for the matrix product.
+
+Sources (cited by page and section):
+  [AWQ-SPEC]  tensref.org "AWQ" format page: the "Reader" pseudo-code
+              (unpack with the order map, zero/scale row k // group_size,
+              dequant (code - zero) * scale) and the "Reject the file when"
+              rules AWQ-004 (order map, not sequential nibbles) and AWQ-005
+              (stored zero is subtracted as is, no +1).
+  [GPTQM]     GPTQModel wiki "AWQ": section "Saved formats and packing"
+              (GEMM shapes qweight [K, N/8], qzeros [K/G, N/8], scales [K/G, N];
+              the INT4 order and reverse-order constants; INT4 packing rejects
+              N not divisible by 8), section "Group quantization and zero
+              points" (group_size -1 is one group across the row; GEMM
+              dequant is (code - zero) * scale).
+  [VLLM]      rkmt.cn article on vLLM's AWQ loading, sections 5.1 (reverse
+              pack order [0,4,1,5,2,6,3,7]) and 5.3 (kernels unpack with
+              (w >> shift) & 0xF, then (w - z) * s, before the matmul).
+
+Readings where the pages are silent (each is listed in the design notes):
+  * group_size == -1 means G = 1 (one group spanning all K rows).
+  * N % 8 != 0 and K % group_size != 0 are rejected, never truncated.
+  * A stored int32 word may be negative; the nibbles are its two's-complement
+    bits, extracted as if the word were unsigned.
+  * Bias is added in float64 to the float64 product (one final rounding if the
+    caller rounds to fp16).
+
+Pins: every function here is pinned in tests/test_oracle.py against facts that
+do not come from this file (a hand-built word, bijectivity, exact rational
+arithmetic, closed-form special cases).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Nibble i of a packed word holds column 8*c + AWQ_ORDER[i]   ([AWQ-SPEC] Reader;
+# [GPTQM] "Saved formats and packing").
+AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+# Column j of a word sits at nibble AWQ_REVERSE[j]   ([GPTQM] same section; [VLLM] 5.1).
+AWQ_REVERSE = (0, 4, 1, 5, 2, 6, 3, 7)
+
+
+class AwqFormatError(ValueError):
+    """A tensor set that the GEMM-format rules reject."""
+
+
+def resolve_groups(K: int, group_size: int) -> tuple[int, int]:
+    """Return (g, G): the effective group length and the number of groups.
+
+    [GPTQM] "Group quantization and zero points": -1 is one group across the
+    whole input row, so g = K and G = 1.  A positive g must divide K (reading:
+    incompatible dimensions are rejected rather than padded).
+    """
+    if group_size == -1:
+        return K, 1
+    if group_size <= 0:
+        raise AwqFormatError(f"group_size must be -1 or positive, got {group_size}")
+    if K % group_size != 0:
+        raise AwqFormatError(f"K={K} is not a multiple of group_size={group_size}")
+    return group_size, K // group_size
+
+
+def validate_pack(K, N, group_size, qweight_shape, qzeros_shape, scales_shape, bias_len=None):
+    """Format rules of the GEMM pack ([GPTQM] "Saved formats and packing"; [AWQ-SPEC]).
+
+    qweight int32 [K, N/8], qzeros int32 [G, N/8], scales [G, N], bias [N] or absent.
+    Raises AwqFormatError on any mismatch.
+    """
+    if K < 1 or N < 1:
+        raise AwqFormatError("K and N must be positive")
+    if N % 8 != 0:
+        raise AwqFormatError(f"N={N} is not a multiple of 8")
+    _, G = resolve_groups(K, group_size)
+    if tuple(qweight_shape) != (K, N // 8):
+        raise AwqFormatError(f"qweight shape {tuple(qweight_shape)} != {(K, N // 8)}")
+    if tuple(qzeros_shape) != (G, N // 8):
+        raise AwqFormatError(f"qzeros shape {tuple(qzeros_shape)} != {(G, N // 8)}")
+    if tuple(scales_shape) != (G, N):
+        raise AwqFormatError(f"scales shape {tuple(scales_shape)} != {(G, N)}")
+    if bias_len is not None and bias_len != N:
+        raise AwqFormatError(f"bias length {bias_len} != N={N}")
+
+
+def pack_awq(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes [R, N] (values 0..15) into int32 words [R, N/8].
+
+    Writer side of the reader in [AWQ-SPEC]: the code of column 8c + ORDER[i]
+    goes to bits 4i..4i+3 of word c.  Built in uint32 so the top nibble can
+    set the sign bit, then reinterpreted as int32 (the stored container).
+    """
+    codes = np.asarray(codes)
+    if codes.ndim != 2:
+        raise AwqFormatError("codes must be 2-D")
+    R, N = codes.shape
+    if N % 8 != 0:
+        raise AwqFormatError(f"N={N} is not a multiple of 8")
+    if codes.size and (codes.min() < 0 or codes.max() > 15):
+        raise AwqFormatError("codes must lie in 0..15")
+    c = codes.astype(np.uint32)
+    words = np.zeros((R, N // 8), dtype=np.uint32)
+    for col in range(N // 8):
+        for i in range(8):
+            words[:, col] |= c[:, col * 8 + AWQ_ORDER[i]] << np.uint32(4 * i)
+    return words.view(np.int32)
+
+
+def unpack_awq(words: np.ndarray) -> np.ndarray:
+    """Unpack int32 words [R, C] into codes [R, 8C], following [AWQ-SPEC]'s reader.
+
+    For each word column c and nibble i: column c*8 + ORDER[i] receives
+    (word >> 4i) & 0xF.  The shift is done on the unsigned view so that a
+    negative word yields the same nibbles as its bit pattern says.
+    """
+    u = np.asarray(words).view(np.uint32) if np.asarray(words).dtype == np.int32 \
+        else np.asarray(words, dtype=np.int64).astype(np.uint32)
+    R, C = u.shape
+    out = np.empty((R, 8 * C), dtype=np.int32)
+    for col in range(C):
+        for i in range(8):
+            out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int32)
+    return out
+
+
+def unpack_awq_gather(words: np.ndarray) -> np.ndarray:
+    """Second, independent formulation of unpack: gather by output column.
+
+    Column j reads word j // 8 at nibble REVERSE[j % 8]  ([GPTQM] reverse
+    order constant; [VLLM] 5.1/5.3).  Uses Python integers per element: no
+    shared loop structure with `unpack_awq`.
+    """
+    w = np.asarray(words)
+    R, C = w.shape
+    out = np.empty((R, 8 * C), dtype=np.int32)
+    for r in range(R):
+        for j in range(8 * C):
+            word = int(w[r, j // 8]) & 0xFFFFFFFF
+            out[r, j] = (word >> (4 * AWQ_REVERSE[j % 8])) & 0xF
+    return out
+
+
+def dequant_ref(qweight, qzeros, scales, group_size) -> np.ndarray:
+    """Dequantised weight W [K, N] in float32:  W[k, n] = (q[k,n] - z[k//g, n]) * s[k//g, n].
+
+    [AWQ-SPEC] Reader (dequant along in_features, group row k // group_size)
+    and rule AWQ-005 (the stored zero is subtracted unchanged).
+    (q - z) is an integer in [-15, 15] (at most 4 significant bits) and s is
+    fp16 (11 significant bits), so the float32 product is exact: every
+    evaluation order gives these same bits.
+    Orientation [K, N] matches y = x . W; `dequant_ref_T` gives the page's [N, K].
+    """
+    q = unpack_awq(qweight)
+    K, N = q.shape
+    g, G = resolve_groups(K, group_size)
+    z = unpack_awq(qzeros)
+    s = np.asarray(scales)
+    if z.shape != (G, N) or s.shape != (G, N):
+        raise AwqFormatError("qzeros/scales shapes do not match K, N, group_size")
+    out = np.empty((K, N), dtype=np.float32)
+    for k in range(K):
+        gi = k // g
+        out[k, :] = (q[k].astype(np.float32) - z[gi].astype(np.float32)) * s[gi].astype(np.float32)
+    return out
+
+
+def dequant_ref_T(qweight, qzeros, scales, group_size) -> np.ndarray:
+    """The reader of [AWQ-SPEC] verbatim in orientation: returns [N, K] (out_features first)."""
+    q = unpack_awq(qweight)
+    K, N = q.shape
+    g, _ = resolve_groups(K, group_size)
+    z = unpack_awq(qzeros)
+    s = np.asarray(scales)
+    out = np.empty((N, K), dtype=np.float32)
+    for k in range(K):
+        gi = k // g
+        out[:, k] = (q[k].astype(np.float32) - z[gi].astype(np.float32)) * s[gi].astype(np.float32)
+    return out
+
+
+def gemm_ref(x, qweight, qzeros, scales, bias, group_size) -> np.ndarray:
+    """y = x . dequant(W) + bias, in float64, shape [M, N].
+
+    The fused linear of the GPU-serving blog (section 1.2: the packed weight
+    is unpacked and dequantised, then multiplied with 16-bit activations) with
+    the dequant of [AWQ-SPEC].  x (fp16) and W (exact fp32) convert to float64
+    exactly; the matmul is a library primitive; bias is optional ([AWQ-SPEC]
+    tensor table: fp16 [out_features], optional).
+    """
+    x = np.asarray(x)
+    W = dequant_ref(qweight, qzeros, scales, group_size).astype(np.float64)
+    if x.ndim != 2 or x.shape[1] != W.shape[0]:
+        raise AwqFormatError(f"x shape {x.shape} does not match K={W.shape[0]}")
+    y = x.astype(np.float64) @ W
+    if bias is not None:
+        y = y + np.asarray(bias).astype(np.float64)[None, :]
+    return y
+
+
+def gemm_ref_entries(x, qweight, qzeros, scales, bias, group_size, rows, cols) -> np.ndarray:
+    """y[rows[i], cols[i]] one entry at a time (for sampled checks at large sizes).
+
+    Each entry unpacks only column cols[i]: nibble REVERSE[n % 8] of word n // 8
+    in every row ([GPTQM] reverse order), dequantises with the group row
+    k // g, and takes a float64 dot product with x[rows[i]].
+    """
+    x = np.asarray(x)
+    qw = np.asarray(qweight).view(np.uint32)
+    qz = np.asarray(qzeros).view(np.uint32)
+    s = np.asarray(scales)
+    K = qw.shape[0]
+    g, _ = resolve_groups(K, group_size)
+    gi = np.arange(K) // g
+    out = np.empty(len(rows), dtype=np.float64)
+    for t, (m, n) in enumerate(zip(rows, cols)):
+        shift = np.uint32(4 * AWQ_REVERSE[n % 8])
+        q = ((qw[:, n // 8] >> shift) & np.uint32(0xF)).astype(np.float64)
+        z = ((qz[:, n // 8] >> shift) & np.uint32(0xF)).astype(np.float64)[gi]
+        w = (q - z) * s[gi, n].astype(np.float64)
+        acc = float(np.dot(x[m].astype(np.float64), w))
+        if bias is not None:
+            acc += float(np.asarray(bias)[n])
+        out[t] = acc
+    return out
+
+
+def fp16_rne(a) -> np.ndarray:
+    """Round to IEEE binary16, nearest-even (numpy's cast), for exact-output pins."""
+    return np.asarray(a).astype(np.float16)

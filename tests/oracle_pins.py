@@ -1,0 +1,266 @@
+"""Pins for the CPU oracle: checks that fix its behaviour from outside itself.
+
+Each `pin_*` takes the oracle module `o` and raises AssertionError if it is
+wrong.  tests/test_oracle.py runs them on the real oracle (all must pass) and
+on planted mutants of it (each mutant must fail at least one pin).
+
+What a pin compares against never comes from the oracle under test:
+  * hand-derived packed words (tests/golden/hand_words.json),
+  * bijectivity of the pack on all 32-bit words,
+  * exact rational arithmetic (fractions.Fraction) on tiny inputs,
+  * closed-form special cases (identity input, integer weights, zero weights).
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(1000 + seed)
+
+
+def _words(rng, shape):
+    return rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32).view(np.int32)
+
+
+def pin_hand_words(o):
+    """Packed values derived by hand from the order constant (golden fixture)."""
+    with open(os.path.join(GOLDEN, "hand_words.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        codes = np.array([c["codes"]], dtype=np.int32)
+        word = o.pack_awq(codes)
+        assert word.shape == (1, 1) and word.dtype == np.int32
+        assert int(word[0, 0]) == c["word_int32"], (c, hex(int(word[0, 0]) & 0xFFFFFFFF))
+        assert int(c["word_hex"], 16) == (c["word_int32"] & 0xFFFFFFFF)
+        back = o.unpack_awq(np.array([[c["word_int32"]]], dtype=np.int32))
+        assert back.tolist() == [c["codes"]], (c, back)
+        back2 = o.unpack_awq_gather(np.array([[c["word_int32"]]], dtype=np.int32))
+        assert back2.tolist() == [c["codes"]], (c, back2)
+        if "sequential_word_hex" in c:
+            assert int(c["sequential_word_hex"], 16) != (int(word[0, 0]) & 0xFFFFFFFF)
+
+
+def pin_permutation_inverse(o):
+    """ORDER and REVERSE are inverse permutations of 0..7 (brute force)."""
+    assert sorted(o.AWQ_ORDER) == list(range(8))
+    assert sorted(o.AWQ_REVERSE) == list(range(8))
+    for i in range(8):
+        assert o.AWQ_REVERSE[o.AWQ_ORDER[i]] == i
+        assert o.AWQ_ORDER[o.AWQ_REVERSE[i]] == i
+
+
+def pin_roundtrip_codes(o):
+    """unpack(pack(c)) == c for random codes of several shapes."""
+    for seed in range(10):
+        rng = _rng(seed)
+        R = int(rng.integers(1, 9))
+        N = 8 * int(rng.integers(1, 9))
+        c = rng.integers(0, 16, size=(R, N)).astype(np.int32)
+        w = o.pack_awq(c)
+        assert w.shape == (R, N // 8) and w.dtype == np.int32
+        assert np.array_equal(o.unpack_awq(w), c)
+
+
+def pin_roundtrip_words(o):
+    """pack(unpack(w)) == w for arbitrary 32-bit words, negatives included:
+    unpack is a bijection, so random words are valid packs."""
+    for seed in range(10):
+        rng = _rng(seed)
+        w = _words(rng, (5, 7))
+        w[0, 0] = np.int32(-1)
+        w[0, 1] = np.int32(-(2 ** 31))
+        c = o.unpack_awq(w)
+        assert c.min() >= 0 and c.max() <= 15
+        assert np.array_equal(o.pack_awq(c), w)
+
+
+def pin_two_unpacks_agree(o):
+    """The reader's scatter form and the reverse-order gather form agree."""
+    rng = _rng(3)
+    w = _words(rng, (6, 5))
+    assert np.array_equal(o.unpack_awq(w), o.unpack_awq_gather(w))
+
+
+def pin_no_plus_one(o):
+    """Rule AWQ-005: dequant subtracts the stored zero unchanged, so q == z gives
+    0 and q == z + 1 gives exactly the scale, for every (q, z) pair."""
+    q = np.array([[a for a in range(16) for _ in range(16)]], dtype=np.int32)  # [1, 256]
+    z = np.array([[b for _ in range(16) for b in range(16)]], dtype=np.int32)
+    s = np.full((1, 256), 0.0078125, dtype=np.float16)  # 2^-7
+    qw = o.pack_awq(q)
+    qz = o.pack_awq(z)
+    W = o.dequant_ref(qw, qz, s, -1)
+    assert W.dtype == np.float32 and W.shape == (1, 256)
+    for j in range(256):
+        a, b = int(q[0, j]), int(z[0, j])
+        assert W[0, j] == np.float32((a - b) * 0.0078125), (a, b, W[0, j])
+        if a == b:
+            assert W[0, j] == 0.0
+        if a == b + 1:
+            assert W[0, j] == np.float32(0.0078125)
+
+
+def pin_fp32_product_exact():
+    """Closed form behind bit-exact dequant: (q - z) in [-15, 15] times any finite
+    fp16 scale is exact in float32 (4 + 11 significant bits <= 24).  Checked
+    over all 31 differences and all finite fp16 values; the float64 product is
+    exact by the same argument (<= 53 bits), and a sample is re-checked with
+    Fractions."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    s16 = bits.view(np.float16)
+    s16 = s16[np.isfinite(s16)]
+    s32 = s16.astype(np.float32)
+    s64 = s16.astype(np.float64)
+    for d in range(-15, 16):
+        p32 = np.float32(d) * s32
+        assert np.array_equal(p32.astype(np.float64), np.float64(d) * s64)
+    rng = _rng(7)
+    for v in rng.choice(s16, size=200, replace=False):
+        for d in (-15, -7, 1, 13):
+            assert Fraction(float(np.float32(d) * np.float32(v))) == d * Fraction(float(v))
+
+
+def _brute_force_y(x, codes, zeros, scales, bias, g):
+    """Exact rational y = x . ((codes - zeros[k//g]) * scales[k//g]) + bias."""
+    M, K = x.shape
+    N = codes.shape[1]
+    xs = [[Fraction(float(x[m, k])) for k in range(K)] for m in range(M)]
+    y = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                gi = k // g
+                w = (int(codes[k, n]) - int(zeros[gi, n])) * Fraction(float(scales[gi, n]))
+                acc += xs[m][k] * w
+            if bias is not None:
+                acc += Fraction(float(bias[n]))
+            y[m][n] = acc
+    return y
+
+
+def pin_brute_force_gemm(o):
+    """gemm_ref against exact rational arithmetic on tiny inputs, for several
+    group sizes (one group per row via -1 included) and negative scales.
+    x, the codes and the zeros are taken from plain integer/float matrices;
+    only the packed words the oracle reads come from its packer, which the
+    hand-word pin fixes independently."""
+    cases = [(3, 8, 16, 8), (3, 16, 16, 4), (2, 16, 24, -1), (3, 16, 16, 16), (1, 32, 8, 8)]
+    for t, (M, K, N, g) in enumerate(cases):
+        rng = _rng(20 + t)
+        gg = K if g == -1 else g
+        G = K // gg
+        codes = rng.integers(0, 16, size=(K, N)).astype(np.int32)
+        zeros = rng.integers(0, 16, size=(G, N)).astype(np.int32)
+        scales = (rng.uniform(1e-3, 2e-2, size=(G, N)) * rng.choice([-1, 1], size=(G, N))).astype(np.float16)
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        bias = rng.normal(0, 0.5, size=N).astype(np.float16) if t % 2 == 0 else None
+        y = o.gemm_ref(x, o.pack_awq(codes), o.pack_awq(zeros), scales, bias, g)
+        assert y.shape == (M, N) and y.dtype == np.float64
+        exact = _brute_force_y(x, codes, zeros, scales, bias, gg)
+        for m in range(M):
+            for n in range(N):
+                e = float(exact[m][n])
+                assert abs(y[m, n] - e) <= 1e-12 * max(1.0, abs(e)), (t, m, n, y[m, n], e)
+        # dequant alone, exact: W[k, n] must equal the rational value bit for bit
+        W = o.dequant_ref(o.pack_awq(codes), o.pack_awq(zeros), scales, g)
+        for k in range(K):
+            for n in range(N):
+                gi = k // gg
+                e = (int(codes[k, n]) - int(zeros[gi, n])) * Fraction(float(scales[gi, n]))
+                assert Fraction(float(W[k, n])) == e, (t, k, n)
+
+
+def pin_dequant_orientation(o):
+    """The page's reader returns [out_features, in_features]; ours is its transpose."""
+    rng = _rng(5)
+    K, N, g = 16, 24, 4
+    qw, qz = _words(rng, (K, N // 8)), _words(rng, (K // g, N // 8))
+    s = rng.uniform(-1, 1, size=(K // g, N)).astype(np.float16)
+    a = o.dequant_ref(qw, qz, s, g)
+    b = o.dequant_ref_T(qw, qz, s, g)
+    assert a.shape == (K, N) and b.shape == (N, K)
+    assert np.array_equal(a.T, b)
+
+
+def pin_special_cases(o):
+    """Closed forms: x = I gives W itself; integer weights give an integer
+    matmul; codes == zeros gives y == bias; g = -1 equals g = K."""
+    rng = _rng(9)
+    K, N = 32, 16
+    qw, qz = _words(rng, (K, N // 8)), _words(rng, (1, N // 8))
+    s = rng.uniform(1e-3, 2e-2, size=(1, N)).astype(np.float16)
+    W = o.dequant_ref(qw, qz, s, -1).astype(np.float64)
+    y = o.gemm_ref(np.eye(K, dtype=np.float16), qw, qz, s, None, -1)
+    assert np.array_equal(y, W)
+    # integer weights: s = 1, z = 0, x in {-1, 0, 1}
+    codes = rng.integers(0, 16, size=(K, N)).astype(np.int32)
+    zero_codes = np.zeros((1, N), dtype=np.int32)
+    x = rng.integers(-1, 2, size=(5, K))
+    y = o.gemm_ref(x.astype(np.float16), o.pack_awq(codes), o.pack_awq(zero_codes),
+                   np.ones((1, N), np.float16), None, -1)
+    assert np.array_equal(y, (x.astype(np.int64) @ codes.astype(np.int64)).astype(np.float64))
+    # codes == zeros in every group -> W == 0 -> y == bias
+    g = 8
+    zc = rng.integers(0, 16, size=(K // g, N)).astype(np.int32)
+    codes = np.repeat(zc, g, axis=0)
+    bias = rng.normal(0, 1, size=N).astype(np.float16)
+    s = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    xx = rng.standard_normal((3, K)).astype(np.float16)
+    y = o.gemm_ref(xx, o.pack_awq(codes), o.pack_awq(zc), s, bias, g)
+    assert np.array_equal(y, np.tile(bias.astype(np.float64), (3, 1)))
+    # g = -1 and g = K are the same layer
+    x2 = rng.standard_normal((2, K)).astype(np.float16)
+    s1 = rng.uniform(1e-3, 2e-2, size=(1, N)).astype(np.float16)
+    assert np.array_equal(o.gemm_ref(x2, qw, qz, s1, bias, -1), o.gemm_ref(x2, qw, qz, s1, bias, K))
+
+
+def pin_entries_agree(o):
+    """Entry-by-entry evaluation (used at large sizes) agrees with the full product."""
+    rng = _rng(11)
+    M, K, N, g = 3, 64, 40, 16
+    qw, qz = _words(rng, (K, N // 8)), _words(rng, (K // g, N // 8))
+    s = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    b = rng.normal(0, 0.01, size=N).astype(np.float16)
+    y = o.gemm_ref(x, qw, qz, s, b, g)
+    rows = [m for m in range(M) for _ in range(N)]
+    cols = [n for _ in range(M) for n in range(N)]
+    e = o.gemm_ref_entries(x, qw, qz, s, b, g, rows, cols).reshape(M, N)
+    assert np.allclose(e, y, rtol=1e-12, atol=1e-12)
+
+
+def pin_format_rules(o):
+    """Rejections the pages require: N % 8, K % g, shapes of every tensor."""
+    ok = dict(K=64, N=32, group_size=16, qweight_shape=(64, 4), qzeros_shape=(4, 4),
+              scales_shape=(4, 32), bias_len=32)
+    o.validate_pack(**ok)
+    o.validate_pack(**{**ok, "group_size": -1, "qzeros_shape": (1, 4), "scales_shape": (1, 32)})
+    o.validate_pack(**{**ok, "bias_len": None})
+    bad = [dict(N=36, qweight_shape=(64, 4), qzeros_shape=(4, 4), scales_shape=(4, 36), bias_len=36), dict(group_size=24), dict(group_size=0),
+           dict(qweight_shape=(4, 64)), dict(qzeros_shape=(4, 32)), dict(scales_shape=(32, 4)),
+           dict(bias_len=31), dict(K=0)]
+    for b in bad:
+        try:
+            o.validate_pack(**{**ok, **b})
+        except o.AwqFormatError:
+            continue
+        raise AssertionError(f"accepted bad layer {b}")
+    for badcodes in (np.zeros((2, 12), np.int32), np.full((1, 8), 16, np.int32)):
+        try:
+            o.pack_awq(badcodes)
+        except o.AwqFormatError:
+            continue
+        raise AssertionError("pack accepted an invalid code matrix")
+
+
+ALL_PINS = [pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
+            pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
+            pin_special_cases, pin_entries_agree, pin_format_rules]

@@ -1,0 +1,112 @@
+"""CPU tests: the oracle against its pins, and planted oracle mistakes against the pins."""
+from __future__ import annotations
+
+import importlib.util
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import oracle  # noqa: E402
+from oracle import awq_ref  # noqa: E402
+from tests import oracle_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(awq_ref)
+
+
+def test_fp32_product_exact():
+    oracle_pins.pin_fp32_product_exact()
+
+
+# Each mutant is a plausible slip in the oracle; at least one pin must catch it.
+# (description, text in oracle/awq_ref.py, replacement, occurrence index)
+MUTANTS = [
+    ("sequential nibble order (AWQ-004 violated)",
+     "AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)", "AWQ_ORDER = (0, 1, 2, 3, 4, 5, 6, 7)", 0),
+    ("reverse table used as the order",
+     "AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)", "AWQ_ORDER = (0, 4, 1, 5, 2, 6, 3, 7)", 0),
+    ("zero plus one (AWQ-005 violated)",
+     "- z[gi].astype(np.float32))", "- z[gi].astype(np.float32) - 1)", 0),
+    ("group row k % G instead of k // g",
+     "gi = k // g\n        out[k, :]", "gi = k % (K // g)\n        out[k, :]", 0),
+    ("scale taken from group 0",
+     "* s[gi].astype(np.float32)", "* s[0].astype(np.float32)", 0),
+    ("bias dropped",
+     "y = y + np.asarray(bias).astype(np.float64)[None, :]", "y = y", 0),
+    ("nibble mask dropped",
+     "out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)) & np.uint32(0xF))",
+     "out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)))", 0),
+    ("gather uses the order table instead of its inverse",
+     "(4 * AWQ_REVERSE[j % 8])", "(4 * AWQ_ORDER[j % 8])", 0),
+    ("entries use the wrong group row",
+     "gi = np.arange(K) // g", "gi = np.arange(K) % (K // g)", 0),
+    ("entries use the wrong nibble",
+     "shift = np.uint32(4 * AWQ_REVERSE[n % 8])", "shift = np.uint32(4 * AWQ_ORDER[n % 8])", 0),
+    ("N % 8 rule missing",
+     "    if N % 8 != 0:\n        raise AwqFormatError(f\"N={N} is not a multiple of 8\")\n    _, G",
+     "    _, G", 0),
+    ("pack shifts by the column index",
+     "<< np.uint32(4 * i)", "<< np.uint32(4 * AWQ_ORDER[i])", 0),
+]
+
+
+def _load_mutant(old, new, occurrence):
+    path = awq_ref.__file__
+    with open(path) as f:
+        src = f.read()
+    pos = -1
+    for _ in range(occurrence + 1):
+        pos = src.find(old, pos + 1)
+    assert pos >= 0, f"mutation site not found: {old!r}"
+    mutated = src[:pos] + new + src[pos + len(old):]
+    mod = types.ModuleType("awq_ref_mutant")
+    mod.__file__ = path
+    exec(compile(mutated, path + ":mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("desc,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(desc, old, new, occ):
+    mutant = _load_mutant(old, new, occ)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as e:  # AssertionError or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches the planted mistake: {desc}"
+
+
+def test_package_exports():
+    for name in ("pack_awq", "unpack_awq", "dequant_ref", "gemm_ref", "gemm_ref_entries"):
+        assert callable(getattr(oracle, name))
+
+
+def test_synthetic_generator_distribution():
+    """Random words unpack to codes that are uniform over 0..15 (chi-square-free check)."""
+    from w4a16_weight_only_amd import synth
+    d = synth.make_custom(4, 256, 256, 64, seed=1)
+    codes = awq_ref.unpack_awq(d["qweight"])
+    counts = np.bincount(codes.ravel(), minlength=16)
+    assert counts.sum() == 256 * 256
+    assert counts.min() > 0.9 * 4096 and counts.max() < 1.1 * 4096
+    assert d["scales"].dtype == np.float16 and d["scales"].shape == (4, 256)
+    assert float(d["scales"].min()) >= 1e-3 * 0.999 and float(d["scales"].max()) <= 2e-2 * 1.001
+    assert d["x"].dtype == np.float16 and d["bias"].dtype == np.float16
+
+
+def test_outlier_channels():
+    from w4a16_weight_only_amd import synth
+    w = synth.WORKLOADS["prefill_m2048_k4096_n4096_g128"]
+    small = synth.Workload("p", 64, 4096, 64, 128, False, outlier_count=41)
+    d = synth.make_inputs(small)
+    col_rms = np.sqrt((d["x"].astype(np.float64) ** 2).mean(axis=0))
+    assert (col_rms > 20).sum() == 41
+    assert w.outlier_count == 41

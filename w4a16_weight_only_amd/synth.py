@@ -1,0 +1,101 @@
+"""Seeded synthetic workloads for the fused AWQ W4A16 linear.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic.  Both the HIP path (tests, benchmark) and the CPU oracle take their
+inputs from here.
+
+Packed tensors are drawn as uniformly random 32-bit words.  In the AWQ GEMM
+layout every 32-bit pattern is a valid pack of eight 4-bit codes (the pack is a
+bijection between eight codes in 0..15 and one word), so uniform random words
+are exactly "codes and zeros uniform in 0..15, packed in AWQ order" without
+running a packer here.
+
+Draw order for one workload (one numpy Generator seeded per workload):
+  1. qweight words  [K, N/8]
+  2. qzeros words   [G, N/8]
+  3. scales         uniform [1e-3, 2e-2), rounded to fp16, [G, N]
+  4. x              standard normal [M, K] (float64 draws)
+  5. outlier input channels (only if outlier_count > 0): rng.choice without
+     replacement; those columns of x are multiplied by outlier_gain before the
+     fp16 rounding
+  6. bias           normal(0, 0.01) rounded to fp16, [N] (only if bias)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    K: int
+    N: int
+    group_size: int
+    bias: bool
+    outlier_count: int = 0
+    outlier_gain: float = 50.0
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def groups(self) -> int:
+        return 1 if self.group_size == -1 else self.K // self.group_size
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the fused linear must move at least once: packed weight, packed
+        zeros, fp16 scales, fp16 x, fp16 bias (if any) and fp16 y."""
+        G = self.groups
+        return (self.K * self.N // 2 + G * self.N // 2 + 2 * G * self.N
+                + 2 * self.M * self.K + (2 * self.N if self.bias else 0) + 2 * self.M * self.N)
+
+    def flops(self) -> int:
+        return 2 * self.M * self.K * self.N
+
+
+def _down_proj(M: int, g: int) -> Workload:
+    return Workload(f"down_proj_m{M}_k11008_n4096_g{g}", M, 11008, 4096, g, True,
+                    note="7B MLP down_proj shape sweep")
+
+
+# The measured and parity workloads: a tiny correctness layer, the 7B attention
+# q_proj decode GEMV, the 7B MLP up_proj small-batch decode, a 2048-token
+# prefill with activation-outlier channels, and the down_proj M sweep.
+WORKLOADS = {w.name: w for w in [
+    Workload("tiny_m4_k512_n512_g128", 4, 512, 512, 128, False, note="tiny correctness layer"),
+    Workload("decode_m1_k4096_n4096_g128", 1, 4096, 4096, 128, True, note="7B q_proj decode GEMV"),
+    Workload("decode_m16_k4096_n11008_g128", 16, 4096, 11008, 128, True, note="7B MLP up_proj small batch"),
+    Workload("prefill_m2048_k4096_n4096_g128", 2048, 4096, 4096, 128, False, outlier_count=41,
+             note="prefill, 1% of input channels x50"),
+    *[_down_proj(M, g) for g in (64, -1) for M in (1, 8, 64, 512)],
+]}
+
+
+def random_words(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform random 32-bit patterns as int32."""
+    return rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32).view(np.int32)
+
+
+def make_inputs(w: Workload, seed: int | None = None) -> dict:
+    """numpy inputs for workload `w` (see the module docstring for the draw order)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    M, K, N, G = w.M, w.K, w.N, w.groups
+    qweight = random_words(rng, (K, N // 8))
+    qzeros = random_words(rng, (G, N // 8))
+    scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K))
+    if w.outlier_count:
+        idx = rng.choice(K, size=w.outlier_count, replace=False)
+        x[:, idx] *= w.outlier_gain
+    x = x.astype(np.float16)
+    bias = rng.normal(0.0, 0.01, size=N).astype(np.float16) if w.bias else None
+    return dict(x=x, qweight=qweight, qzeros=qzeros, scales=scales, bias=bias,
+                group_size=w.group_size)
+
+
+def make_custom(M, K, N, group_size, bias=True, seed=0, outlier_count=0) -> dict:
+    """Same distributions at an arbitrary shape (ragged and edge-case tests)."""
+    return make_inputs(Workload(f"custom_m{M}_k{K}_n{N}_g{group_size}", M, K, N, group_size,
+                                bias, outlier_count=outlier_count, seed=seed))
