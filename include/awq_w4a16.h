@@ -1,0 +1,145 @@
+/*
+ * awq_w4a16.h - C ABI of the fused AWQ W4A16 linear for AMD Instinct MI355X (gfx950).
+ *
+ *   y[M, N] = x[M, K] . W[K, N] + bias[N],
+ *   W[k, n] = (q[k, n] - z[k / g, n]) * s[k / g, n]
+ *
+ * The weights arrive in the AWQ "GEMM" checkpoint layout, consumed as stored:
+ *   qweight  int32 [K, N/8]  row-major; bits 4i..4i+3 of word (k, c) hold the
+ *                            code of column 8c + ORDER[i], ORDER = {0,2,4,6,1,3,5,7}
+ *                            (tensref.org "AWQ" format page, Reader; GPTQModel wiki
+ *                            "AWQ", section "Saved formats and packing")
+ *   qzeros   int32 [G, N/8]  zero codes packed the same way; subtracted as stored,
+ *                            never plus one (format page, rule AWQ-005)
+ *   scales   fp16  [G, N]    row k / g scales input row k (format page, Reader)
+ *   bias     fp16  [N]       optional (format page, tensor table)
+ *   x        fp16  [M, K]    activations, row-major
+ *   y        fp16  [M, N]    output, row-major
+ * with g = group_size and G = K / g; group_size == -1 means one group spanning all
+ * K rows, G = 1 (GPTQModel wiki "AWQ", section "Group quantization and zero points").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers to tensor data are DEVICE pointers of the current HIP device; fp16
+ *     tensors are passed as raw 16-bit storage (IEEE binary16).
+ *   - The caller owns every buffer.  The library keeps no pointer to them after the
+ *     call returns.  Outputs must not alias inputs.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream); the
+ *     library never synchronises the stream except when it must grow its own
+ *     workspace (see awq_gemm).
+ *   - Every argument is checked before anything is enqueued; a failed check returns
+ *     a negative status and enqueues nothing.  No entry point aborts, prints or
+ *     throws.  awq_status_string() names a status.
+ *   - Entry points are safe to call from several host threads.
+ */
+#ifndef AWQ_W4A16_H
+#define AWQ_W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* a hipStream_t */
+
+enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  AWQ_ERR_SHAPE = -2,       /* tensor shapes disagree with K, N, group_size, or N % 8 != 0 */
+  AWQ_ERR_GROUP = -3,       /* group_size is neither -1 nor a positive divisor of K */
+  AWQ_ERR_ALIGN = -4,       /* a tensor base pointer is not 16-byte aligned */
+  AWQ_ERR_UNSUPPORTED = -5, /* a valid layer outside the kernels' limits (below) */
+  AWQ_ERR_HIP = -6          /* the HIP runtime reported an error */
+};
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char* awq_status_string(int status);
+
+/*
+ * Format rules of the GEMM pack, host-only (touches no device).
+ * Source: GPTQModel wiki "AWQ", section "Saved formats and packing" (shapes,
+ * INT4 packing needs N % 8 == 0) and section "Group quantization and zero points"
+ * (-1 = one group; positive sizes must fit K).  Shapes that do not divide are
+ * rejected, never truncated.
+ *   K, N          in_features, out_features (both >= 1, N % 8 == 0)
+ *   group_size    -1 or a positive divisor of K
+ *   *_rows/_cols  the caller's tensor shapes; qweight [K, N/8], qzeros [G, N/8],
+ *                 scales [G, N]
+ *   bias_len      N, or -1 when there is no bias
+ * Returns AWQ_OK, AWQ_ERR_SHAPE or AWQ_ERR_GROUP.
+ */
+int awq_validate_pack(int64_t K, int64_t N, int64_t group_size,
+                      int64_t qweight_rows, int64_t qweight_cols,
+                      int64_t qzeros_rows, int64_t qzeros_cols,
+                      int64_t scales_rows, int64_t scales_cols,
+                      int64_t bias_len);
+
+/*
+ * Kernel limits on top of the format rules (AWQ_ERR_UNSUPPORTED otherwise):
+ *   K % 32 == 0, N % 32 == 0, group_size == -1 or group_size % 32 == 0,
+ *   K, N <= 2^24, M <= 2^24.
+ * Host-only check; returns AWQ_OK, AWQ_ERR_SHAPE, AWQ_ERR_GROUP or AWQ_ERR_UNSUPPORTED.
+ */
+int awq_check_limits(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/*
+ * Dequantise the packed weight to float32:  out[k, n] = (float)(q - z) * (float)s.
+ * Source: tensref.org "AWQ" format page, Reader (group row k / group_size, no +1 on
+ * zeros); orientation [K, N] as multiplied by x (the page's reader returns the
+ * transpose, [N, K]).  (q - z) has at most 4 significant bits and s 11, so the
+ * product is exact in float32: the result is bit-identical to any correct
+ * implementation, including the signed zero of (q - z) == 0 with s < 0.
+ *   qweight, qzeros, scales_f16   device, layouts as above
+ *   out                           device float32 [K, N], written in full
+ * Returns AWQ_OK or an error status (nothing enqueued on error).
+ */
+int awq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                int64_t K, int64_t N, int64_t group_size, float* out,
+                struct ihipStream_t* stream);
+
+/*
+ * Fused linear y = x . dequant(W) + bias, accumulated in float32 and rounded once
+ * to fp16 (round to nearest even) after the bias is added.
+ * Source: GPU LLM serving-stack blog, section 1.2 (W4A16: packed weights are
+ * unpacked and dequantised on chip inside the matrix multiply, activations stay
+ * 16-bit), with the dequant of the format page's Reader; fp32 accumulation as in
+ * the GPTQModel wiki "AWQ", sections "Native GEMM" and "Triton GEMM and dispatch
+ * policy".
+ *   x_f16       device fp16 [M, K]
+ *   qweight     device int32 [K, N/8];  qzeros int32 [G, N/8];  scales fp16 [G, N]
+ *   bias_f16    device fp16 [N], or NULL for no bias
+ *   y_f16       device fp16 [M, N], written in full
+ * M == 0 returns AWQ_OK and enqueues nothing (GPTQModel wiki, "Native GEMM": empty
+ * input launches no kernel).  Two kernel families are chosen by M: a
+ * bandwidth-bound skinny family for small M and an MFMA tile family above it
+ * (awq_gemm_plan reports the choice).  The result is deterministic: the same
+ * inputs give the same bits on every call.
+ * Workspace: the skinny family splits K across workgroups and reduces the partial
+ * sums in a fixed order through a library-owned device buffer, one per
+ * (device, stream).  The first call on a (device, stream) that needs a larger
+ * buffer allocates it (and synchronises that stream); later calls allocate
+ * nothing, so run one eager call before capturing a stream into a graph.
+ * Returns AWQ_OK or an error status.
+ */
+int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
+             const void* scales_f16, const void* bias_f16,
+             int64_t M, int64_t K, int64_t N, int64_t group_size,
+             void* y_f16, struct ihipStream_t* stream);
+
+/*
+ * The launch plan awq_gemm would use for this shape (host-only, no device work).
+ *   family   0 = skinny split-K family, 1 = MFMA tile family
+ *   splits   number of K splits across workgroups (1 = none)
+ *   grid_x, grid_y, block   launch geometry of the main kernel
+ *   workspace_bytes         device workspace the call needs (0 if none)
+ * Any output pointer may be NULL.  Returns AWQ_OK or the awq_check_limits status.
+ */
+int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
+                  int* family, int* splits, int* grid_x, int* grid_y, int* block,
+                  int64_t* workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_W4A16_H */

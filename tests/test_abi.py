@@ -1,0 +1,120 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and its host-only checks return the documented statuses.  No device work."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_weight_only_amd as awq
+from w4a16_weight_only_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq_w4a16.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(awq_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libawq_w4a16.so is not built; run `python -m w4a16_weight_only_amd.build`")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("awq_validate_pack", "awq_dequant", "awq_gemm", "awq_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(-6, 1):
+        s = _lib.status_string(st)
+        assert s.startswith("AWQ")
+    assert "unknown" in _lib.status_string(-99)
+
+
+def _validate(lib, K=4096, N=4096, g=128, qw=None, qz=None, sc=None, bias=-1):
+    G = 1 if g == -1 else (K // g if g > 0 and K % g == 0 else 1)
+    qw = qw or (K, N // 8)
+    qz = qz or (G, N // 8)
+    sc = sc or (G, N)
+    return lib.awq_validate_pack(K, N, g, *qw, *qz, *sc, bias)
+
+
+def test_validate_pack_rules(lib):
+    assert _validate(lib) == _lib.AWQ_OK
+    assert _validate(lib, bias=4096) == _lib.AWQ_OK
+    assert _validate(lib, g=-1) == _lib.AWQ_OK
+    assert _validate(lib, K=11008, N=4096, g=64) == _lib.AWQ_OK
+    assert _validate(lib, N=4100) == _lib.AWQ_ERR_SHAPE            # N % 8
+    assert _validate(lib, g=100) == _lib.AWQ_ERR_GROUP             # K % g
+    assert _validate(lib, g=0) == _lib.AWQ_ERR_GROUP
+    assert _validate(lib, g=-2) == _lib.AWQ_ERR_GROUP
+    assert _validate(lib, qw=(512, 4096)) == _lib.AWQ_ERR_SHAPE    # transposed qweight
+    assert _validate(lib, qz=(32, 4096)) == _lib.AWQ_ERR_SHAPE     # unpacked zeros
+    assert _validate(lib, sc=(4096, 32)) == _lib.AWQ_ERR_SHAPE     # transposed scales
+    assert _validate(lib, bias=4095) == _lib.AWQ_ERR_SHAPE
+    assert _validate(lib, K=0) == _lib.AWQ_ERR_SHAPE
+
+
+def test_kernel_limits(lib):
+    assert lib.awq_check_limits(1, 4096, 4096, 128) == _lib.AWQ_OK
+    assert lib.awq_check_limits(1, 4096, 4096, -1) == _lib.AWQ_OK
+    assert lib.awq_check_limits(0, 4096, 4096, 128) == _lib.AWQ_OK
+    assert lib.awq_check_limits(-1, 4096, 4096, 128) == _lib.AWQ_ERR_SHAPE
+    assert lib.awq_check_limits(1, 4096, 4104, 8) == _lib.AWQ_ERR_UNSUPPORTED   # N % 32, g % 32
+    assert lib.awq_check_limits(1, 4112, 4096, -1) == _lib.AWQ_ERR_UNSUPPORTED  # K % 32
+    assert lib.awq_check_limits(1, 4096, 4096, 16) == _lib.AWQ_ERR_UNSUPPORTED  # group 16
+    assert lib.awq_check_limits(1, 1 << 25, 4096, -1) == _lib.AWQ_ERR_UNSUPPORTED
+
+
+def test_plan_families():
+    p1 = awq.plan(1, 4096, 4096, 128)
+    assert p1["family"] == "skinny" and p1["splits"] > 1 and p1["workspace_bytes"] > 0
+    p16 = awq.plan(16, 4096, 11008, 128)
+    assert p16["family"] == "skinny"
+    p2048 = awq.plan(2048, 4096, 4096, 128)
+    assert p2048["family"] == "tile" and p2048["workspace_bytes"] == 0
+    with pytest.raises(ValueError):
+        awq.plan(1, 4096, 4104, 128)
+
+
+def test_gemm_argument_errors_touch_no_device(lib):
+    """Checks run before any HIP call, so these are safe without a GPU."""
+    p = ctypes.c_void_p(1 << 20)  # aligned dummy, never dereferenced
+    # M == 0: nothing to do, no launch.
+    assert lib.awq_gemm(p, p, p, p, None, 0, 4096, 4096, 128, p, None) == _lib.AWQ_OK
+    assert lib.awq_gemm(None, p, p, p, None, 1, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_NULL
+    assert lib.awq_gemm(p, p, p, p, None, 1, 4096, 4096, 128, None, None) == _lib.AWQ_ERR_NULL
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.awq_gemm(odd, p, p, p, None, 1, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
+    assert lib.awq_gemm(p, p, p, p, odd, 1, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
+    assert lib.awq_gemm(p, p, p, p, None, 1, 4096, 4100, 128, p, None) == _lib.AWQ_ERR_SHAPE
+    assert lib.awq_gemm(p, p, p, p, None, 1, 4096, 4096, 100, p, None) == _lib.AWQ_ERR_GROUP
+    assert lib.awq_gemm(p, p, p, p, None, 1, 4096, 4096, 16, p, None) == _lib.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_dequant(None, p, p, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_NULL
+    assert lib.awq_dequant(p, p, odd, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
+
+
+def test_quantization_config():
+    cfg = {"quant_method": "awq", "bits": 4, "group_size": 64, "zero_point": True, "version": "gemm"}
+    assert awq.group_size_from_config(cfg) == 64
+    for bad in ({**cfg, "bits": 8}, {**cfg, "version": "gemv"}, {**cfg, "zero_point": False},
+                {**cfg, "quant_method": "gptq"}):
+        with pytest.raises(ValueError):
+            awq.group_size_from_config(bad)

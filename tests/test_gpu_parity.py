@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+awq_dequant must match the oracle bit for bit (the fp32 product is exact).
+awq_gemm (fp16 out, fp32 accumulation) must satisfy, over the whole output,
+    max |y - y_ref| <= 1e-2 * max(1, max |y_ref|)   and   ||y - y_ref||_F <= 2e-3 ||y_ref||_F
+against the oracle's float64 result; special inputs whose exact result is a single
+rounding (identity rows, integer weights, zero weights) must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import w4a16_weight_only_amd as awq
+from oracle import awq_ref as oracle
+from w4a16_weight_only_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL = 1e-2
+FRO_TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a HIP GPU")
+    awq.load_library()
+
+
+def dev(d):
+    out = {}
+    for k, v in d.items():
+        out[k] = torch.from_numpy(np.ascontiguousarray(v)).cuda() if isinstance(v, np.ndarray) else v
+    return out
+
+
+def gemm(d):
+    t = dev(d)
+    y = awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], d["group_size"])
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def tol_check(y, yref, label=""):
+    assert y.shape == yref.shape
+    assert np.isfinite(y).all(), label
+    err = np.abs(y.astype(np.float64) - yref)
+    bound = MAX_TOL * max(1.0, float(np.abs(yref).max()))
+    fro = float(np.linalg.norm(err) / max(np.linalg.norm(yref), 1e-300))
+    print(f"[{label}] max_err={err.max():.3e} (bound {bound:.3e}) rel_fro={fro:.3e}", flush=True)
+    assert err.max() <= bound, label
+    assert fro <= FRO_TOL, label
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+ALL = list(synth.WORKLOADS)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_dequant_bit_exact(name):
+    w = synth.WORKLOADS[name]
+    print(f"dequant {name}", flush=True)
+    d = synth.make_inputs(w)
+    t = dev(d)
+    W = awq.awq_dequant(t["qweight"], t["qzeros"], t["scales"], w.group_size)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], w.group_size)
+    assert np.array_equal(bits(W.cpu().numpy()), bits(ref))
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_gemm_workload(name):
+    w = synth.WORKLOADS[name]
+    print(f"gemm {name} plan={awq.plan(w.M, w.K, w.N, w.group_size)}", flush=True)
+    d = synth.make_inputs(w)
+    y = gemm(d)
+    yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], w.group_size)
+    tol_check(y, yref, name)
+
+
+RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
+    (1, 32, 32, 32, False),
+    (5, 352, 800, 32, True),
+    (16, 320, 544, 64, True),
+    (3, 4096, 96, 128, True),
+    (2, 11008, 32, -1, True),
+    (7, 2048, 288, 256, False),
+    (17, 320, 544, 64, True),
+    (130, 256, 416, -1, True),
+    (257, 512, 256, 128, False),
+    (64, 1024, 4128, 128, True),
+]
+
+
+@pytest.mark.parametrize("M,K,N,g,bias", RAGGED)
+def test_gemm_ragged(M, K, N, g, bias):
+    print(f"ragged M={M} K={K} N={N} g={g} plan={awq.plan(M, K, N, g)}", flush=True)
+    d = synth.make_custom(M, K, N, g, bias=bias, seed=M + K + N)
+    yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    tol_check(gemm(d), yref, f"M{M}K{K}N{N}g{g}")
+
+
+@pytest.mark.parametrize("M,K,N,g", [(5, 352, 800, 32), (2, 11008, 32, -1)])
+def test_dequant_ragged_negative_scales(M, K, N, g):
+    """Negative scales make (q - z) == 0 a negative zero: bits must still agree."""
+    d = synth.make_custom(M, K, N, g, seed=3)
+    d["scales"] = (-d["scales"].astype(np.float32)).astype(np.float16)
+    t = dev(d)
+    W = awq.awq_dequant(t["qweight"], t["qzeros"], t["scales"], g).cpu().numpy()
+    ref = oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], g)
+    assert (np.signbit(ref) & (ref == 0)).any()
+    assert np.array_equal(bits(W), bits(ref))
+
+
+@pytest.mark.parametrize("M,K,N,g", [(9, 1024, 512, 128), (300, 512, 384, 64)])
+def test_gemm_negative_scales(M, K, N, g):
+    d = synth.make_custom(M, K, N, g, seed=4)
+    d["scales"] = (-d["scales"].astype(np.float32)).astype(np.float16)
+    yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    tol_check(gemm(d), yref, "negative scales")
+
+
+@pytest.mark.parametrize("K,N,g,rows", [(512, 512, 128, 16), (256, 384, 64, 256), (4096, 256, -1, 3)])
+def test_identity_rows_exact(K, N, g, rows):
+    """x = rows of I_K: every output is one exact weight, so y == fp16(W) bit for bit."""
+    d = synth.make_custom(rows, K, N, g, bias=False, seed=5)
+    pick = np.linspace(0, K - 1, rows).astype(np.int64) if rows < K else np.arange(K)
+    x = np.zeros((len(pick), K), dtype=np.float16)
+    x[np.arange(len(pick)), pick] = 1.0
+    d["x"] = x
+    W = oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], g)
+    expect = oracle.fp16_rne(W[pick])
+    y = gemm(d)
+    assert np.array_equal(bits(y), bits(expect))
+
+
+@pytest.mark.parametrize("M", [1, 6, 16, 40, 200])
+def test_integer_weights_exact(M):
+    """s = 1, z = 0, x in {-1, 0, 1}, K = 128: |y| <= 1920, an exact fp16 integer."""
+    K, N = 128, 256
+    rng = np.random.default_rng(M)
+    d = synth.make_custom(M, K, N, -1, bias=False, seed=6)
+    d["qzeros"] = np.zeros_like(d["qzeros"])
+    d["scales"] = np.ones_like(d["scales"])
+    d["x"] = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    codes = oracle.unpack_awq(d["qweight"]).astype(np.int64)
+    expect = (d["x"].astype(np.int64) @ codes).astype(np.float16)
+    assert np.array_equal(bits(gemm(d)), bits(expect))
+
+
+@pytest.mark.parametrize("M", [1, 12, 33])
+def test_zero_weights_give_bias(M):
+    """codes == zeros in every group: W == 0 and y == bias exactly."""
+    K, N, g = 256, 512, 64
+    d = synth.make_custom(M, K, N, g, bias=True, seed=7)
+    d["qweight"] = np.repeat(d["qzeros"], g, axis=0)
+    y = gemm(d)
+    assert np.array_equal(bits(y), bits(np.tile(d["bias"], (M, 1))))
+
+
+@pytest.mark.parametrize("M", [1, 16, 100])
+def test_group_minus_one_equals_group_k(M):
+    K, N = 1024, 512
+    d = synth.make_custom(M, K, N, -1, seed=8)
+    y1 = gemm(d)
+    d2 = dict(d, group_size=K)
+    y2 = gemm(d2)
+    assert np.array_equal(bits(y1), bits(y2))
+
+
+@pytest.mark.parametrize("name", ["decode_m1_k4096_n4096_g128", "decode_m16_k4096_n11008_g128",
+                                  "down_proj_m64_k11008_n4096_g64"])
+def test_deterministic(name):
+    w = synth.WORKLOADS[name]
+    t = dev(synth.make_inputs(w))
+    ys = [awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], w.group_size).clone()
+          for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+
+
+def test_m_zero_is_a_noop():
+    d = dev(synth.make_custom(1, 256, 256, 128))
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    y = awq.awq_gemm(x, d["qweight"], d["qzeros"], d["scales"], d["bias"], 128)
+    assert tuple(y.shape) == (0, 256)
+
+
+def test_leading_dims_and_side_stream():
+    d = synth.make_custom(6, 512, 256, 64, seed=9)
+    t = dev(d)
+    x3 = t["x"].view(2, 3, 512)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = awq.awq_gemm(x3, t["qweight"], t["qzeros"], t["scales"], t["bias"], 64)
+    s.synchronize()
+    assert tuple(y.shape) == (2, 3, 256)
+    yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], 64)
+    tol_check(y.reshape(6, 256).cpu().numpy(), yref, "leading dims")
+
+
+def test_bad_arguments_raise_before_launch():
+    t = dev(synth.make_custom(2, 256, 256, 64))
+    with pytest.raises(ValueError):
+        awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], 128)  # wrong group
+    with pytest.raises(ValueError):
+        awq.awq_gemm(t["x"][:, :128].contiguous(), t["qweight"], t["qzeros"], t["scales"], t["bias"], 64)
+    with pytest.raises(TypeError):
+        awq.awq_gemm(t["x"].float(), t["qweight"], t["qzeros"], t["scales"], t["bias"], 64)
+    with pytest.raises(ValueError):
+        awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"][:100].contiguous(), 64)

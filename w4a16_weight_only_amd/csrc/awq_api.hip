@@ -1,0 +1,240 @@
+// C ABI of the AWQ W4A16 library: argument checks, launch planning, workspace.
+// The declarations and their contracts are in include/awq_w4a16.h.
+#include <mutex>
+#include <map>
+#include <utility>
+
+#include "../../include/awq_w4a16.h"
+#include "awq_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t groups_of(int64_t K, int64_t group_size) { return group_size == -1 ? 1 : K / group_size; }
+
+// Effective group length passed to kernels: -1 means one group spanning K.
+int eff_group(int64_t K, int64_t group_size) { return (int)(group_size == -1 ? K : group_size); }
+
+int format_check(int64_t K, int64_t N, int64_t group_size) {
+  if (K < 1 || N < 1 || N % 8 != 0) return AWQ_ERR_SHAPE;
+  if (group_size == -1) return AWQ_OK;
+  if (group_size <= 0 || K % group_size != 0) return AWQ_ERR_GROUP;
+  return AWQ_OK;
+}
+
+int limits_check(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  int st = format_check(K, N, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 0) return AWQ_ERR_SHAPE;
+  if (K % 32 != 0 || N % 32 != 0) return AWQ_ERR_UNSUPPORTED;
+  if (group_size != -1 && group_size % 32 != 0) return AWQ_ERR_UNSUPPORTED;
+  if (K > kMaxDim || N > kMaxDim || M > kMaxDim) return AWQ_ERR_UNSUPPORTED;
+  // The tile family's 1-D grid must stay below 2^31 workgroups.
+  if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  return AWQ_OK;
+}
+
+struct Plan {
+  int family = 0;  // 0 skinny, 1 tile
+  int splits = 1;
+  int grid_x = 0, grid_y = 0, block = 0;
+  int mrows = 0;
+  int64_t partial_bytes = 0, counter_bytes = 0;
+  int64_t workspace_bytes() const { return partial_bytes ? partial_bytes + counter_bytes : 0; }
+};
+
+// Compute units of the current device (cached per device ordinal).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+Plan make_plan(int64_t M, int64_t K, int64_t N, int cus) {
+  Plan p;
+  if (M <= awq::kSkinnyMaxM) {
+    p.family = 0;
+    p.block = awq::kSkinnyThreads;
+    const int n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
+    const int T = (int)(K / awq::kKStep);
+    // Aim for about two workgroups per compute unit, while every wave keeps at
+    // least one k-step.
+    const int target = 2 * cus;
+    int s = (target + n_tiles - 1) / n_tiles;
+    const int cap = T / 4 > 0 ? T / 4 : 1;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    p.splits = s;
+    p.grid_x = n_tiles;
+    p.grid_y = s;
+    p.mrows = M <= 4 ? 4 : 16;
+    if (s > 1) {
+      p.counter_bytes = ((int64_t)n_tiles * 4 + 255) / 256 * 256;
+      p.partial_bytes = (int64_t)n_tiles * s * p.mrows * awq::kSkinnyCols * 4;
+    }
+  } else {
+    p.family = 1;
+    p.block = awq::kTileThreads;
+    const int64_t n_tiles = (N + awq::kTileN - 1) / awq::kTileN;
+    const int64_t m_tiles = (M + awq::kTileM - 1) / awq::kTileM;
+    p.grid_x = (int)(n_tiles * m_tiles);
+    p.grid_y = 1;
+  }
+  return p;
+}
+
+// Library-owned split-K workspace, one per (device, stream).  Counters sit at the
+// front and must be zero between calls (each reduction resets its own).
+struct Workspace {
+  void* ptr = nullptr;
+  int64_t bytes = 0;
+  int64_t counter_bytes = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(const Plan& p, hipStream_t stream, float** partial, uint32_t** counters) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& ws = g_ws[{dev, stream}];
+  // Counters need p.counter_bytes at the front; partials follow.  Keep the counter
+  // region at least as large as any earlier one so old counters stay zero.
+  const int64_t cb = p.counter_bytes > ws.counter_bytes ? p.counter_bytes : ws.counter_bytes;
+  const int64_t need = cb + p.partial_bytes;
+  if (ws.ptr == nullptr || need > ws.bytes || cb > ws.counter_bytes) {
+    if (ws.ptr) {
+      // Work already queued on this stream may still read the old buffer.
+      if (hipStreamSynchronize(stream) != hipSuccess) return AWQ_ERR_HIP;
+      if (hipFree(ws.ptr) != hipSuccess) return AWQ_ERR_HIP;
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    int64_t bytes = need + need / 4;  // headroom against frequent regrowth
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, (size_t)bytes) != hipSuccess) return AWQ_ERR_HIP;
+    if (hipMemset(ptr, 0, (size_t)cb) != hipSuccess) {
+      (void)hipFree(ptr);
+      return AWQ_ERR_HIP;
+    }
+    ws.ptr = ptr;
+    ws.bytes = bytes;
+    ws.counter_bytes = cb;
+  }
+  *counters = reinterpret_cast<uint32_t*>(ws.ptr);
+  *partial = reinterpret_cast<float*>(reinterpret_cast<char*>(ws.ptr) + ws.counter_bytes);
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_NULL: return "AWQ_ERR_NULL: a required pointer is NULL";
+    case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE: tensor shapes disagree with K, N, group_size (or N % 8 != 0)";
+    case AWQ_ERR_GROUP: return "AWQ_ERR_GROUP: group_size must be -1 or a positive divisor of K";
+    case AWQ_ERR_ALIGN: return "AWQ_ERR_ALIGN: tensor base pointers must be 16-byte aligned";
+    case AWQ_ERR_UNSUPPORTED:
+      return "AWQ_ERR_UNSUPPORTED: needs K % 32 == 0, N % 32 == 0, group_size -1 or a multiple of 32, sizes <= 2^24";
+    case AWQ_ERR_HIP: return "AWQ_ERR_HIP: the HIP runtime reported an error";
+    default: return "AWQ: unknown status";
+  }
+}
+
+int awq_validate_pack(int64_t K, int64_t N, int64_t group_size, int64_t qweight_rows,
+                      int64_t qweight_cols, int64_t qzeros_rows, int64_t qzeros_cols,
+                      int64_t scales_rows, int64_t scales_cols, int64_t bias_len) {
+  const int st = format_check(K, N, group_size);
+  if (st != AWQ_OK) return st;
+  const int64_t G = groups_of(K, group_size);
+  if (qweight_rows != K || qweight_cols != N / 8) return AWQ_ERR_SHAPE;
+  if (qzeros_rows != G || qzeros_cols != N / 8) return AWQ_ERR_SHAPE;
+  if (scales_rows != G || scales_cols != N) return AWQ_ERR_SHAPE;
+  if (bias_len != -1 && bias_len != N) return AWQ_ERR_SHAPE;
+  return AWQ_OK;
+}
+
+int awq_check_limits(int64_t M, int64_t K, int64_t N, int64_t group_size) {
+  return limits_check(M, K, N, group_size);
+}
+
+int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* family, int* splits,
+                  int* grid_x, int* grid_y, int* block, int64_t* workspace_bytes) {
+  const int st = limits_check(M, K, N, group_size);
+  if (st != AWQ_OK) return st;
+  // Planning uses a 256-CU device when no device is visible (host-only callers).
+  int cus = 256;
+  int count = 0;
+  if (hipGetDeviceCount(&count) == hipSuccess && count > 0) cus = device_cus();
+  else (void)hipGetLastError();
+  const Plan p = make_plan(M, K, N, cus);
+  if (family) *family = p.family;
+  if (splits) *splits = p.splits;
+  if (grid_x) *grid_x = p.grid_x;
+  if (grid_y) *grid_y = p.grid_y;
+  if (block) *block = p.block;
+  if (workspace_bytes) *workspace_bytes = p.workspace_bytes();
+  return AWQ_OK;
+}
+
+int awq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K,
+                int64_t N, int64_t group_size, float* out, struct ihipStream_t* stream) {
+  const int st = limits_check(0, K, N, group_size);
+  if (st != AWQ_OK) return st;
+  if (!qweight || !qzeros || !scales_f16 || !out) return AWQ_ERR_NULL;
+  if (!aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16) || !aligned16(out))
+    return AWQ_ERR_ALIGN;
+  hipError_t e = awq::launch_dequant(qweight, qzeros, static_cast<const uint16_t*>(scales_f16), (int)K,
+                                     (int)N, eff_group(K, group_size), out, stream);
+  return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+
+int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+             const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
+             struct ihipStream_t* stream) {
+  const int st = limits_check(M, K, N, group_size);
+  if (st != AWQ_OK) return st;
+  if (M == 0) return AWQ_OK;
+  if (!x_f16 || !qweight || !qzeros || !scales_f16 || !y_f16) return AWQ_ERR_NULL;
+  if (!aligned16(x_f16) || !aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16) ||
+      !aligned16(y_f16) || (bias_f16 && !aligned16(bias_f16)))
+    return AWQ_ERR_ALIGN;
+  const Plan p = make_plan(M, K, N, device_cus());
+  const auto* x = static_cast<const uint16_t*>(x_f16);
+  const auto* sc = static_cast<const uint16_t*>(scales_f16);
+  const auto* b = static_cast<const uint16_t*>(bias_f16);
+  auto* y = static_cast<uint16_t*>(y_f16);
+  const int g = eff_group(K, group_size);
+  hipError_t e;
+  if (p.family == 0) {
+    float* partial = nullptr;
+    uint32_t* counters = nullptr;
+    if (p.splits > 1) {
+      const int ws = get_workspace(p, stream, &partial, &counters);
+      if (ws != AWQ_OK) return ws;
+    }
+    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.splits, partial,
+                           counters, y, stream);
+  } else {
+    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, y, stream);
+  }
+  return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side building blocks of the AWQ W4A16 kernels (gfx950 only).
+//
+// Layout facts used throughout (tensref.org "AWQ" format page, Reader; GPTQModel
+// wiki "AWQ", section "Saved formats and packing"):
+//   word (k, c) of qweight holds, in bits 4i..4i+3, the code of column 8c + ORDER[i]
+//   with ORDER = {0,2,4,6,1,3,5,7}.  Byte t of the word therefore holds two columns:
+//   its low nibble (nibble 2t) is column ORDER[2t] and its high nibble (nibble 2t+1)
+//   is column ORDER[2t+1]:
+//       byte 0 -> columns 0 (low), 2 (high)     byte 1 -> columns 4, 6
+//       byte 2 -> columns 1, 3                  byte 3 -> columns 5, 7
+//   qzeros words use the same packing; dequant is (q - z) * s with the stored zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Column held by the low / high nibble of byte t (see the table above).
+__host__ __device__ constexpr int lo_col(int t) { return ((t & 1) << 2) | (t >> 1); }
+__host__ __device__ constexpr int hi_col(int t) { return lo_col(t) + 2; }
+// Nibble index (0..7) that holds column j of a word: the inverse of ORDER.
+__host__ __device__ constexpr int nibble_of_col(int j) {
+  return (j & 1) ? (4 + (j >> 1)) : (j >> 1);
+}
+
+static_assert(lo_col(0) == 0 && hi_col(0) == 2 && lo_col(1) == 4 && hi_col(1) == 6, "byte->column table");
+static_assert(lo_col(2) == 1 && hi_col(2) == 3 && lo_col(3) == 5 && hi_col(3) == 7, "byte->column table");
+static_assert(nibble_of_col(0) == 0 && nibble_of_col(1) == 4 && nibble_of_col(2) == 1 && nibble_of_col(3) == 5 &&
+              nibble_of_col(4) == 2 && nibble_of_col(5) == 6 && nibble_of_col(6) == 3 && nibble_of_col(7) == 7,
+              "column->nibble table");
+
+__device__ __forceinline__ uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+
+// Interleave byte t of two words a (row r) and b (row r+1): result bytes are
+// [a.t, 0, b.t, 0], so the low nibbles of byte t sit in bits 0-3 / 16-19 and the
+// high nibbles in bits 4-7 / 20-23 of the two 16-bit halves.
+template <int t>
+__device__ __forceinline__ uint32_t pair_byte(uint32_t a, uint32_t b) {
+  constexpr uint32_t sel = (uint32_t)t | (0x0Cu << 8) | ((uint32_t)(4 + t) << 16) | (0x0Cu << 24);
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// fp16 pair (1024 + lo_a, 1024 + lo_b): the nibble ORed into the mantissa of 1024.0
+// (0x6400) gives the integer exactly, since 1024..2047 are exact in fp16.
+__device__ __forceinline__ half2v lo_magic(uint32_t p) { return as_h2((p & 0x000F000Fu) | 0x64006400u); }
+// fp16 pair (1024 + 16*hi_a, 1024 + 16*hi_b), also exact.
+__device__ __forceinline__ half2v hi_magic(uint32_t p) { return as_h2((p & 0x00F000F0u) | 0x64006400u); }
+
+// (code - zero) as exact small fp16 integers from the magic forms.
+//   lo: (1024 + q) - (1024 + z)                      one packed add
+//   hi: (1024 + 16 q) / 16 - (64 + z) = q - z         one packed fma, exact
+__device__ __forceinline__ half2v lo_minus_zero(uint32_t p, half2v neg_1024_plus_z) {
+  return lo_magic(p) + neg_1024_plus_z;
+}
+__device__ __forceinline__ half2v hi_minus_zero(uint32_t p, half2v neg_64_plus_z) {
+  const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  return __builtin_elementwise_fma(hi_magic(p), sixteenth, neg_64_plus_z);
+}
+
+// Zero code of column j of a packed zero word.
+__device__ __forceinline__ uint32_t zero_code(uint32_t zw, int j) {
+  return (zw >> (4 * nibble_of_col(j))) & 0xFu;
+}
+
+__device__ __forceinline__ half2v splat(_Float16 v) { return half2v{v, v}; }
+
+}  // namespace awq

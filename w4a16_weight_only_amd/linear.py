@@ -1,0 +1,148 @@
+"""Python boundary of the AWQ W4A16 linear: torch tensors in, C ABI calls out.
+
+torch supplies device memory and the current stream; every arithmetic step runs
+in libawq_w4a16.so.  Tensor layouts are the AWQ GEMM checkpoint layout
+(tensref.org "AWQ" format page; GPTQModel wiki "AWQ", "Saved formats and packing"):
+qweight int32 [K, N/8], qzeros int32 [G, N/8], scales fp16 [G, N], bias fp16 [N].
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(name, t, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def group_size_from_config(cfg: dict) -> int:
+    """Accept a checkpoint's quantization_config for the 4-bit GEMM layout and return
+    its group size.  Bit width and group size come from this metadata, not from the
+    tensors (tensref.org "AWQ" format page, introduction); AWQ keeps zero points even
+    for symmetric quantization (GPTQModel wiki "AWQ", "Group quantization and zero
+    points"), so a config without zero points is not this layout."""
+    method = str(cfg.get("quant_method", "awq")).lower()
+    if method != "awq":
+        raise ValueError(f"quant_method {method!r} is not awq")
+    if int(cfg.get("bits", cfg.get("w_bit", 4))) != 4:
+        raise ValueError("only 4-bit AWQ is supported")
+    fmt = str(cfg.get("version", cfg.get("format", "gemm"))).lower()
+    if fmt != "gemm":
+        raise ValueError(f"checkpoint format {fmt!r} is not the GEMM layout")
+    if not cfg.get("zero_point", True):
+        raise ValueError("GEMM-layout AWQ checkpoints carry zero points")
+    return int(cfg.get("group_size", cfg.get("q_group_size", 128)))
+
+
+def validate(K: int, N: int, group_size: int, qweight, qzeros, scales, bias=None) -> None:
+    """Format rules of the GEMM pack, checked by the library (host-only)."""
+    lib = _lib.load()
+    st = lib.awq_validate_pack(K, N, group_size, *qweight.shape, *qzeros.shape, *scales.shape,
+                               -1 if bias is None else bias.numel())
+    _lib.check(st, "awq_validate_pack")
+
+
+def plan(M: int, K: int, N: int, group_size: int) -> dict:
+    """The launch plan awq_gemm uses for a shape (host-only)."""
+    lib = _lib.load()
+    vals = [ctypes.c_int() for _ in range(5)]
+    ws = ctypes.c_int64()
+    st = lib.awq_gemm_plan(M, K, N, group_size, *[ctypes.byref(v) for v in vals], ctypes.byref(ws))
+    _lib.check(st, "awq_gemm_plan")
+    fam, splits, gx, gy, block = (v.value for v in vals)
+    return dict(family="skinny" if fam == 0 else "tile", splits=splits, grid=(gx, gy), block=block,
+                workspace_bytes=ws.value)
+
+
+def awq_dequant(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
+                group_size: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """float32 [K, N] = (q - z) * s, bit-exact."""
+    _check_tensor("qweight", qweight, torch.int32)
+    dev = qweight.device
+    _check_tensor("qzeros", qzeros, torch.int32, dev)
+    _check_tensor("scales", scales, torch.float16, dev)
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    validate(K, N, group_size, qweight, qzeros, scales)
+    if out is None:
+        out = torch.empty((K, N), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, torch.float32, dev)
+        if tuple(out.shape) != (K, N):
+            raise ValueError(f"out must be [{K}, {N}]")
+    with torch.cuda.device(dev):
+        st = _lib.load().awq_dequant(_ptr(qweight), _ptr(qzeros), _ptr(scales), K, N, group_size,
+                                     _ptr(out), _stream(dev))
+    _lib.check(st, "awq_dequant")
+    return out
+
+
+def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
+             bias: torch.Tensor | None = None, group_size: int = 128,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . dequant(W) + bias in fp16 with fp32 accumulation.
+
+    x may have leading dimensions; they are flattened into rows (as the pages'
+    kernels do) and restored on the output."""
+    _check_tensor("x", x, torch.float16)
+    dev = x.device
+    _check_tensor("qweight", qweight, torch.int32, dev)
+    _check_tensor("qzeros", qzeros, torch.int32, dev)
+    _check_tensor("scales", scales, torch.float16, dev)
+    if bias is not None:
+        _check_tensor("bias", bias, torch.float16, dev)
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} input features, qweight has {K}")
+    validate(K, N, group_size, qweight, qzeros, scales, bias)
+    lead = tuple(x.shape[:-1])
+    M = 1
+    for d in lead:
+        M *= d
+    if out is None:
+        out = torch.empty(lead + (N,), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != lead + (N,):
+            raise ValueError(f"out must be {lead + (N,)}")
+    with torch.cuda.device(dev):
+        st = _lib.load().awq_gemm(_ptr(x), _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(bias),
+                                  M, K, N, group_size, _ptr(out), _stream(dev))
+    _lib.check(st, "awq_gemm")
+    return out
+
+
+class AwqLinear(torch.nn.Module):
+    """Inference-only linear layer holding one AWQ GEMM-layout weight."""
+
+    def __init__(self, qweight, qzeros, scales, bias=None, group_size=128):
+        super().__init__()
+        self.register_buffer("qweight", qweight)
+        self.register_buffer("qzeros", qzeros)
+        self.register_buffer("scales", scales)
+        self.register_buffer("bias", bias)
+        self.group_size = group_size
+        self.in_features = qweight.shape[0]
+        self.out_features = qweight.shape[1] * 8
+
+    def forward(self, x):
+        return awq_gemm(x.contiguous(), self.qweight, self.qzeros, self.scales, self.bias, self.group_size)
