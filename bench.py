@@ -1,0 +1,233 @@
+"""Benchmark of the fused AWQ W4A16 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one awq_gemm call (dispatch by M, packed-weight streaming, unpack,
+dequant, multiply-accumulate, reduction, bias, fp16 store) on the workload's
+synthetic layer.  Inputs are resident in HBM before timing starts.  The packed
+weights are rotated over independent copies totalling >= 512 MB, so every step
+reads its weights from HBM rather than from the 256 MB Infinity Cache.  The K
+timed steps are captured once into a HIP graph and replayed, so the host's
+per-call Python overhead is not what is measured; the graph's output is checked
+bit for bit against an eager call.
+
+Prints one JSON line.  `value` is the achieved algorithmic HBM bandwidth (GB/s)
+for the bandwidth-bound workloads or TFLOP/s for the compute-bound prefill
+workload, over the whole timed region.  `roofline` prices the kernel's average
+launch duration (HIP events on the launch stream over the timed region) against
+MI355X's peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP16_MFMA_PEAK_TFS = 2500.0  # MI355X dense fp16 MFMA
+ROTATE_BYTES = 512 << 20     # > 2x the 256 MB Infinity Cache
+HEADLINE = "decode_m1_k4096_n4096_g128"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the M=16 and M=2048 workloads (reported under 'secondary')")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a16_weight_only_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_workload(name, steps, warmup, torch, awq, synth):
+    w = synth.WORKLOADS[name]
+    d = synth.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    layer_bytes = d["qweight"].nbytes + d["qzeros"].nbytes + d["scales"].nbytes
+    copies = max(1, -(-ROTATE_BYTES // layer_bytes))
+    x = torch.from_numpy(d["x"]).to(dev)
+    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+    weights = []
+    for i in range(copies):
+        # Independent buffers with identical contents: the same layer, fresh addresses.
+        weights.append(tuple(torch.from_numpy(d[k]).to(dev) for k in ("qweight", "qzeros", "scales")))
+    y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    g = w.group_size
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        qw, qz, sc = weights[i % copies]
+        awq.awq_gemm(x, qw, qz, sc, bias, g, out=y)
+
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 1)):  # eager warm-up; allocates the split-K workspace
+            step(i)
+        eager = y.clone()
+    stream.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()  # untimed replay: graph upload and first-touch
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall_s = t1 - t0
+    event_s = ev0.elapsed_time(ev1) / 1e3
+    if not torch.equal(y.view(torch.int16), eager.view(torch.int16)):
+        raise RuntimeError("graph replay output differs from the eager call")
+    del weights
+    torch.cuda.empty_cache()
+    return dict(workload=w, wall_s=wall_s, event_s=event_s, copies=copies,
+                plan=awq.plan(w.M, w.K, w.N, w.group_size))
+
+
+def summarize(r, steps):
+    w = r["workload"]
+    ab = w.algorithmic_bytes()
+    fl = w.flops()
+    per_launch_s = r["event_s"] / steps
+    compute_bound = w.M >= 512
+    if compute_bound:
+        value = fl * steps / r["wall_s"] / 1e12
+        achieved = fl / per_launch_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=FP16_MFMA_PEAK_TFS, unit="TFLOP/s",
+                    frac=round(achieved / FP16_MFMA_PEAK_TFS, 4))
+        unit = "TFLOP/s"
+    else:
+        value = ab * steps / r["wall_s"] / 1e9
+        achieved = ab / per_launch_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+        unit = "GB/s"
+    return value, unit, roof, per_launch_s
+
+
+def cpu_baseline(name, synth):
+    """The CPU oracle on the same workload: a bounded number of full-layer calls."""
+    from oracle import awq_ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    w = synth.WORKLOADS[name]
+    d = synth.make_inputs(w)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        awq_ref.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], w.group_size)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 5:
+            break
+    per = el / reps
+    if w.M >= 512:
+        value, unit = w.flops() / per / 1e12, "TFLOP/s"
+    else:
+        value, unit = w.algorithmic_bytes() / per / 1e9, "GB/s"
+    return dict(value=round(value, 4), unit=unit, cores=int(blas_threads), kind="oracle",
+                sample=f"{reps} full calls of the {name} layer (unpack, fp32 dequant, fp64 matmul), "
+                       f"{per:.2f} s each; numpy elementwise on 1 thread, BLAS on {blas_threads}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a "
+              f"single MI355X and has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(1)
+    import w4a16_weight_only_amd as awq
+    from w4a16_weight_only_amd import synth
+    awq.load_library()
+
+    r = time_workload(args.workload, args.steps, args.warmup, torch, awq, synth)
+    value, unit, roof, per_launch_s = summarize(r, args.steps)
+    digest = kernel_source_digest()
+    roof["traffic"] = load_traffic(args.workload, digest)
+    w = r["workload"]
+    out = {
+        "metric": "awq_gemm achieved HBM GB/s (M=1,16) and TFLOP/s (M=2048), % of roofline",
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_s"] / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 x / int4 weights / fp32 accumulate",
+        "data": "synthetic (seeded; random packed words, fp16 scales U[1e-3,2e-2], x ~ N(0,1))",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
+                   "bias": w.bias, "algorithmic_bytes": w.algorithmic_bytes(), "flops": w.flops(),
+                   "plan": r["plan"], "weight_copies_rotated": r["copies"],
+                   "timing": "HIP graph of all steps, wall clock over one replay"},
+        "roofline": roof,
+        "kernel_avg_us": round(per_launch_s * 1e6, 3),
+        "source_digest": digest,
+    }
+    if args.secondary:
+        sec = []
+        for name in ("decode_m16_k4096_n11008_g128", "prefill_m2048_k4096_n4096_g128"):
+            if name == args.workload:
+                continue
+            rs = time_workload(name, min(args.steps, 400), 10, torch, awq, synth)
+            v, u, rf, pl = summarize(rs, min(args.steps, 400))
+            sec.append(dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3),
+                            roofline=rf))
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

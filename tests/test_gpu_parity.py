@@ -95,6 +95,8 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (130, 256, 416, -1, True),
     (257, 512, 256, 128, False),
     (64, 1024, 4128, 128, True),
+    (1, 131072, 64, -1, True),   # skinny at the 128-split cap, 64 k-steps per wave
+    (3, 65536, 96, 32, True),    # too many groups per workgroup for skinny: tile family
 ]
 
 

@@ -39,11 +39,10 @@ int limits_check(int64_t M, int64_t K, int64_t N, int64_t group_size) {
 
 struct Plan {
   int family = 0;  // 0 skinny, 1 tile
-  int splits = 1;
+  awq::SkinnyPlan sk{};
   int grid_x = 0, grid_y = 0, block = 0;
-  int mrows = 0;
-  int64_t partial_bytes = 0, counter_bytes = 0;
-  int64_t workspace_bytes() const { return partial_bytes ? partial_bytes + counter_bytes : 0; }
+  int64_t accum_bytes = 0;
+  int64_t workspace_bytes() const { return accum_bytes; }
 };
 
 // Compute units of the current device (cached per device ordinal).
@@ -62,28 +61,61 @@ int device_cus() {
   return cus;
 }
 
-Plan make_plan(int64_t M, int64_t K, int64_t N, int cus) {
-  Plan p;
-  if (M <= awq::kSkinnyMaxM) {
-    p.family = 0;
-    p.block = awq::kSkinnyThreads;
-    const int n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
-    const int T = (int)(K / awq::kKStep);
-    // Aim for about two workgroups per compute unit, while every wave keeps at
-    // least one k-step.
-    const int target = 2 * cus;
-    int s = (target + n_tiles - 1) / n_tiles;
-    const int cap = T / 4 > 0 ? T / 4 : 1;
-    if (s > cap) s = cap;
-    if (s < 1) s = 1;
-    p.splits = s;
-    p.grid_x = n_tiles;
-    p.grid_y = s;
-    p.mrows = M <= 4 ? 4 : 16;
-    if (s > 1) {
-      p.counter_bytes = ((int64_t)n_tiles * 4 + 255) / 256 * 256;
-      p.partial_bytes = (int64_t)n_tiles * s * p.mrows * awq::kSkinnyCols * 4;
+#ifndef AWQ_SKINNY_WG_PER_CU
+#define AWQ_SKINNY_WG_PER_CU 2  // resident 4-wave workgroups per compute unit
+#endif
+
+// Skinny plan for M <= kSkinnyMaxM, or false when no launch shape fits the
+// kernel's limits (at most kSkinnyMaxSplits splits, at most kSkinnyMaxGroups
+// quantization groups per workgroup).
+bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::SkinnyPlan& s) {
+  const int64_t T = K / awq::kKStep;
+  const int64_t gsteps = g / awq::kKStep;  // g already resolved (-1 -> K)
+  s.n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
+  s.waves = M <= 4 ? 4 : 8;
+  s.mrows = M <= 4 ? 4 : 16;
+  const int64_t W = s.waves;
+  // Whole grid resident in one round: 4-wave workgroups fit AWQ_SKINNY_WG_PER_CU per
+  // CU, 8-wave ones (large LDS reduction buffer) one per CU.
+  const int64_t cap = (int64_t)cus * (s.waves == 4 ? AWQ_SKINNY_WG_PER_CU : 1);
+  int64_t L = (T * s.n_tiles + W * cap - 1) / (W * cap);
+  const int64_t l_min = (T + W * awq::kSkinnyMaxSplits - 1) / (W * awq::kSkinnyMaxSplits);
+  if (L < l_min) L = l_min;
+  if (L < 1) L = 1;
+  if (L > T) L = T;
+  auto splits_of = [&](int64_t l) { return (T + W * l - 1) / (W * l); };
+  if (gsteps >= T) {
+    s.single_group = true;  // one group spans K
+  } else if (L <= gsteps) {
+    while (gsteps % L != 0) ++L;  // stays <= gsteps: each wave's run in one group
+    s.single_group = true;
+  } else {
+    s.single_group = false;
+    // A workgroup's run of W*L steps may touch at most kSkinnyMaxGroups groups.
+    if ((W * L - 1) / gsteps + 2 > awq::kSkinnyMaxGroups) {
+      int64_t l2 = ((int64_t)(awq::kSkinnyMaxGroups - 2) * gsteps + 1) / W;
+      if (l2 < 1) l2 = 1;
+      if (l2 <= gsteps) {
+        while (gsteps % l2 != 0) --l2;
+        s.single_group = true;
+      }
+      L = l2;
     }
+  }
+  if (splits_of(L) > awq::kSkinnyMaxSplits) return false;
+  s.L = (int)L;
+  s.splits = (int)splits_of(L);
+  return true;
+}
+
+Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
+  Plan p;
+  if (M <= awq::kSkinnyMaxM && plan_skinny(M, K, N, g, cus, p.sk)) {
+    p.family = 0;
+    p.grid_x = p.sk.n_tiles;
+    p.grid_y = p.sk.splits;
+    p.block = 64 * p.sk.waves;
+    if (p.sk.splits > 1) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
   } else {
     p.family = 1;
     p.block = awq::kTileThreads;
@@ -95,47 +127,42 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int cus) {
   return p;
 }
 
-// Library-owned split-K workspace, one per (device, stream).  Counters sit at the
-// front and must be zero between calls (each reduction resets its own).
+// Library-owned split-K workspace, one per (device, stream): 64-bit fixed-point
+// accumulators, zeroed once at allocation and left zero by every call.  Growing it
+// frees the old buffer after the stream drains.
 struct Workspace {
   void* ptr = nullptr;
   int64_t bytes = 0;
-  int64_t counter_bytes = 0;
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(const Plan& p, hipStream_t stream, float** partial, uint32_t** counters) {
+int get_workspace(const Plan& p, hipStream_t stream, uint64_t** accum) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& ws = g_ws[{dev, stream}];
-  // Counters need p.counter_bytes at the front; partials follow.  Keep the counter
-  // region at least as large as any earlier one so old counters stay zero.
-  const int64_t cb = p.counter_bytes > ws.counter_bytes ? p.counter_bytes : ws.counter_bytes;
-  const int64_t need = cb + p.partial_bytes;
-  if (ws.ptr == nullptr || need > ws.bytes || cb > ws.counter_bytes) {
+  const int64_t need = p.accum_bytes;
+  if (ws.ptr == nullptr || need > ws.bytes) {
     if (ws.ptr) {
-      // Work already queued on this stream may still read the old buffer.
+      // Work already queued on this stream may still use the old buffer.
       if (hipStreamSynchronize(stream) != hipSuccess) return AWQ_ERR_HIP;
       if (hipFree(ws.ptr) != hipSuccess) return AWQ_ERR_HIP;
       ws.ptr = nullptr;
       ws.bytes = 0;
     }
-    int64_t bytes = need + need / 4;  // headroom against frequent regrowth
+    const int64_t bytes = need + need / 4;  // headroom against frequent regrowth
     void* ptr = nullptr;
     if (hipMalloc(&ptr, (size_t)bytes) != hipSuccess) return AWQ_ERR_HIP;
-    if (hipMemset(ptr, 0, (size_t)cb) != hipSuccess) {
+    if (hipMemset(ptr, 0, (size_t)bytes) != hipSuccess) {
       (void)hipFree(ptr);
       return AWQ_ERR_HIP;
     }
     ws.ptr = ptr;
     ws.bytes = bytes;
-    ws.counter_bytes = cb;
   }
-  *counters = reinterpret_cast<uint32_t*>(ws.ptr);
-  *partial = reinterpret_cast<float*>(reinterpret_cast<char*>(ws.ptr) + ws.counter_bytes);
+  *accum = reinterpret_cast<uint64_t*>(ws.ptr);
   return AWQ_OK;
 }
 
@@ -183,9 +210,9 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* fami
   int count = 0;
   if (hipGetDeviceCount(&count) == hipSuccess && count > 0) cus = device_cus();
   else (void)hipGetLastError();
-  const Plan p = make_plan(M, K, N, cus);
+  const Plan p = make_plan(M, K, N, eff_group(K, group_size), cus);
   if (family) *family = p.family;
-  if (splits) *splits = p.splits;
+  if (splits) *splits = p.family == 0 ? p.sk.splits : 1;
   if (grid_x) *grid_x = p.grid_x;
   if (grid_y) *grid_y = p.grid_y;
   if (block) *block = p.block;
@@ -215,22 +242,20 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
   if (!aligned16(x_f16) || !aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16) ||
       !aligned16(y_f16) || (bias_f16 && !aligned16(bias_f16)))
     return AWQ_ERR_ALIGN;
-  const Plan p = make_plan(M, K, N, device_cus());
+  const int g = eff_group(K, group_size);
+  const Plan p = make_plan(M, K, N, g, device_cus());
   const auto* x = static_cast<const uint16_t*>(x_f16);
   const auto* sc = static_cast<const uint16_t*>(scales_f16);
   const auto* b = static_cast<const uint16_t*>(bias_f16);
   auto* y = static_cast<uint16_t*>(y_f16);
-  const int g = eff_group(K, group_size);
   hipError_t e;
   if (p.family == 0) {
-    float* partial = nullptr;
-    uint32_t* counters = nullptr;
-    if (p.splits > 1) {
-      const int ws = get_workspace(p, stream, &partial, &counters);
+    uint64_t* accum = nullptr;
+    if (p.sk.splits > 1) {
+      const int ws = get_workspace(p, stream, &accum);
       if (ws != AWQ_OK) return ws;
     }
-    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.splits, partial,
-                           counters, y, stream);
+    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, y, stream);
   } else {
     e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, y, stream);
   }

@@ -13,6 +13,18 @@ constexpr int kSkinnyWordCols = 32;
 constexpr int kSkinnyCols = 8 * kSkinnyWordCols;
 constexpr int kKStep = 32;
 constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxGroups = 16;  // quantization groups one workgroup may touch
+constexpr int kSkinnyMaxSplits = 128;  // fixed-point accumulators hold up to 128 arrivals
+
+// Launch plan of the skinny family (chosen on the host, see awq_api.hip).
+struct SkinnyPlan {
+  int n_tiles;       // column tiles of kSkinnyCols
+  int splits;        // K splits across workgroups (grid y)
+  int L;             // k-steps per wave
+  int waves;         // 4 (M <= 4) or 8 (M <= 16) waves per workgroup
+  int mrows;         // rows kept per tile: 4 or 16
+  bool single_group; // every wave's k-steps lie in one quantization group
+};
 
 // MFMA tile family geometry.
 constexpr int kTileM = 128;
@@ -23,11 +35,11 @@ constexpr int kTileThreads = 256;
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, float* out, hipStream_t stream);
 
-// partial: [n_tiles][splits][mrows][256] fp32; counters: [n_tiles] uint32, zero on entry.
+// accum: [n_tiles][mrows * 256] 64-bit accumulators, zero before the first call and
+// left zero by the kernel itself (unused when p.splits == 1).
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         int splits, float* partial, uint32_t* counters, uint16_t* y,
-                         hipStream_t stream);
+                         const SkinnyPlan& p, uint64_t* accum, uint16_t* y, hipStream_t stream);
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,

@@ -5,29 +5,43 @@
 // small-batch decode is limited by weight bandwidth, so the packed weight is read
 // once and expanded only in registers).
 //
-// Per workgroup (256 threads, 4 waves): 32 packed word-columns (256 output columns,
-// 128 contiguous bytes of every qweight row) times a contiguous run of 32-row
-// k-steps.  Each wave takes a contiguous sub-run of those k-steps.
+// Work split.  A workgroup (4 or 8 waves) owns a column tile of 32 packed word-columns
+// (256 output columns = 128 contiguous bytes of every qweight row) and a run of
+// WAVES*L 32-row k-steps; wave w takes L consecutive k-steps of that run.  The host
+// picks L and the number of K splits S so that the whole grid is resident at once.
+// At a few microseconds per call the kernel is latency-bound, so every input is
+// requested up front: each wave issues the weight loads of its first two k-steps,
+// and the workgroup turns the zero words and scales of every group it touches into
+// per-lane LDS tables (fp16 zero splats, fp32 scales) in the same round trip.
 //
 // Per wave and k-step, on v_mfma_f32_16x16x32_f16 (x rows padded to 16):
 //   lane l: q = l / 16 picks rows 8q..8q+7 of the k-step, c = l % 16 picks word
-//   columns 2c, 2c+1 of the tile.  The lane loads 8 rows x 8 bytes (one 8-byte
-//   load per row; 16 lanes cover 128 contiguous bytes of a row).
-//   From each pair of rows, v_perm_b32 interleaves byte t of both words, and the
-//   0x6400 mantissa trick turns each nibble pair into an exact fp16 pair
-//   (code + 1024) or (16 code + 1024); one packed add / fma subtracts the zero,
-//   leaving the exact integers (q - z) for rows (r, r+1) of one column.  Four such
-//   pairs form the B operand (8 consecutive k of one column) of one MFMA.
-//   Each lane's 16 columns give 16 MFMAs; lane c of the MFMA is column
-//   8 (tile_wc + 2c + w) + j.  The A operand is x[m = l % 16][8q..8q+7].
-//   Products fp16 x integer are exact in fp32; the MFMA sums in fp32.
-// Groups: the MFMA accumulates sum_k x (q - z) per group in `part`; at the end of
-// each group it is scaled by s (fp32) into `acc`.  Group boundaries fall on
-// k-step boundaries (g % 32 == 0).
-// Reduction: waves -> LDS (fixed order), then across the K splits of a column tile
-// through a workspace: each workgroup stores its partial, the last to arrive (device
-// counter) sums all splits in split order, adds bias, rounds once to fp16 and
-// stores y, then resets the counter.  The result does not depend on timing.
+//   columns 2c, 2c+1 of the tile; one 8-byte load per row (16 lanes cover 128
+//   contiguous bytes of a row).  From each pair of rows, v_perm_b32 interleaves byte
+//   t of both words, the 0x6400 mantissa trick turns each nibble pair into an exact
+//   fp16 pair (code + 1024) or (16 code + 1024), and one packed add / fma removes the
+//   zero, leaving the exact integers (q - z) of rows (r, r+1) of one column.  Four
+//   pairs form one B operand (8 consecutive k of one column).  The lane's 16 columns
+//   give 16 MFMAs; MFMA column c is output column 8 (tile_wc + 2c + w) + j.  The A
+//   operand is x[m = l % 16][8q..8q+7].  fp16 x times a small integer is exact in
+//   fp32 and the MFMA accumulates in fp32.
+// Groups: the MFMA accumulates sum_k x (q - z) per group; at the end of a group the
+// sum is scaled by s in fp32 (exact dequant, no fp16 weight rounding).
+// Reduction: the waves' accumulators meet in LDS in register order (conflict-free
+// 16-byte accesses) and are summed in wave order.  With S > 1 splits, the splits of
+// an output element meet in one 64-bit accumulator in the workspace: each workgroup
+// adds, with one relaxed atomic fetch-add, its partial as a fixed-point integer
+// (24 fractional bits) plus 2^56, i.e. one arrival in the top byte.  Integer
+// addition does not depend on order, so the sum is bit-reproducible; the add that
+// brings the arrival count to S returns the complete sum to its workgroup, which
+// converts it, adds bias, rounds once to fp16, stores y and resets the accumulator
+// to zero for the next call (graph replays included).  One round trip to the
+// atomic units and no cross-workgroup reads or fences.
+// Fixed point: every fp16 value is a multiple of 2^-24, so a single exact product
+// (an identity input row, an integer weight) survives unchanged; sums are kept to
+// 2^-24 absolute, finer than fp32's rounding for |partial| > 1.  Partials are
+// clamped to +-2^23 so up to 128 splits can never carry into the count byte; a
+// partial that large would already exceed fp16's range by a factor of 128.
 #include "awq_device.h"
 #include "awq_kernels.h"
 
@@ -35,23 +49,29 @@ namespace awq {
 
 namespace {
 
-struct WordPair {
-  uint32_t w0, w1;
-};
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ WordPair load_pair(const uint32_t* p, bool ok) {
-  if (!ok) return WordPair{0u, 0u};
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  return WordPair{v.x, v.y};
-}
+struct Step {
+  u32x2 v[8];  // rows 8q..8q+7, words (2c, 2c+1)
+  half8v a;    // x[m][8q..8q+7] of this k-step
+};
 
 __device__ __forceinline__ half8v pack4(half2v a, half2v b, half2v c, half2v d) {
   return half8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Run the 16 MFMAs of one k-step for one lane's 2 word-columns.
-__device__ __forceinline__ void kstep_mfma(const WordPair (&v)[8], half8v a, const half2v (&zlo)[2][4],
-                                           const half2v (&zhi)[2][4], floatx4 (&part)[2][8]) {
+// Entry v of a lane's 16-entry tables and accumulators: word w = v / 8, byte
+// t = (v / 2) % 4, nibble half h = v % 2 (0: low nibble, column lo_col(t);
+// 1: high nibble, column hi_col(t)).
+__host__ __device__ constexpr int tab_idx(int w, int t, int h) { return w * 8 + 2 * t + h; }
+__host__ __device__ constexpr int tab_col(int v) {  // column within the word
+  return (v & 1) ? hi_col((v >> 1) & 3) : lo_col((v >> 1) & 3);
+}
+
+// The 16 MFMAs of one k-step for one lane's 2 word-columns.  zs holds, per entry,
+// the fp16 splat to add: -(1024 + z) for low-nibble columns, -(64 + z) for
+// high-nibble columns.
+__device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[16], floatx4 (&part)[16]) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
@@ -59,37 +79,55 @@ __device__ __forceinline__ void kstep_mfma(const WordPair (&v)[8], half8v a, con
       half2v lo[4], hi[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t ra = w ? v[2 * p].w1 : v[2 * p].w0;
-        const uint32_t rb = w ? v[2 * p + 1].w1 : v[2 * p + 1].w0;
+        const uint32_t ra = st.v[2 * p][w];
+        const uint32_t rb = st.v[2 * p + 1][w];
         uint32_t pb;
         if (t == 0) pb = pair_byte<0>(ra, rb);
         else if (t == 1) pb = pair_byte<1>(ra, rb);
         else if (t == 2) pb = pair_byte<2>(ra, rb);
         else pb = pair_byte<3>(ra, rb);
-        lo[p] = lo_minus_zero(pb, zlo[w][t]);
-        hi[p] = hi_minus_zero(pb, zhi[w][t]);
+        lo[p] = lo_minus_zero(pb, as_h2(zs[tab_idx(w, t, 0)]));
+        hi[p] = hi_minus_zero(pb, as_h2(zs[tab_idx(w, t, 1)]));
       }
-      part[w][lo_col(t)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pack4(lo[0], lo[1], lo[2], lo[3]),
-                                                                  part[w][lo_col(t)], 0, 0, 0);
-      part[w][hi_col(t)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pack4(hi[0], hi[1], hi[2], hi[3]),
-                                                                  part[w][hi_col(t)], 0, 0, 0);
+      const int il = tab_idx(w, t, 0), ih = tab_idx(w, t, 1);
+      part[il] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a, pack4(lo[0], lo[1], lo[2], lo[3]), part[il], 0, 0, 0);
+      part[ih] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a, pack4(hi[0], hi[1], hi[2], hi[3]), part[ih], 0, 0, 0);
     }
   }
 }
 
+// LDS tables: per group and lane column c, 16 entries padded to 20 words (spreads
+// the 16-byte reads of the 16 column lanes over the banks).
+constexpr int kTabStride = 20;
+
+template <int WAVES>
+struct SkinnyLds {
+  union {
+    struct {
+      uint32_t zsplat[kSkinnyMaxGroups][16][kTabStride];
+      float scale[kSkinnyMaxGroups][16][kTabStride];
+    } meta;
+    floatx4 red[WAVES][16][64];  // [wave][accumulator][lane]
+  } u;
+};
+
 }  // namespace
 
-template <int MROWS>
-__global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(
+// Workspace: per tile, 64-bit accumulator 4 * slot + i holds row 4 (slot / 256) + i
+// of the slot's column, slot = q * 256 + accumulator * 16 + c.  All zero between calls.
+template <int WAVES, int MROWS, bool SINGLE>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const _Float16* __restrict__ bias, int M, int K, int N, int g, int splits,
-    float* __restrict__ partial, uint32_t* __restrict__ counters, _Float16* __restrict__ y) {
-  __shared__ float red[4][MROWS][kSkinnyCols];
-  __shared__ int is_last;
+    const _Float16* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
+    uint64_t* __restrict__ accum, _Float16* __restrict__ y) {
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
+  __shared__ SkinnyLds<WAVES> sh;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int q = lane >> 4;
   const int c = lane & 15;
   const int NW = N >> 3;
@@ -98,159 +136,207 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_kernel(
   const int wc = tile * kSkinnyWordCols + 2 * c;
   const bool col_ok = wc < NW;  // NW % 4 == 0, so wc + 1 < NW as well
 
-  // k-steps of this workgroup, then of this wave (contiguous runs).
+  // k-steps: workgroup run [s0, s1), wave run [kb, ke).
   const int T = K / kKStep;
-  const int s0 = (int)((int64_t)T * split / splits);
-  const int s1 = (int)((int64_t)T * (split + 1) / splits);
-  const int L = s1 - s0;
-  const int kb = s0 + (L * wave) / 4;
-  const int ke = s0 + (L * (wave + 1)) / 4;
+  const int s0 = split * WAVES * L;
+  const int s1 = min(T, s0 + WAVES * L);
+  const int kb = min(s1, s0 + wave * L);
+  const int ke = min(s1, kb + L);
+  const int gsteps = g / kKStep;
+  const int g0 = s0 / gsteps;
 
   const int m = lane & 15;
   const bool row_ok = m < M;
-  const _Float16* xrow = x + (int64_t)m * K + 8 * q;
-  const uint32_t* wbase = qweight + (int64_t)(8 * q) * NW + wc;
+  const _Float16* xrow = x + (int64_t)(row_ok ? m : 0) * K + 8 * q;
+  const uint32_t* wbase = qweight + (int64_t)(8 * q) * NW + (col_ok ? wc : 0);
 
-  floatx4 acc[2][8];
-  floatx4 part[2][8];
+  // Branch-free loads: an invalid step, row or column reads a valid address and is
+  // masked to zero.
+  auto issue = [&](Step& st, int ks) {
+    const bool ok = ks < ke;
+    const int kr = min(ks, T - 1) * kKStep;
+    const bool wok = ok && col_ok;
 #pragma unroll
-  for (int w = 0; w < 2; ++w)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[w][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-      part[w][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 8; ++r) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wbase + (int64_t)(kr + r) * NW));
+      st.v[r] = wok ? v : u32x2{0u, 0u};
     }
-
-  half2v zlo[2][4], zhi[2][4];
-  int cur_g = -1;
-
-  auto flush = [&](int gi) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      u32x4 sv = u32x4{0u, 0u, 0u, 0u};
-      if (col_ok) sv = *reinterpret_cast<const u32x4*>(scales + (int64_t)gi * N + 8 * (wc + w));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)((sv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
-        acc[w][j] += s * part[w][j];
-        part[w][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  auto load_zeros = [&](int gi) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t zw = col_ok ? qzeros[(int64_t)gi * NW + wc + w] : 0u;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        zlo[w][t] = splat(-(_Float16)(float)(1024u + zero_code(zw, lo_col(t))));
-        zhi[w][t] = splat(-(_Float16)(float)(64u + zero_code(zw, hi_col(t))));
-      }
-    }
+    const half8v a = *reinterpret_cast<const half8v*>(xrow + kr);
+    st.a = (ok && row_ok) ? a : half8v{0, 0, 0, 0, 0, 0, 0, 0};
   };
 
-  WordPair v[8];
-  half8v a = half8v{0, 0, 0, 0, 0, 0, 0, 0};
-  if (kb < ke) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = load_pair(wbase + (int64_t)(kb * kKStep + r) * NW, col_ok);
-    if (row_ok) a = *reinterpret_cast<const half8v*>(xrow + kb * kKStep);
-  }
-  for (int ks = kb; ks < ke; ++ks) {
-    const int gi = (ks * kKStep) / g;
-    if (gi != cur_g) {
-      if (cur_g >= 0) flush(cur_g);
-      load_zeros(gi);
-      cur_g = gi;
-    }
-    // Issue the next k-step's loads before this step's arithmetic.
-    WordPair vn[8];
-    half8v an = half8v{0, 0, 0, 0, 0, 0, 0, 0};
-    const bool more = ks + 1 < ke;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      vn[r] = load_pair(wbase + (int64_t)((ks + 1) * kKStep + r) * NW, col_ok && more);
-    if (row_ok && more) an = *reinterpret_cast<const half8v*>(xrow + (ks + 1) * kKStep);
-
-    kstep_mfma(v, a, zlo, zhi, part);
-
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = vn[r];
-    a = an;
-  }
-  if (cur_g >= 0) flush(cur_g);
-
-  // Wave partials -> LDS.  MFMA 16x16 output: lane l holds rows 4(l/16)+i, column l%16.
-#pragma unroll
-  for (int w = 0; w < 2; ++w)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * q + i;
-        if (row < MROWS) red[wave][row][8 * (2 * c + w) + j] = acc[w][j][i];
+  // 1. Weight loads of the first two k-steps; group tables into LDS meanwhile.
+  Step cur, nxt;
+  issue(cur, kb);
+  issue(nxt, kb + 1);
+  {
+    const int ng = (s1 > s0) ? (s1 - 1) / gsteps - g0 + 1 : 0;  // <= kSkinnyMaxGroups (host)
+    for (int i = tid; i < ng * 256; i += THREADS) {
+      const int gl = i >> 8, cc = (i >> 4) & 15, v = i & 15;
+      const int wcol = tile * kSkinnyWordCols + 2 * cc + (v >> 3);
+      const int col = tab_col(v);
+      uint32_t zw = 0u;
+      float s = 0.f;
+      if (wcol < NW) {
+        zw = qzeros[(int64_t)(g0 + gl) * NW + wcol];
+        s = (float)scales[(int64_t)(g0 + gl) * N + 8 * wcol + col];
       }
+      const uint32_t z = zero_code(zw, col);
+      // fp16 bits of -(1024 + z) (low nibble) or -(64 + z) (high nibble), splatted.
+      const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
+      sh.u.meta.zsplat[gl][cc][v] = h | (h << 16);
+      sh.u.meta.scale[gl][cc][v] = s;
+    }
+  }
   __syncthreads();
 
-  const int t = threadIdx.x;  // output column within the tile
-  const int n = tile * kSkinnyCols + t;
+  floatx4 part[16];
+  floatx4 acc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (!SINGLE) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto load_tab = [&](const uint32_t* row, uint32_t (&dst)[16]) {
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + 4 * k4);
+      dst[4 * k4 + 0] = v[0];
+      dst[4 * k4 + 1] = v[1];
+      dst[4 * k4 + 2] = v[2];
+      dst[4 * k4 + 3] = v[3];
+    }
+  };
+  // Scale this group's sums: into acc (several groups) or in place (one group).
+  auto flush = [&](int gl) {
+    uint32_t sb[16];
+    load_tab(reinterpret_cast<const uint32_t*>(sh.u.meta.scale[gl][c]), sb);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float s = __builtin_bit_cast(float, sb[v]);
+      if (SINGLE) {
+        part[v] *= s;
+      } else {
+        acc[v] += s * part[v];
+        part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  uint32_t zs[16];
+  int cur_g = -1;
+  for (int ks = kb; ks < ke; ++ks) {
+    const int gl = ks / gsteps - g0;
+    if (gl != cur_g) {
+      if (!SINGLE && cur_g >= 0) flush(cur_g);
+      load_tab(sh.u.meta.zsplat[gl][c], zs);
+      cur_g = gl;
+    }
+    kstep_mfma(cur, zs, part);
+    cur = nxt;
+    if (ks + 2 < ke) issue(nxt, ks + 2);
+  }
+  if (cur_g >= 0) flush(cur_g);
+  __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
+
+  // 2. Waves -> LDS in register order, then sums over waves per slot.
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sh.u.red[wave][v][lane] = SINGLE ? part[v] : acc[v];
+  __syncthreads();
+
+  // Slots in q-major order so that M <= 4 touches only q = 0 (one slot per thread).
   const int rows = M < MROWS ? M : MROWS;
+  const int nslots = 256 * ((rows + 3) / 4);
+  constexpr int SLOTS = 1024 / THREADS;  // slots per thread when all 16 rows are live
+  floatx4 sum[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int s = tid + k * THREADS;
+    sum[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (s < nslots) {
+#pragma unroll
+      for (int wv = 0; wv < WAVES; ++wv) sum[k] += sh.u.red[wv][(s >> 4) & 15][(s >> 8) * 16 + (s & 15)];
+    }
+  }
+  // Output column of a slot.
+  auto slot_n = [&](int s) {
+    const int sv = (s >> 4) & 15, sc = s & 15;
+    return tile * kSkinnyCols + 8 * (2 * sc + (sv >> 3)) + tab_col(sv);
+  };
+
   if (splits == 1) {
-    if (n < N) {
-      const float b = bias ? (float)bias[n] : 0.f;
-      for (int row = 0; row < rows; ++row) {
-        const float s = ((red[0][row][t] + red[1][row][t]) + red[2][row][t]) + red[3][row][t];
-        y[(int64_t)row * N + n] = (_Float16)(s + b);
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int s = tid + k * THREADS;
+      const int n = slot_n(s);
+      if (s < nslots && n < N) {
+        const float b = bias ? (float)bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * (s >> 8) + i;
+          if (row < rows) y[(int64_t)row * N + n] = (_Float16)(sum[k][i] + b);
+        }
       }
     }
     return;
   }
 
-  float* my_part = partial + ((int64_t)tile * splits + split) * MROWS * kSkinnyCols;
-  for (int row = 0; row < rows; ++row)
-    my_part[row * kSkinnyCols + t] = ((red[0][row][t] + red[1][row][t]) + red[2][row][t]) + red[3][row][t];
-
-  // Publish the partial device-wide, then count arrivals for this column tile.
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (uint32_t)(splits - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // Last arrival: sum the splits in split order (deterministic), add bias, round once.
-  if (n < N) {
-    const float b = bias ? (float)bias[n] : 0.f;
-    const float* base = partial + (int64_t)tile * splits * MROWS * kSkinnyCols;
-    for (int row = 0; row < rows; ++row) {
-      float s = 0.f;
-      for (int sp = 0; sp < splits; ++sp)
-        s += __builtin_nontemporal_load(base + ((int64_t)sp * MROWS + row) * kSkinnyCols + t);
-      y[(int64_t)row * N + n] = (_Float16)(s + b);
+  // 3. Fixed-point accumulation across splits; the last arrival finishes the element.
+  uint64_t* tile_acc = accum + (int64_t)tile * TILE_ENTRIES;
+  constexpr float kClamp = 8388608.0f;  // 2^23
+  constexpr float kToFixed = 16777216.0f;  // 2^24
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int s = tid + k * THREADS;
+    if (s >= nslots) continue;
+    const int n = slot_n(s);
+    uint64_t ret[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ret[i] = 0;
+      if (4 * (s >> 8) + i < rows) {
+        const float v = fminf(fmaxf(sum[k][i], -kClamp), kClamp);
+        const int64_t fx = (int64_t)rintf(v * kToFixed);
+        const uint64_t add = (1ull << 56) + (uint64_t)fx;
+        ret[i] = __hip_atomic_fetch_add(tile_acc + 4 * s + i, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (s >> 8) + i;
+      if (row >= rows) continue;
+      const int64_t value = (int64_t)(ret[i] << 8) >> 8;  // low 56 bits, signed
+      const uint64_t count = (ret[i] - (uint64_t)value) >> 56;
+      if (count == (uint64_t)splits) {
+        __hip_atomic_store(tile_acc + 4 * s + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n < N) {
+          const float b = bias ? (float)bias[n] : 0.f;
+          y[(int64_t)row * N + n] = (_Float16)((float)value * (1.0f / kToFixed) + b);
+        }
+      }
     }
   }
-  if (t == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         int splits, float* partial, uint32_t* counters, uint16_t* y,
-                         hipStream_t stream) {
-  const int n_tiles = (N + kSkinnyCols - 1) / kSkinnyCols;
-  const dim3 grid(n_tiles, splits);
-  auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(kSkinnyThreads), 0, stream,
+                         const SkinnyPlan& p, uint64_t* accum, uint16_t* y, hipStream_t stream) {
+  const dim3 grid(p.n_tiles, p.splits);
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, splits, partial, counters,
+                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, p.L, p.splits, accum,
                        reinterpret_cast<_Float16*>(y));
   };
-  if (M <= 4) args(skinny_kernel<4>);
-  else args(skinny_kernel<16>);
+  if (p.waves == 4) {
+    if (p.single_group) go(skinny_kernel<4, 4, true>, 256);
+    else go(skinny_kernel<4, 4, false>, 256);
+  } else {
+    if (p.single_group) go(skinny_kernel<8, 16, true>, 512);
+    else go(skinny_kernel<8, 16, false>, 512);
+  }
   return hipGetLastError();
 }
 
