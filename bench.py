@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the M=16 and M=2048 workloads (reported under 'secondary')")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three 256 MiB device-to-device copies, a plain copy kernel of "
+                         "known size that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -60,7 +63,7 @@ def kernel_source_digest() -> str:
 def load_traffic(workload: str, digest: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -162,7 +165,7 @@ def cpu_baseline(name, synth):
         awq_ref.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], w.group_size)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or reps >= 5:
+        if el >= 10.0 or reps >= 200:  # about 10 s of CPU work
             break
     per = el / reps
     if w.M >= 512:
@@ -187,6 +190,14 @@ def main():
     import w4a16_weight_only_amd as awq
     from w4a16_weight_only_amd import synth
     awq.load_library()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     r = time_workload(args.workload, args.steps, args.warmup, torch, awq, synth)
     value, unit, roof, per_launch_s = summarize(r, args.steps)
