@@ -188,6 +188,18 @@ def test_deterministic(name):
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
 
 
+def test_reduction_modes_share_a_stream():
+    """Alternate plans that combine K splits differently (fixed-point atomics for
+    M <= 4, fp32 partials + reduce kernel above) on one stream, twice over: each
+    keeps its own workspace state valid for the other."""
+    shapes = [(1, 4096, 4096, 128), (16, 4096, 1024, 128), (3, 2048, 512, 64), (9, 4096, 2048, -1)]
+    for rep in range(2):
+        for (M, K, N, g) in shapes:
+            d = synth.make_custom(M, K, N, g, seed=rep + M)
+            yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+            tol_check(gemm(d), yref, f"alternating M{M} rep{rep}")
+
+
 def test_m_zero_is_a_noop():
     d = dev(synth.make_custom(1, 256, 256, 128))
     x = torch.empty((0, 256), dtype=torch.float16, device="cuda")

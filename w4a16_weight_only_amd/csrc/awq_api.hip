@@ -41,8 +41,9 @@ struct Plan {
   int family = 0;  // 0 skinny, 1 tile
   awq::SkinnyPlan sk{};
   int grid_x = 0, grid_y = 0, block = 0;
-  int64_t accum_bytes = 0;
-  int64_t workspace_bytes() const { return accum_bytes; }
+  int64_t accum_bytes = 0;    // zero-maintained fixed-point accumulators (4-wave plans)
+  int64_t partial_bytes = 0;  // scratch fp32 partials (8-wave plans)
+  int64_t workspace_bytes() const { return accum_bytes + partial_bytes; }
 };
 
 // Compute units of the current device (cached per device ordinal).
@@ -69,6 +70,8 @@ int device_cus() {
 // kernel's limits (at most kSkinnyMaxSplits splits, at most kSkinnyMaxGroups
 // quantization groups per workgroup).
 bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::SkinnyPlan& s) {
+  // The kernel addresses qweight with 32-bit byte offsets.
+  if (K * (N / 2) >= (int64_t(1) << 32) - 4096) return false;
   const int64_t T = K / awq::kKStep;
   const int64_t gsteps = g / awq::kKStep;  // g already resolved (-1 -> K)
   s.n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
@@ -115,7 +118,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
     p.grid_x = p.sk.n_tiles;
     p.grid_y = p.sk.splits;
     p.block = 64 * p.sk.waves;
-    if (p.sk.splits > 1) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+    // 4-wave plans: 64-bit fixed-point accumulators per tile entry; 8-wave plans:
+    // fp32 partials per (tile, split, entry).
+    if (p.sk.splits > 1) {
+      if (p.sk.waves == 4) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+      else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * awq::kSkinnyCols * 4;
+    }
   } else {
     p.family = 1;
     p.block = awq::kTileThreads;
@@ -127,42 +135,54 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
   return p;
 }
 
-// Library-owned split-K workspace, one per (device, stream): 64-bit fixed-point
-// accumulators, zeroed once at allocation and left zero by every call.  Growing it
-// frees the old buffer after the stream drains.
-struct Workspace {
+// Library-owned split-K workspace, one per (device, stream), in two buffers:
+//   accum    64-bit fixed-point accumulators; zeroed once at allocation and left zero
+//            by every call that uses them, so they must never hold anything else;
+//   partial  fp32 scratch, fully written before it is read in each call.
+// Growing a buffer frees the old one after the stream drains.
+struct Buffer {
   void* ptr = nullptr;
   int64_t bytes = 0;
+};
+struct Workspace {
+  Buffer accum, partial;
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(const Plan& p, hipStream_t stream, uint64_t** accum) {
+int ensure(Buffer& b, int64_t need, bool zero, hipStream_t stream) {
+  if (need <= 0 || (b.ptr && need <= b.bytes)) return AWQ_OK;
+  if (b.ptr) {
+    // Work already queued on this stream may still use the old buffer.
+    if (hipStreamSynchronize(stream) != hipSuccess) return AWQ_ERR_HIP;
+    if (hipFree(b.ptr) != hipSuccess) return AWQ_ERR_HIP;
+    b.ptr = nullptr;
+    b.bytes = 0;
+  }
+  const int64_t bytes = need + need / 4;  // headroom against frequent regrowth
+  void* ptr = nullptr;
+  if (hipMalloc(&ptr, (size_t)bytes) != hipSuccess) return AWQ_ERR_HIP;
+  if (zero && hipMemset(ptr, 0, (size_t)bytes) != hipSuccess) {
+    (void)hipFree(ptr);
+    return AWQ_ERR_HIP;
+  }
+  b.ptr = ptr;
+  b.bytes = bytes;
+  return AWQ_OK;
+}
+
+int get_workspace(const Plan& p, hipStream_t stream, uint64_t** accum, float** partial) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& ws = g_ws[{dev, stream}];
-  const int64_t need = p.accum_bytes;
-  if (ws.ptr == nullptr || need > ws.bytes) {
-    if (ws.ptr) {
-      // Work already queued on this stream may still use the old buffer.
-      if (hipStreamSynchronize(stream) != hipSuccess) return AWQ_ERR_HIP;
-      if (hipFree(ws.ptr) != hipSuccess) return AWQ_ERR_HIP;
-      ws.ptr = nullptr;
-      ws.bytes = 0;
-    }
-    const int64_t bytes = need + need / 4;  // headroom against frequent regrowth
-    void* ptr = nullptr;
-    if (hipMalloc(&ptr, (size_t)bytes) != hipSuccess) return AWQ_ERR_HIP;
-    if (hipMemset(ptr, 0, (size_t)bytes) != hipSuccess) {
-      (void)hipFree(ptr);
-      return AWQ_ERR_HIP;
-    }
-    ws.ptr = ptr;
-    ws.bytes = bytes;
-  }
-  *accum = reinterpret_cast<uint64_t*>(ws.ptr);
+  int st = ensure(ws.accum, p.accum_bytes, true, stream);
+  if (st != AWQ_OK) return st;
+  st = ensure(ws.partial, p.partial_bytes, false, stream);
+  if (st != AWQ_OK) return st;
+  *accum = reinterpret_cast<uint64_t*>(ws.accum.ptr);
+  *partial = reinterpret_cast<float*>(ws.partial.ptr);
   return AWQ_OK;
 }
 
@@ -251,11 +271,13 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
   hipError_t e;
   if (p.family == 0) {
     uint64_t* accum = nullptr;
+    float* partial = nullptr;
     if (p.sk.splits > 1) {
-      const int ws = get_workspace(p, stream, &accum);
+      const int ws = get_workspace(p, stream, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
-    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, y, stream);
+    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, partial, y,
+                           stream);
   } else {
     e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, y, stream);
   }

@@ -48,21 +48,33 @@ __device__ __forceinline__ uint32_t pair_byte(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, sel);
 }
 
+// Bit masks of the unpack, held in VGPRs.  gfx9 VOP3 encodings take no literal
+// constants, so with literals the compiler splits (p & mask) | magic into two
+// instructions; opaque register copies let it emit one v_and_or_b32.
+struct UnpackConsts {
+  uint32_t magic, mlo, mhi;
+};
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts k{0x64006400u, 0x000F000Fu, 0x00F000F0u};
+  asm volatile("" : "+v"(k.magic), "+v"(k.mlo), "+v"(k.mhi));
+  return k;
+}
+
 // fp16 pair (1024 + lo_a, 1024 + lo_b): the nibble ORed into the mantissa of 1024.0
 // (0x6400) gives the integer exactly, since 1024..2047 are exact in fp16.
-__device__ __forceinline__ half2v lo_magic(uint32_t p) { return as_h2((p & 0x000F000Fu) | 0x64006400u); }
+__device__ __forceinline__ half2v lo_magic(uint32_t p, const UnpackConsts& k) { return as_h2((p & k.mlo) | k.magic); }
 // fp16 pair (1024 + 16*hi_a, 1024 + 16*hi_b), also exact.
-__device__ __forceinline__ half2v hi_magic(uint32_t p) { return as_h2((p & 0x00F000F0u) | 0x64006400u); }
+__device__ __forceinline__ half2v hi_magic(uint32_t p, const UnpackConsts& k) { return as_h2((p & k.mhi) | k.magic); }
 
 // (code - zero) as exact small fp16 integers from the magic forms.
 //   lo: (1024 + q) - (1024 + z)                      one packed add
 //   hi: (1024 + 16 q) / 16 - (64 + z) = q - z         one packed fma, exact
-__device__ __forceinline__ half2v lo_minus_zero(uint32_t p, half2v neg_1024_plus_z) {
-  return lo_magic(p) + neg_1024_plus_z;
+__device__ __forceinline__ half2v lo_minus_zero(uint32_t p, half2v neg_1024_plus_z, const UnpackConsts& k) {
+  return lo_magic(p, k) + neg_1024_plus_z;
 }
-__device__ __forceinline__ half2v hi_minus_zero(uint32_t p, half2v neg_64_plus_z) {
+__device__ __forceinline__ half2v hi_minus_zero(uint32_t p, half2v neg_64_plus_z, const UnpackConsts& k) {
   const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  return __builtin_elementwise_fma(hi_magic(p), sixteenth, neg_64_plus_z);
+  return __builtin_elementwise_fma(hi_magic(p, k), sixteenth, neg_64_plus_z);
 }
 
 // Zero code of column j of a packed zero word.

@@ -35,11 +35,13 @@ constexpr int kTileThreads = 256;
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, float* out, hipStream_t stream);
 
-// accum: [n_tiles][mrows * 256] 64-bit accumulators, zero before the first call and
-// left zero by the kernel itself (unused when p.splits == 1).
+// With p.splits > 1: 4-wave plans use accum, [n_tiles][mrows * 256] 64-bit
+// accumulators that are zero before the call and left zero by it; 8-wave plans use
+// partial, [n_tiles][splits][16 * 256] fp32 scratch, and a second reduce kernel.
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         const SkinnyPlan& p, uint64_t* accum, uint16_t* y, hipStream_t stream);
+                         const SkinnyPlan& p, uint64_t* accum, float* partial, uint16_t* y,
+                         hipStream_t stream);
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,

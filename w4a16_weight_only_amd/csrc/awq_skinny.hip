@@ -71,7 +71,8 @@ __host__ __device__ constexpr int tab_col(int v) {  // column within the word
 // The 16 MFMAs of one k-step for one lane's 2 word-columns.  zs holds, per entry,
 // the fp16 splat to add: -(1024 + z) for low-nibble columns, -(64 + z) for
 // high-nibble columns.
-__device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[16], floatx4 (&part)[16]) {
+__device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[16], const UnpackConsts& uk,
+                                           floatx4 (&part)[16]) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
@@ -86,8 +87,8 @@ __device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[
         else if (t == 1) pb = pair_byte<1>(ra, rb);
         else if (t == 2) pb = pair_byte<2>(ra, rb);
         else pb = pair_byte<3>(ra, rb);
-        lo[p] = lo_minus_zero(pb, as_h2(zs[tab_idx(w, t, 0)]));
-        hi[p] = hi_minus_zero(pb, as_h2(zs[tab_idx(w, t, 1)]));
+        lo[p] = lo_minus_zero(pb, as_h2(zs[tab_idx(w, t, 0)]), uk);
+        hi[p] = hi_minus_zero(pb, as_h2(zs[tab_idx(w, t, 1)]), uk);
       }
       const int il = tab_idx(w, t, 0), ih = tab_idx(w, t, 1);
       part[il] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a, pack4(lo[0], lo[1], lo[2], lo[3]), part[il], 0, 0, 0);
@@ -120,9 +121,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
     const _Float16* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
-    uint64_t* __restrict__ accum, _Float16* __restrict__ y) {
+    uint64_t* __restrict__ accum, float* __restrict__ partial, _Float16* __restrict__ y) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
+  // k-steps in flight per wave, and how K splits meet: 4-wave workgroups (M <= 4)
+  // combine splits with fixed-point atomics; 8-wave ones (up to 16 rows, where the
+  // atomic count M * N * S gets large) store fp32 partials for skinny_reduce_kernel.
+  constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
+  constexpr bool ATOMIC = WAVES == 4;
   __shared__ SkinnyLds<WAVES> sh;
 
   const int tid = threadIdx.x;
@@ -145,30 +151,31 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const int gsteps = g / kKStep;
   const int g0 = s0 / gsteps;
 
+  // Loads address the uniform base pointers with 32-bit byte offsets (the host
+  // keeps qweight under 4 GiB).  Lanes of x rows >= M or of columns >= N read a
+  // valid clamped address instead of being masked: an MFMA output row depends only
+  // on its own x row, and rows >= M and columns >= N are never stored.
   const int m = lane & 15;
-  const bool row_ok = m < M;
-  const _Float16* xrow = x + (int64_t)(row_ok ? m : 0) * K + 8 * q;
-  const uint32_t* wbase = qweight + (int64_t)(8 * q) * NW + (col_ok ? wc : 0);
+  const uint32_t x_off = ((uint32_t)(m < M ? m : 0) * (uint32_t)K + 8u * q) * 2u;
+  const uint32_t w_off = ((uint32_t)(8 * q) * (uint32_t)NW + (uint32_t)(col_ok ? wc : 0)) * 4u;
+  const uint32_t row_bytes = (uint32_t)NW * 4u;
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* wb = reinterpret_cast<const char*>(qweight);
 
-  // Branch-free loads: an invalid step, row or column reads a valid address and is
-  // masked to zero.
+  // Loads of k-step ks (ks < ke, uniform across the wave).
   auto issue = [&](Step& st, int ks) {
-    const bool ok = ks < ke;
-    const int kr = min(ks, T - 1) * kKStep;
-    const bool wok = ok && col_ok;
+    const uint32_t o = w_off + (uint32_t)ks * (uint32_t)kKStep * row_bytes;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wbase + (int64_t)(kr + r) * NW));
-      st.v[r] = wok ? v : u32x2{0u, 0u};
-    }
-    const half8v a = *reinterpret_cast<const half8v*>(xrow + kr);
-    st.a = (ok && row_ok) ? a : half8v{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = 0; r < 8; ++r)
+      st.v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wb + (o + (uint32_t)r * row_bytes)));
+    st.a = *reinterpret_cast<const half8v*>(xb + (x_off + (uint32_t)ks * (uint32_t)(kKStep * 2)));
   };
 
-  // 1. Weight loads of the first two k-steps; group tables into LDS meanwhile.
-  Step cur, nxt;
-  issue(cur, kb);
-  issue(nxt, kb + 1);
+  // 1. Weight loads of the first PF k-steps; group tables into LDS meanwhile.
+  Step ring[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (kb + j < ke) issue(ring[j], kb + j);
   {
     const int ng = (s1 > s0) ? (s1 - 1) / gsteps - g0 + 1 : 0;  // <= kSkinnyMaxGroups (host)
     for (int i = tid; i < ng * 256; i += THREADS) {
@@ -224,25 +231,35 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     }
   };
 
+  const UnpackConsts uk = unpack_consts();
   uint32_t zs[16];
   int cur_g = -1;
-  for (int ks = kb; ks < ke; ++ks) {
-    const int gl = ks / gsteps - g0;
-    if (gl != cur_g) {
-      if (!SINGLE && cur_g >= 0) flush(cur_g);
-      load_tab(sh.u.meta.zsplat[gl][c], zs);
-      cur_g = gl;
+  // Ring of PF k-steps in flight: after step ks is consumed its slot loads ks + PF.
+  for (int base = kb; base < ke; base += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int ks = base + j;
+      if (ks < ke) {
+        const int gl = ks / gsteps - g0;
+        if (gl != cur_g) {
+          if (!SINGLE && cur_g >= 0) flush(cur_g);
+          load_tab(sh.u.meta.zsplat[gl][c], zs);
+          cur_g = gl;
+        }
+        kstep_mfma(ring[j], zs, uk, part);
+        if (ks + PF < ke) issue(ring[j], ks + PF);
+      }
     }
-    kstep_mfma(cur, zs, part);
-    cur = nxt;
-    if (ks + 2 < ke) issue(nxt, ks + 2);
   }
   if (cur_g >= 0) flush(cur_g);
   __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
 
-  // 2. Waves -> LDS in register order, then sums over waves per slot.
+  // 2. Waves -> LDS in register order, then sums over waves per slot.  With at most
+  // 4 rows only the q = 0 lanes (rows 0..3) hold rows that are ever stored.
+  if (MROWS > 4 || q == 0) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) sh.u.red[wave][v][lane] = SINGLE ? part[v] : acc[v];
+    for (int v = 0; v < 16; ++v) sh.u.red[wave][v][lane] = SINGLE ? part[v] : acc[v];
+  }
   __syncthreads();
 
   // Slots in q-major order so that M <= 4 touches only q = 0 (one slot per thread).
@@ -278,6 +295,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
           if (row < rows) y[(int64_t)row * N + n] = (_Float16)(sum[k][i] + b);
         }
       }
+    }
+    return;
+  }
+
+  if (!ATOMIC) {
+    // 3'. Plain fp32 partial stores [tile][split][entry]; skinny_reduce_kernel sums
+    // them in split order after this kernel completes.
+    float* tile_part = partial + ((int64_t)tile * splits + split) * TILE_ENTRIES;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int s = tid + k * THREADS;
+      if (s < nslots) *reinterpret_cast<floatx4*>(tile_part + 4 * s) = sum[k];
     }
     return;
   }
@@ -319,15 +348,36 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   }
 }
 
+// Sums the fp32 partials of the 8-wave skinny kernel in split order, adds bias,
+// rounds once to fp16.  One thread per (tile, entry); entry 4 * slot + i is row
+// 4 (slot / 256) + i of the slot's column.
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
+                                                            const _Float16* __restrict__ bias, int M, int N,
+                                                            int splits, _Float16* __restrict__ y) {
+  constexpr int TILE_ENTRIES = 16 * kSkinnyCols;
+  const int tile = blockIdx.x / (TILE_ENTRIES / 256);
+  const int e = (blockIdx.x % (TILE_ENTRIES / 256)) * 256 + threadIdx.x;
+  const int s = e >> 2, i = e & 3;
+  const int row = 4 * (s >> 8) + i;
+  const int sv = (s >> 4) & 15, sc = s & 15;
+  const int n = tile * kSkinnyCols + 8 * (2 * sc + (sv >> 3)) + tab_col(sv);
+  if (row >= M || n >= N) return;
+  const float* p = partial + (int64_t)tile * splits * TILE_ENTRIES + e;
+  float acc = 0.f;
+  for (int sp = 0; sp < splits; ++sp) acc += p[(int64_t)sp * TILE_ENTRIES];
+  y[(int64_t)row * N + n] = (_Float16)(acc + (bias ? (float)bias[n] : 0.f));
+}
+
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         const SkinnyPlan& p, uint64_t* accum, uint16_t* y, hipStream_t stream) {
+                         const SkinnyPlan& p, uint64_t* accum, float* partial, uint16_t* y,
+                         hipStream_t stream) {
   const dim3 grid(p.n_tiles, p.splits);
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, p.L, p.splits, accum,
+                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, p.L, p.splits, accum, partial,
                        reinterpret_cast<_Float16*>(y));
   };
   if (p.waves == 4) {
@@ -336,6 +386,13 @@ hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_
   } else {
     if (p.single_group) go(skinny_kernel<8, 16, true>, 512);
     else go(skinny_kernel<8, 16, false>, 512);
+    if (p.splits > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(p.n_tiles * 16), dim3(256), 0, stream,
+                         partial, reinterpret_cast<const _Float16*>(bias), M, N,
+                         p.splits, reinterpret_cast<_Float16*>(y));
+    }
   }
   return hipGetLastError();
 }

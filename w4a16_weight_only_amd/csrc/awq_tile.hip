@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  const UnpackConsts uk = unpack_consts();
   load(0);
   for (int k0 = 0; k0 < K; k0 += kTileK) {
     __syncthreads();  // previous k-tile's fragments have been read
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(
         const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)((sreg[jh >> 1] >> (16 * (jh & 1))) & 0xFFFFu));
         const half2v zl = splat(-(_Float16)(float)(1024u + zero_code(zreg, jl)));
         const half2v zh = splat(-(_Float16)(float)(64u + zero_code(zreg, jh)));
-        const half2v wl = lo_minus_zero(pb[t], zl) * splat(sl);
-        const half2v wh = hi_minus_zero(pb[t], zh) * splat(sh);
+        const half2v wl = lo_minus_zero(pb[t], zl, uk) * splat(sl);
+        const half2v wh = hi_minus_zero(pb[t], zh, uk) * splat(sh);
         *reinterpret_cast<uint32_t*>(&Bs[8 * bw + jl][2 * bp]) = as_u32(wl);
         *reinterpret_cast<uint32_t*>(&Bs[8 * bw + jh][2 * bp]) = as_u32(wh);
       }
