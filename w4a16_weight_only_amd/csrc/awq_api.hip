@@ -33,12 +33,13 @@ int limits_check(int64_t M, int64_t K, int64_t N, int64_t group_size) {
   if (group_size != -1 && group_size % 32 != 0) return AWQ_ERR_UNSUPPORTED;
   if (K > kMaxDim || N > kMaxDim || M > kMaxDim) return AWQ_ERR_UNSUPPORTED;
   // The tile family's 1-D grid must stay below 2^31 workgroups.
-  if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  if (((M + 127) / 128) * ((N + 63) / 64) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
   return AWQ_OK;
 }
 
 struct Plan {
   int family = 0;  // 0 skinny, 1 tile
+  int tile_variant = 0;
   awq::SkinnyPlan sk{};
   int grid_x = 0, grid_y = 0, block = 0;
   int64_t accum_bytes = 0;    // zero-maintained fixed-point accumulators (4-wave plans)
@@ -127,9 +128,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
   } else {
     p.family = 1;
     p.block = awq::kTileThreads;
-    const int64_t n_tiles = (N + awq::kTileN - 1) / awq::kTileN;
-    const int64_t m_tiles = (M + awq::kTileM - 1) / awq::kTileM;
-    p.grid_x = (int)(n_tiles * m_tiles);
+    // The large tile unless it would leave most compute units idle.
+    auto tiles = [&](int v) {
+      return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
+    };
+    p.tile_variant = tiles(0) >= (int64_t)cus * 3 / 4 ? 0 : 1;
+    p.grid_x = (int)tiles(p.tile_variant);
     p.grid_y = 1;
   }
   return p;
@@ -279,7 +283,7 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
     e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, partial, y,
                            stream);
   } else {
-    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, y, stream);
+    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tile_variant, y, stream);
   }
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
 }

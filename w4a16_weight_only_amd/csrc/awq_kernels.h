@@ -26,11 +26,11 @@ struct SkinnyPlan {
   bool single_group; // every wave's k-steps lie in one quantization group
 };
 
-// MFMA tile family geometry.
-constexpr int kTileM = 128;
-constexpr int kTileN = 128;
-constexpr int kTileK = 32;
+// MFMA tile family: 4 waves; variant 0 covers 256 x 128 outputs per workgroup,
+// variant 1 covers 128 x 64.
 constexpr int kTileThreads = 256;
+constexpr int kTileBM[2] = {256, 128};
+constexpr int kTileBN[2] = {128, 64};
 
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, float* out, hipStream_t stream);
@@ -45,6 +45,6 @@ hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       uint16_t* y, hipStream_t stream);
+                       int variant, uint16_t* y, hipStream_t stream);
 
 }  // namespace awq

@@ -2,154 +2,274 @@
 //
 // y = x . dequant(W) + bias with fp16 MFMA and fp32 accumulation (GPTQModel wiki
 // "AWQ", section "Native GEMM": fp32 accumulation; GPU LLM serving-stack blog,
-// section 1.2: large batches are compute-bound, so dequant work must hide under
+// section 1.2: large batches are compute-bound, so the dequant work must hide under
 // the matrix products).
 //
-// Workgroup tile 128 (M) x 128 (N), k-tile 32, 256 threads as 2 x 2 waves, each
-// wave 64 x 64 = 2 x 2 v_mfma_f32_32x32x16_f16.
-// Per k-tile:
-//   A: 128 x 32 fp16 of x staged into LDS (two 16-byte loads per thread).
-//   B: 32 rows x 16 packed words; each thread takes two rows of one word column,
-//      interleaves their bytes (v_perm_b32), expands each nibble pair to exact fp16
-//      with the 0x6400 mantissa trick, subtracts the zero exactly, multiplies by the
-//      fp16 scale (one rounding: fp16((q - z) s)) and writes the eight (k, k+1)
-//      pairs of its eight columns to LDS in [n][k] order, un-permuting the AWQ
-//      column order on the way.  Each weight is dequantised once per workgroup.
-//   Waves read 16-byte A and B fragments from LDS and issue 2 k16 steps x 4 MFMAs.
-// The next k-tile's global loads are issued before the current tile's MFMAs.
+// Workgroup: 4 waves as 2 (M) x 2 (N); wave tile (32 FM) x (32 FN) of
+// v_mfma_f32_32x32x16_f16 accumulators.  Instantiations: FM = 4, FN = 2 (workgroup
+// 256 x 128) for large M, FM = 2, FN = 1 (128 x 64) when fewer rows would leave
+// compute units idle.
+//
+// Staging, per k-tile of 64 rows: two LDS buffers and two register sets in
+// ping-pong.  The global loads of k-tile t + 3 are issued right after k-tile t is
+// multiplied and written to LDS two k-tiles later, so each load has two k-tiles of
+// MFMA work to arrive (a loaded round trip is 1.5-2 us on this part):
+//   x: BM x 64 fp16, 16-byte coalesced pieces; rows padded so that 16-byte fragment
+//      reads are conflict-free;
+//   qweight: the workgroup's BN / 8 packed word columns x 64 rows, still packed
+//      (4 KB for BN = 128), transposed to word-column-major so that a lane's 8
+//      consecutive rows are two 16-byte reads;
+//   group data: the zero words and fp16 scales of the (at most two) groups the
+//      k-tile touches.
+// B operand, dequantised in registers: in a 32x32x16 B operand lane l supplies 8
+// consecutive k of column n = l % 32.  A wave's 32 FN columns are its packed word
+// columns x nibble positions: lane l takes word column l % 8 (FN = 2) or l % 4
+// (FN = 1) and extracts the nibble(s) of its own column(s), for FN = 2 nibbles p and
+// p + 4 (bytes t and t + 2, same half).  Per pair of rows: one v_perm_b32 gathers the
+// needed bytes of both rows, one v_and_or_b32 per column makes exact fp16
+// (1024 + q) or (1024 + 16 q) (0x6400 mantissa trick), one packed fma with per-lane
+// constants gives (q - z) exactly (x 1 or x 1/16, plus -(1024 + z) or -(64 + z)),
+// and one packed multiply by the fp16 scale rounds once: B = fp16((q - z) s).
+// Output columns are un-permuted at the store: MFMA column i of N-tile f is packed
+// word column (base + i % 8 or i % 4) at nibble position ((i / 8) % 4 + 4 f) or
+// (i / 4) % 8, i.e. output column 8 wc + ORDER[nibble].
+// Grid order: M tiles fastest, so consecutive workgroups (spread round-robin over
+// the 8 XCDs) share column tiles and each XCD's L2 sees one slab of x.
 #include "awq_device.h"
 #include "awq_kernels.h"
 
 namespace awq {
 
 namespace {
-constexpr int LDK = kTileK + 8;  // padded LDS row (halves) to spread banks
-}
 
-__global__ __launch_bounds__(kTileThreads) void tile_kernel(
+constexpr int kBK = 64;            // k-tile of the x staging
+constexpr int kALd = kBK + 8;      // padded LDS row (halves): 144 B, conflict-free fragment reads
+
+// ORDER[p]: column within a packed word held by nibble p.
+__device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 1 : 2 * p; }
+
+}  // namespace
+
+template <int FM, int FN>
+__global__ __launch_bounds__(256) void tile_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const _Float16* __restrict__ bias, int M, int K, int N, int g, int n_tiles,
+    const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles,
     _Float16* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[kTileM][LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[kTileN][LDK];
+  constexpr int BM = 2 * 32 * FM;     // workgroup rows
+  constexpr int BN = 2 * 32 * FN;     // workgroup columns
+  constexpr int BW = BN / 8;          // packed word columns per workgroup (16 or 8)
+  constexpr int WW = 32 * FN / 8;     // packed word columns per wave (8 or 4)
+  constexpr int kBLd = kBK + 4;       // words per staged word column (padded)
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kALd];
+  __shared__ __attribute__((aligned(16))) uint32_t Bs[2][BW][kBLd];
+  __shared__ uint32_t Zs[2][2][BW];       // zero words of the k-tile's first/second group
+  __shared__ _Float16 Ss[2][2][BN];       // scales of the k-tile's first/second group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tile_n = blockIdx.x % n_tiles;
-  const int tile_m = blockIdx.x / n_tiles;
-  const int m0 = tile_m * kTileM, n0 = tile_n * kTileN;
+  const int tile_m = blockIdx.x % m_tiles;
+  const int tile_n = blockIdx.x / m_tiles;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int NW = N >> 3;
-  const int wc0 = n0 >> 3;
+  const int wc0 = n0 / 8;
 
-  // Global -> register mapping.
-  const int ar = tid >> 1, ap = (tid & 1) * 16;  // A: row, half offset
-  const int bp = tid >> 4, bw = tid & 15;         // B: row pair, word column
-  const bool a_ok = m0 + ar < M;
-  const bool b_ok = wc0 + bw < NW;
-  const _Float16* aptr = x + (int64_t)(m0 + ar) * K + ap;
-  const uint32_t* bptr = qweight + (int64_t)(2 * bp) * NW + wc0 + bw;
-
-  u32x4 areg0, areg1, sreg;
-  uint32_t bra, brb, zreg;
-  auto load = [&](int k0) {
-    areg0 = areg1 = u32x4{0u, 0u, 0u, 0u};
-    if (a_ok) {
-      areg0 = *reinterpret_cast<const u32x4*>(aptr + k0);
-      areg1 = *reinterpret_cast<const u32x4*>(aptr + k0 + 8);
+  // ---- Global -> register staging of one k-tile.
+  constexpr int A_PIECES = BM * kBK * 2 / 16 / 256;  // 16-byte pieces of x per thread
+  const int a_chunk = tid & 7;
+  const char* xb = reinterpret_cast<const char*>(x);
+  // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns.
+  constexpr int B_PIECES = BW * kBK / 4;                 // 256 (BW 16) or 128 (BW 8)
+  const bool b_active = tid < B_PIECES;
+  const int b_row = tid / (BW / 4), b_wc = (tid % (BW / 4)) * 4;
+  // group data: thread t < 2 * BW loads a zero word (group t / BW, word column
+  // t % BW); the next 2 * BN / 8 threads load 8 scales (16 bytes) each.
+  struct Stage {
+    u32x4 a[A_PIECES];
+    u32x4 b;
+    uint32_t z;
+    u32x4 s;
+  };
+  auto stage_load = [&](Stage& st, int k0) {
+#pragma unroll
+    for (int i = 0; i < A_PIECES; ++i) {
+      const int row = m0 + (tid >> 3) + 32 * i;
+      const int rr = row < M ? row : M - 1;          // rows >= M: clamped, never stored
+      const int kk = min(k0 + 8 * a_chunk, K - 8);   // k >= K: clamped, step skipped
+      st.a[i] = *reinterpret_cast<const u32x4*>(xb + ((int64_t)rr * K + kk) * 2);
     }
-    bra = brb = zreg = 0u;
-    sreg = u32x4{0u, 0u, 0u, 0u};
-    if (b_ok) {
-      const int gi = k0 / g;
-      bra = bptr[(int64_t)k0 * NW];
-      brb = bptr[(int64_t)(k0 + 1) * NW];
-      zreg = qzeros[(int64_t)gi * NW + wc0 + bw];
-      sreg = *reinterpret_cast<const u32x4*>(scales + (int64_t)gi * N + 8 * (wc0 + bw));
+    if (b_active) {
+      const int r = min(k0 + b_row, K - 1);
+      const int wc = min(wc0 + b_wc, NW - 4);        // columns >= N: clamped, never stored
+      st.b = *reinterpret_cast<const u32x4*>(qweight + (int64_t)r * NW + wc);
+    }
+    const int ga = k0 / g, gb = min(K - 1, k0 + kBK - 1) / g;
+    if (tid < 2 * BW) {
+      const int gi = (tid < BW) ? ga : gb;
+      const int wc = min(wc0 + tid % BW, NW - 1);
+      st.z = qzeros[(int64_t)gi * NW + wc];
+    } else if (tid < 2 * BW + 2 * BN / 8) {
+      const int u = tid - 2 * BW;
+      const int gi = (u < BN / 8) ? ga : gb;
+      const int wc = min(wc0 + u % (BN / 8), NW - 1);
+      st.s = *reinterpret_cast<const u32x4*>(scales + (int64_t)gi * N + 8 * wc);
+    }
+  };
+  auto stage_store = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PIECES; ++i)
+      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32 * i][8 * a_chunk]) = st.a[i];
+    if (b_active) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
+    }
+    if (tid < 2 * BW) {
+      Zs[buf][tid / BW][tid % BW] = st.z;
+    } else if (tid < 2 * BW + 2 * BN / 8) {
+      const int u = tid - 2 * BW;
+      *reinterpret_cast<u32x4*>(&Ss[buf][u / (BN / 8)][8 * (u % (BN / 8))]) = st.s;
     }
   };
 
-  floatx16 acc[2][2];
+  // ---- This lane's column(s) of the B operand.
+  const int lc = lane & 31;                    // MFMA column slot
+  const int wsub = FN == 2 ? (lc & 7) : (lc & 3);
+  const int p0 = FN == 2 ? ((lc >> 3) & 3) : ((lc >> 2) & 7);  // nibble of N-tile 0
+  const int wloc = wn * WW + wsub;             // word column within the workgroup tile
+  const int wcol = wc0 + wloc;
+  const int kq = 8 * (lane >> 5);              // this lane's k offset within a k16 step
+  // v_perm_b32 selector: [a.t0, a.t1, b.t0, b.t1], t0 = byte of nibble p0, t1 = t0 + 2.
+  const int byte0 = p0 >> 1;
+  const uint32_t sel = FN == 2 ? ((uint32_t)byte0 | ((uint32_t)(byte0 + 2) << 8) | ((uint32_t)(4 + byte0) << 16) |
+                                  ((uint32_t)(6 + byte0) << 24))
+                               : ((uint32_t)byte0 | (0x0Cu << 8) | ((uint32_t)(4 + byte0) << 16) | (0x0Cu << 24));
+  const bool hi_nib = p0 & 1;
+  const UnpackConsts uk = unpack_consts();
+  const uint32_t mask = hi_nib ? uk.mhi : uk.mlo;
+  const half2v mult = hi_nib ? half2v{(_Float16)0.0625f, (_Float16)0.0625f} : half2v{(_Float16)1.f, (_Float16)1.f};
+  const int c0 = 8 * wloc + order_of(p0);      // column within the workgroup tile, N-tile 0
+  const int c1 = 8 * wloc + order_of(p0 + 4);  // N-tile 1 (FN = 2)
+  const _Float16 zbase = hi_nib ? (_Float16)64.f : (_Float16)1024.f;
+
+  half2v off0, off1, sc0, sc1;
+  auto apply_group = [&](int buf, int g2) {
+    const uint32_t zw = Zs[buf][g2][wloc];
+    off0 = splat(-(zbase + (_Float16)(float)((zw >> (4 * p0)) & 0xFu)));
+    sc0 = splat(Ss[buf][g2][c0]);
+    if (FN == 2) {
+      off1 = splat(-(zbase + (_Float16)(float)((zw >> (4 * (p0 + 4))) & 0xFu)));
+      sc1 = splat(Ss[buf][g2][c1]);
+    }
+  };
+
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const UnpackConsts uk = unpack_consts();
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += kTileK) {
-    __syncthreads();  // previous k-tile's fragments have been read
-    *reinterpret_cast<u32x4*>(&As[ar][ap]) = areg0;
-    *reinterpret_cast<u32x4*>(&As[ar][ap + 8]) = areg1;
-    {
-      uint32_t pb[4] = {pair_byte<0>(bra, brb), pair_byte<1>(bra, brb), pair_byte<2>(bra, brb),
-                        pair_byte<3>(bra, brb)};
+  // Multiply the k-tile staged in LDS buffer buf (k-tile kt).
+  auto compute = [&](int kt, int buf) {
+    const int k0 = kt * kBK;
+    const int ga = k0 / g;
+    int cur = -1;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jl = lo_col(t), jh = hi_col(t);
-        const _Float16 sl = __builtin_bit_cast(_Float16, (uint16_t)((sreg[jl >> 1] >> (16 * (jl & 1))) & 0xFFFFu));
-        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)((sreg[jh >> 1] >> (16 * (jh & 1))) & 0xFFFFu));
-        const half2v zl = splat(-(_Float16)(float)(1024u + zero_code(zreg, jl)));
-        const half2v zh = splat(-(_Float16)(float)(64u + zero_code(zreg, jh)));
-        const half2v wl = lo_minus_zero(pb[t], zl, uk) * splat(sl);
-        const half2v wh = hi_minus_zero(pb[t], zh, uk) * splat(sh);
-        *reinterpret_cast<uint32_t*>(&Bs[8 * bw + jl][2 * bp]) = as_u32(wl);
-        *reinterpret_cast<uint32_t*>(&Bs[8 * bw + jh][2 * bp]) = as_u32(wh);
+    for (int s = 0; s < kBK / 16; ++s) {
+      const int k = k0 + 16 * s;
+      if (k < K) {  // uniform; a partial last k-tile has 32 valid k
+        const int g2 = k / g - ga;  // 0 or 1
+        if (g2 != cur) {
+          apply_group(buf, g2);
+          cur = g2;
+        }
+        const u32x4 wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq]);
+        const u32x4 whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq + 4]);
+        const uint32_t w[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
+        half2v h0[4], h1[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
+          h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
+          if (FN == 2)
+            h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
+        }
+        half8v bf[2];
+        bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
+        if (FN == 2) bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const half8v af =
+              *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][16 * s + kq]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
-    if (k0 + kTileK < K) load(k0 + kTileK);
+  };
 
-#pragma unroll
-    for (int kk = 0; kk < kTileK; kk += 16) {
-      const int kc = kk + 8 * (lane >> 5);
-      half8v af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const half8v*>(&As[wm * 64 + i * 32 + (lane & 31)][kc]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const half8v*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kc]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  // k-tile t lives in register set t % 2 (st0 / st1) and LDS buffer t % 2.  After
+  // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.
+  const int KT = (K + kBK - 1) / kBK;
+  Stage st0, st1;
+  stage_load(st0, 0);
+  stage_store(st0, 0);
+  if (KT > 1) stage_load(st1, kBK);
+  if (KT > 2) stage_load(st0, 2 * kBK);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    compute(kt, 0);
+    if (kt + 1 < KT) {
+      stage_store(st1, 1);
+      if (kt + 3 < KT) stage_load(st1, (kt + 3) * kBK);
+    }
+    __syncthreads();
+    if (kt + 1 < KT) {
+      compute(kt + 1, 1);
+      if (kt + 2 < KT) {
+        stage_store(st0, 0);
+        if (kt + 4 < KT) stage_load(st0, (kt + 4) * kBK);
+      }
+      __syncthreads();
     }
   }
 
   // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4,
-  // column l%32.
+  // MFMA column l % 32 -> output column n0 + c0 / c1.
+  if (wcol < NW) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (n >= N) continue;
-    const float b = bias ? (float)bias[n] : 0.f;
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + (j == 0 ? c0 : c1);
+      const float b = bias ? (float)bias[n] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) y[(int64_t)row * N + n] = (_Float16)(acc[i][j][r] + b);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < M) y[(int64_t)row * N + n] = (_Float16)(acc[i][j][r] + b);
+        }
+    }
   }
 }
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       uint16_t* y, hipStream_t stream) {
-  const int n_tiles = (N + kTileN - 1) / kTileN;
-  const int m_tiles = (M + kTileM - 1) / kTileM;
-  const int64_t blocks = (int64_t)n_tiles * m_tiles;
-  hipLaunchKernelGGL(tile_kernel, dim3((unsigned)blocks), dim3(kTileThreads), 0, stream,
-                     reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
-                     reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                     reinterpret_cast<const _Float16*>(bias), M, K, N, g, n_tiles,
-                     reinterpret_cast<_Float16*>(y));
+                       int variant, uint16_t* y, hipStream_t stream) {
+  auto go = [&](auto kern, int bm, int bn) {
+    const int m_tiles = (M + bm - 1) / bm;
+    const int n_tiles = (N + bn - 1) / bn;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles)), dim3(256), 0, stream,
+                       reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
+                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
+                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles,
+                       reinterpret_cast<_Float16*>(y));
+  };
+  if (variant == 0) go(tile_kernel<4, 2>, 256, 128);
+  else go(tile_kernel<2, 1>, 128, 64);
   return hipGetLastError();
 }
 
