@@ -19,8 +19,8 @@
 //   qweight: the workgroup's BN / 8 packed word columns x 64 rows, still packed
 //      (4 KB for BN = 128), transposed to word-column-major so that a lane's 8
 //      consecutive rows are two 16-byte reads;
-//   group data: the zero words and fp16 scales of the (at most two) groups the
-//      k-tile touches.
+//   group data: the zero words and fp16 scales of the groups of the k-tile's two
+//      32-row halves (g is a multiple of 32, so no other boundary can occur).
 // B operand, dequantised in registers: in a 32x32x16 B operand lane l supplies 8
 // consecutive k of column n = l % 32.  A wave's 32 FN columns are its packed word
 // columns x nibble positions: lane l takes word column l % 8 (FN = 2) or l % 4
@@ -35,6 +35,8 @@
 // (i / 4) % 8, i.e. output column 8 wc + ORDER[nibble].
 // Grid order: M tiles fastest, so consecutive workgroups (spread round-robin over
 // the 8 XCDs) share column tiles and each XCD's L2 sees one slab of x.
+#include <type_traits>
+
 #include "awq_device.h"
 #include "awq_kernels.h"
 
@@ -61,10 +63,12 @@ __global__ __launch_bounds__(256) void tile_kernel(
   constexpr int BW = BN / 8;          // packed word columns per workgroup (16 or 8)
   constexpr int WW = 32 * FN / 8;     // packed word columns per wave (8 or 4)
   constexpr int kBLd = kBK + 4;       // words per staged word column (padded)
+  // Group data of one k-tile, per 32-row half: the zero words of the BW word columns
+  // then the BN fp16 scales, in 16-byte pieces.
+  constexpr int ZP = BW / 4, SP = BN / 8, GP = ZP + SP;  // pieces: zeros, scales, per half
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kALd];
   __shared__ __attribute__((aligned(16))) uint32_t Bs[2][BW][kBLd];
-  __shared__ uint32_t Zs[2][2][BW];       // zero words of the k-tile's first/second group
-  __shared__ _Float16 Ss[2][2][BN];       // scales of the k-tile's first/second group
+  __shared__ __attribute__((aligned(16))) u32x4 Gs[2][2 * GP + 1];  // + 1: sink of idle threads
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,61 +80,59 @@ __global__ __launch_bounds__(256) void tile_kernel(
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
 
-  // ---- Global -> register staging of one k-tile.
+  // ---- Global -> register staging of one k-tile.  Every thread runs the same
+  // code (no divergent branches): out-of-range rows and columns are clamped and
+  // never stored to y; rows past K are only read by a partial last k-tile's unused
+  // half.
   constexpr int A_PIECES = BM * kBK * 2 / 16 / 256;  // 16-byte pieces of x per thread
   const int a_chunk = tid & 7;
   const char* xb = reinterpret_cast<const char*>(x);
-  // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns.
+  // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns; with
+  // fewer pieces than threads the rest duplicate them.
   constexpr int B_PIECES = BW * kBK / 4;                 // 256 (BW 16) or 128 (BW 8)
-  const bool b_active = tid < B_PIECES;
-  const int b_row = tid / (BW / 4), b_wc = (tid % (BW / 4)) * 4;
-  // group data: thread t < 2 * BW loads a zero word (group t / BW, word column
-  // t % BW); the next 2 * BN / 8 threads load 8 scales (16 bytes) each.
+  const int b_id = tid % B_PIECES;
+  const int b_row = b_id / (BW / 4), b_wc = (b_id % (BW / 4)) * 4;
+  // group data: thread t < 2 GP loads piece t % GP of half t / GP.
+  const int g_half = tid < GP ? 0 : 1;
+  const int g_u = tid - g_half * GP;                     // piece within the half
+  const int g_slot = min(tid, 2 * GP);
   struct Stage {
     u32x4 a[A_PIECES];
     u32x4 b;
-    uint32_t z;
-    u32x4 s;
+    u32x4 gd;
   };
   auto stage_load = [&](Stage& st, int k0) {
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
-      const int row = m0 + (tid >> 3) + 32 * i;
-      const int rr = row < M ? row : M - 1;          // rows >= M: clamped, never stored
-      const int kk = min(k0 + 8 * a_chunk, K - 8);   // k >= K: clamped, step skipped
-      st.a[i] = *reinterpret_cast<const u32x4*>(xb + ((int64_t)rr * K + kk) * 2);
+      const int row = min(m0 + (tid >> 3) + 32 * i, M - 1);
+      const int kk = min(k0 + 8 * a_chunk, K - 8);
+      st.a[i] = *reinterpret_cast<const u32x4*>(xb + ((int64_t)row * K + kk) * 2);
     }
-    if (b_active) {
+    {
       const int r = min(k0 + b_row, K - 1);
-      const int wc = min(wc0 + b_wc, NW - 4);        // columns >= N: clamped, never stored
+      const int wc = min(wc0 + b_wc, NW - 4);
       st.b = *reinterpret_cast<const u32x4*>(qweight + (int64_t)r * NW + wc);
     }
-    const int ga = k0 / g, gb = min(K - 1, k0 + kBK - 1) / g;
-    if (tid < 2 * BW) {
-      const int gi = (tid < BW) ? ga : gb;
-      const int wc = min(wc0 + tid % BW, NW - 1);
-      st.z = qzeros[(int64_t)gi * NW + wc];
-    } else if (tid < 2 * BW + 2 * BN / 8) {
-      const int u = tid - 2 * BW;
-      const int gi = (u < BN / 8) ? ga : gb;
-      const int wc = min(wc0 + u % (BN / 8), NW - 1);
-      st.s = *reinterpret_cast<const u32x4*>(scales + (int64_t)gi * N + 8 * wc);
-    }
+    // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
+    // inside the k-tile can only fall between the halves.
+    const int gi = min(k0 + g_half * (kBK / 2), K - 1) / g;
+    // Blended operands (z = 0 / 1) rather than selected pointers, so that the
+    // compiler makes no branch of it.
+    const int64_t z = g_u < ZP;
+    const int64_t zcol = min(wc0 + 4 * g_u, NW - 4), scol = min(n0 + 8 * (g_u - ZP), N - 8);
+    const int64_t zrow = (int64_t)gi * NW, srow = (int64_t)gi * N;
+    const int64_t byte_off = ((srow + scol) << 1) + z * (((zrow + zcol) << 2) - ((srow + scol) << 1));
+    const int64_t base = reinterpret_cast<int64_t>(scales) +
+                         z * (reinterpret_cast<int64_t>(qzeros) - reinterpret_cast<int64_t>(scales));
+    st.gd = *reinterpret_cast<const u32x4*>(base + byte_off);
   };
   auto stage_store = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i)
       *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32 * i][8 * a_chunk]) = st.a[i];
-    if (b_active) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
-    }
-    if (tid < 2 * BW) {
-      Zs[buf][tid / BW][tid % BW] = st.z;
-    } else if (tid < 2 * BW + 2 * BN / 8) {
-      const int u = tid - 2 * BW;
-      *reinterpret_cast<u32x4*>(&Ss[buf][u / (BN / 8)][8 * (u % (BN / 8))]) = st.s;
-    }
+    for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
+    Gs[buf][g_slot] = st.gd;
   };
 
   // ---- This lane's column(s) of the B operand.
@@ -154,13 +156,15 @@ __global__ __launch_bounds__(256) void tile_kernel(
   const _Float16 zbase = hi_nib ? (_Float16)64.f : (_Float16)1024.f;
 
   half2v off0, off1, sc0, sc1;
-  auto apply_group = [&](int buf, int g2) {
-    const uint32_t zw = Zs[buf][g2][wloc];
+  auto apply_group = [&](int buf, int h) {
+    const uint32_t* gz = reinterpret_cast<const uint32_t*>(&Gs[buf][h * GP]);
+    const _Float16* gs = reinterpret_cast<const _Float16*>(&Gs[buf][h * GP + ZP]);
+    const uint32_t zw = gz[wloc];
     off0 = splat(-(zbase + (_Float16)(float)((zw >> (4 * p0)) & 0xFu)));
-    sc0 = splat(Ss[buf][g2][c0]);
+    sc0 = splat(gs[c0]);
     if (FN == 2) {
       off1 = splat(-(zbase + (_Float16)(float)((zw >> (4 * (p0 + 4))) & 0xFu)));
-      sc1 = splat(Ss[buf][g2][c1]);
+      sc1 = splat(gs[c1]);
     }
   };
 
@@ -172,70 +176,87 @@ __global__ __launch_bounds__(256) void tile_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Multiply the k-tile staged in LDS buffer buf (k-tile kt).
-  auto compute = [&](int kt, int buf) {
-    const int k0 = kt * kBK;
-    const int ga = k0 / g;
-    int cur = -1;
+  // Multiply the k-tile staged in LDS buffer buf: STEPS k16 steps (4, or 2 for a
+  // partial last k-tile).  Straight-line code with the fragments of step s + 1
+  // read from LDS while step s is dequantised and multiplied; the group data of
+  // half h is applied before steps 2h and 2h + 1.
+  struct Frag {
+    half8v a[FM];
+    u32x4 wlo, whi;
+  };
+  auto read_frag = [&](Frag& f, int buf, int s) {
+    f.wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq]);
+    f.whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq + 4]);
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int k = k0 + 16 * s;
-      if (k < K) {  // uniform; a partial last k-tile has 32 valid k
-        const int g2 = k / g - ga;  // 0 or 1
-        if (g2 != cur) {
-          apply_group(buf, g2);
-          cur = g2;
-        }
-        const u32x4 wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq]);
-        const u32x4 whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq + 4]);
-        const uint32_t w[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
-        half2v h0[4], h1[4];
+    for (int i = 0; i < FM; ++i)
+      f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][16 * s + kq]);
+  };
+  auto compute = [&](auto steps_c, int buf) {
+    constexpr int STEPS = decltype(steps_c)::value;
+    Frag fr[2];
+    read_frag(fr[0], buf, 0);
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
-          h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
-          if (FN == 2)
-            h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
-        }
-        half8v bf[2];
-        bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
-        if (FN == 2) bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+    for (int s = 0; s < STEPS; ++s) {
+      const Frag& f = fr[s & 1];
+      if (s + 1 < STEPS) read_frag(fr[(s + 1) & 1], buf, s + 1);
+      if (s % 2 == 0) apply_group(buf, s / 2);
+      const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
+      half2v h0[4], h1[4];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const half8v af =
-              *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][16 * s + kq]);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
-        }
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
+        h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
+        if (FN == 2)
+          h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
       }
+      half8v bf[2];
+      bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
+      if (FN == 2) bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
+  using Full = std::integral_constant<int, kBK / 16>;
+  using Half = std::integral_constant<int, kBK / 32>;
 
   // k-tile t lives in register set t % 2 (st0 / st1) and LDS buffer t % 2.  After
-  // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.
-  const int KT = (K + kBK - 1) / kBK;
+  // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.  The loop
+  // covers pairs of full k-tiles with no branches: loads past the last k-tile
+  // re-read it (clamped) and their stores land in a buffer no one reads again.
+  const int KT = (K + kBK - 1) / kBK;   // k-tiles, the last one partial when K % 64 = 32
+  const int KTF = K / kBK;              // full k-tiles
+  auto kofs = [&](int t) { return min(t, KT - 1) * kBK; };
   Stage st0, st1;
   stage_load(st0, 0);
   stage_store(st0, 0);
-  if (KT > 1) stage_load(st1, kBK);
-  if (KT > 2) stage_load(st0, 2 * kBK);
+  stage_load(st1, kofs(1));
+  stage_load(st0, kofs(2));
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    compute(kt, 0);
+  int kt = 0;
+  for (; kt + 2 <= KTF; kt += 2) {
+    compute(Full{}, 0);
+    stage_store(st1, 1);
+    stage_load(st1, kofs(kt + 3));
+    __syncthreads();
+    compute(Full{}, 1);
+    stage_store(st0, 0);
+    stage_load(st0, kofs(kt + 4));
+    __syncthreads();
+  }
+  // Left: k-tile kt (in buffer 0) and possibly kt + 1 (in st1), of which at most
+  // one is full.
+  if (kt < KTF) {
+    compute(Full{}, 0);
     if (kt + 1 < KT) {
       stage_store(st1, 1);
-      if (kt + 3 < KT) stage_load(st1, (kt + 3) * kBK);
-    }
-    __syncthreads();
-    if (kt + 1 < KT) {
-      compute(kt + 1, 1);
-      if (kt + 2 < KT) {
-        stage_store(st0, 0);
-        if (kt + 4 < KT) stage_load(st0, (kt + 4) * kBK);
-      }
       __syncthreads();
+      compute(Half{}, 1);
     }
+  } else if (kt < KT) {
+    compute(Half{}, 0);
   }
 
   // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4,
