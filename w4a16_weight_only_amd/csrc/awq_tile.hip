@@ -40,6 +40,13 @@
 #include "awq_device.h"
 #include "awq_kernels.h"
 
+#ifndef TILE0_FM
+#define TILE0_FM 4
+#define TILE0_FN 2
+#define TILE0_WM 2
+#define TILE0_MINB 1
+#endif
+
 namespace awq {
 
 namespace {
@@ -52,14 +59,15 @@ __device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 
 
 }  // namespace
 
-template <int FM, int FN>
-__global__ __launch_bounds__(256) void tile_kernel(
+template <int FM, int FN, int WM, int MINB>
+__global__ __launch_bounds__(256, MINB) void tile_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
     const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles,
     _Float16* __restrict__ y) {
-  constexpr int BM = 2 * 32 * FM;     // workgroup rows
-  constexpr int BN = 2 * 32 * FN;     // workgroup columns
+  constexpr int WN = 4 / WM;          // waves along N
+  constexpr int BM = WM * 32 * FM;    // workgroup rows
+  constexpr int BN = WN * 32 * FN;    // workgroup columns
   constexpr int BW = BN / 8;          // packed word columns per workgroup (16 or 8)
   constexpr int WW = 32 * FN / 8;     // packed word columns per wave (8 or 4)
   constexpr int kBLd = kBK + 4;       // words per staged word column (padded)
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void tile_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int tile_m = blockIdx.x % m_tiles;
   const int tile_n = blockIdx.x / m_tiles;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
@@ -140,7 +148,6 @@ __global__ __launch_bounds__(256) void tile_kernel(
   const int wsub = FN == 2 ? (lc & 7) : (lc & 3);
   const int p0 = FN == 2 ? ((lc >> 3) & 3) : ((lc >> 2) & 7);  // nibble of N-tile 0
   const int wloc = wn * WW + wsub;             // word column within the workgroup tile
-  const int wcol = wc0 + wloc;
   const int kq = 8 * (lane >> 5);              // this lane's k offset within a k16 step
   // v_perm_b32 selector: [a.t0, a.t1, b.t0, b.t1], t0 = byte of nibble p0, t1 = t0 + 2.
   const int byte0 = p0 >> 1;
@@ -259,21 +266,40 @@ __global__ __launch_bounds__(256) void tile_kernel(
     compute(Half{}, 0);
   }
 
-  // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4,
-  // MFMA column l % 32 -> output column n0 + c0 / c1.
-  if (wcol < NW) {
+  // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4
+  // of the block, MFMA column l % 32 -> tile column c0 / c1 (for FN = 2 the pair
+  // c0, c0 + 1).  The fp16 tile (bias added in fp32) is staged in LDS over the x
+  // buffers, then written as whole 16-byte pieces of rows.
+  constexpr int YLD = BN + 16;  // staged row (halves); rows 4 apart fall in opposite bank halves
+  static_assert(BM * YLD <= 2 * BM * kALd, "staged output must fit in the x buffers");
+  _Float16* Ys = &As[0][0][0];
+  __syncthreads();  // every wave is done reading As
+  float bj[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + (j == 0 ? c0 : c1);
-      const float b = bias ? (float)bias[n] : 0.f;
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + (j == 0 ? c0 : c1);
+    bj[j] = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
+  }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < M) y[(int64_t)row * N + n] = (_Float16)(acc[i][j][r] + b);
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (FN == 2)
+        *reinterpret_cast<half2v*>(&Ys[row * YLD + c0]) =
+            half2v{(_Float16)(acc[i][0][r] + bj[0]), (_Float16)(acc[i][FN - 1][r] + bj[FN - 1])};
+      else
+        Ys[row * YLD + c0] = (_Float16)(acc[i][0][r] + bj[0]);
     }
+  __syncthreads();
+  constexpr int PR = BN / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int q = tid; q < BM * PR; q += 256) {
+    const int row = q / PR, p = q % PR;
+    const int grow = m0 + row, gcol = n0 + 8 * p;
+    if (grow < M && gcol < N)
+      *reinterpret_cast<u32x4*>(&y[(int64_t)grow * N + gcol]) =
+          *reinterpret_cast<const u32x4*>(&Ys[row * YLD + 8 * p]);
   }
 }
 
@@ -289,8 +315,8 @@ hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t*
                        reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles,
                        reinterpret_cast<_Float16*>(y));
   };
-  if (variant == 0) go(tile_kernel<4, 2>, 256, 128);
-  else go(tile_kernel<2, 1>, 128, 64);
+  if (variant == 0) go(tile_kernel<TILE0_FM, TILE0_FN, TILE0_WM, TILE0_MINB>, TILE0_FM * TILE0_WM * 32, TILE0_FN * (4 / TILE0_WM) * 32);
+  else go(tile_kernel<2, 1, 2, 1>, 128, 64);
   return hipGetLastError();
 }
 
