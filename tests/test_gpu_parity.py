@@ -97,6 +97,9 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (64, 1024, 4128, 128, True),
     (1, 131072, 64, -1, True),   # skinny at the 128-split cap, 64 k-steps per wave
     (3, 65536, 96, 32, True),    # too many groups per workgroup for skinny: tile family
+    (40, 4128, 96, 32, True),    # tile split over K, last split ends in a half k-tile
+    (100, 2080, 160, -1, True),  # 128 x 64 tiles split over K
+    (300, 4096, 256, 128, False),  # 256 x 128 tiles split over K
 ]
 
 
@@ -190,9 +193,10 @@ def test_deterministic(name):
 
 def test_reduction_modes_share_a_stream():
     """Alternate plans that combine K splits differently (fixed-point atomics for
-    M <= 4, fp32 partials + reduce kernel above) on one stream, twice over: each
-    keeps its own workspace state valid for the other."""
-    shapes = [(1, 4096, 4096, 128), (16, 4096, 1024, 128), (3, 2048, 512, 64), (9, 4096, 2048, -1)]
+    M <= 4, fp32 partials + reduce kernel for skinny M > 4 and for split tiles) on
+    one stream, twice over: each keeps its own workspace state valid for the others."""
+    shapes = [(1, 4096, 4096, 128), (16, 4096, 1024, 128), (3, 2048, 512, 64), (9, 4096, 2048, -1),
+              (64, 2048, 512, 64)]
     for rep in range(2):
         for (M, K, N, g) in shapes:
             d = synth.make_custom(M, K, N, g, seed=rep + M)

@@ -39,11 +39,11 @@ int limits_check(int64_t M, int64_t K, int64_t N, int64_t group_size) {
 
 struct Plan {
   int family = 0;  // 0 skinny, 1 tile
-  int tile_variant = 0;
   awq::SkinnyPlan sk{};
+  awq::TilePlan tp{};
   int grid_x = 0, grid_y = 0, block = 0;
   int64_t accum_bytes = 0;    // zero-maintained fixed-point accumulators (4-wave plans)
-  int64_t partial_bytes = 0;  // scratch fp32 partials (8-wave plans)
+  int64_t partial_bytes = 0;  // scratch fp32 partials (8-wave skinny plans, split tile plans)
   int64_t workspace_bytes() const { return accum_bytes + partial_bytes; }
 };
 
@@ -128,13 +128,30 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
   } else {
     p.family = 1;
     p.block = awq::kTileThreads;
-    // The large tile unless it would leave most compute units idle.
     auto tiles = [&](int v) {
       return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
     };
-    p.tile_variant = tiles(0) >= (int64_t)cus * 3 / 4 ? 0 : 1;
-    p.grid_x = (int)tiles(p.tile_variant);
-    p.grid_y = 1;
+    // The large tile while it fills the device by itself; below that, the tile
+    // whose rows fit M best, and K split until the grid covers every compute unit
+    // (each split keeps at least 8 k-tiles).
+    const int64_t fill = (int64_t)cus * 3 / 4;
+    int v = 0;
+    if (tiles(0) < fill) v = M > 128 ? 0 : (M > 64 ? 1 : 2);
+    const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
+    int64_t splits = 1;
+    if (tiles(v) < fill) {
+      splits = ((int64_t)cus + tiles(v) - 1) / tiles(v);
+      const int64_t max_splits = KT / 8 > 1 ? KT / 8 : 1;
+      if (splits > max_splits) splits = max_splits;
+    }
+    const int64_t kps = (KT + splits - 1) / splits;
+    splits = (KT + kps - 1) / kps;
+    p.tp.variant = v;
+    p.tp.splits = (int)splits;
+    p.tp.kps = (int)kps;
+    p.grid_x = (int)tiles(v);
+    p.grid_y = (int)splits;
+    if (splits > 1) p.partial_bytes = splits * M * N * 4;
   }
   return p;
 }
@@ -236,7 +253,7 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* fami
   else (void)hipGetLastError();
   const Plan p = make_plan(M, K, N, eff_group(K, group_size), cus);
   if (family) *family = p.family;
-  if (splits) *splits = p.family == 0 ? p.sk.splits : 1;
+  if (splits) *splits = p.family == 0 ? p.sk.splits : p.tp.splits;
   if (grid_x) *grid_x = p.grid_x;
   if (grid_y) *grid_y = p.grid_y;
   if (block) *block = p.block;
@@ -283,7 +300,13 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
     e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, partial, y,
                            stream);
   } else {
-    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tile_variant, y, stream);
+    uint64_t* accum = nullptr;
+    float* partial = nullptr;
+    if (p.tp.splits > 1) {
+      const int ws = get_workspace(p, stream, &accum, &partial);
+      if (ws != AWQ_OK) return ws;
+    }
+    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tp, partial, y, stream);
   }
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
 }

@@ -26,11 +26,20 @@ struct SkinnyPlan {
   bool single_group; // every wave's k-steps lie in one quantization group
 };
 
-// MFMA tile family: 4 waves; variant 0 covers 256 x 128 outputs per workgroup,
-// variant 1 covers 128 x 64.
+// MFMA tile family: 4 waves per workgroup.  Variants (rows x columns per workgroup):
+// 0: 256 x 128, 1: 128 x 64, 2: 64 x 128.  With splits > 1 each workgroup covers kps
+// k-tiles of 64 and writes fp32 sums to partial, [splits][M][N]; a second kernel
+// adds the splits and the bias.
 constexpr int kTileThreads = 256;
-constexpr int kTileBM[2] = {256, 128};
-constexpr int kTileBN[2] = {128, 64};
+constexpr int kTileVariants = 3;
+constexpr int kTileBM[kTileVariants] = {256, 128, 64};
+constexpr int kTileBN[kTileVariants] = {128, 64, 128};
+constexpr int kTileBK = 64;
+struct TilePlan {
+  int variant;
+  int splits;  // K splits (1: direct fp16 output)
+  int kps;     // k-tiles of kTileBK per split
+};
 
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, float* out, hipStream_t stream);
@@ -45,6 +54,6 @@ hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       int variant, uint16_t* y, hipStream_t stream);
+                       const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream);
 
 }  // namespace awq

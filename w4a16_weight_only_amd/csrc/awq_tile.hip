@@ -40,13 +40,6 @@
 #include "awq_device.h"
 #include "awq_kernels.h"
 
-#ifndef TILE0_FM
-#define TILE0_FM 4
-#define TILE0_FN 2
-#define TILE0_WM 2
-#define TILE0_MINB 1
-#endif
-
 namespace awq {
 
 namespace {
@@ -63,8 +56,8 @@ template <int FM, int FN, int WM, int MINB>
 __global__ __launch_bounds__(256, MINB) void tile_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles,
-    _Float16* __restrict__ y) {
+    const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
+    float* __restrict__ partial, _Float16* __restrict__ y) {
   constexpr int WN = 4 / WM;          // waves along N
   constexpr int BM = WM * 32 * FM;    // workgroup rows
   constexpr int BN = WN * 32 * FN;    // workgroup columns
@@ -233,11 +226,15 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.  The loop
   // covers pairs of full k-tiles with no branches: loads past the last k-tile
   // re-read it (clamped) and their stores land in a buffer no one reads again.
-  const int KT = (K + kBK - 1) / kBK;   // k-tiles, the last one partial when K % 64 = 32
-  const int KTF = K / kBK;              // full k-tiles
-  auto kofs = [&](int t) { return min(t, KT - 1) * kBK; };
+  // This workgroup's k-tiles: [kt0, kt0 + KT) of the layer's; the layer's last
+  // k-tile is partial when K % 64 = 32.
+  const int KT_all = (K + kBK - 1) / kBK;
+  const int kt0 = blockIdx.y * kps;
+  const int KT = min(KT_all, kt0 + kps) - kt0;
+  const int KTF = (kt0 + KT == KT_all && K % kBK != 0) ? KT - 1 : KT;  // full k-tiles
+  auto kofs = [&](int t) { return (kt0 + min(t, KT - 1)) * kBK; };
   Stage st0, st1;
-  stage_load(st0, 0);
+  stage_load(st0, kofs(0));
   stage_store(st0, 0);
   stage_load(st1, kofs(1));
   stage_load(st0, kofs(2));
@@ -268,8 +265,30 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
 
   // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4
   // of the block, MFMA column l % 32 -> tile column c0 / c1 (for FN = 2 the pair
-  // c0, c0 + 1).  The fp16 tile (bias added in fp32) is staged in LDS over the x
-  // buffers, then written as whole 16-byte pieces of rows.
+  // c0, c0 + 1).
+  if (partial != nullptr) {
+    // Split K: this split's fp32 sums, no bias, to partial[split][M][N]; rows >= M
+    // and columns >= N are not stored.
+    float* pout = partial + (int64_t)blockIdx.y * M * N;
+    const int n = n0 + c0;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < M) {
+            if (FN == 2)
+              *reinterpret_cast<floatx2*>(&pout[(int64_t)row * N + n]) = floatx2{acc[i][0][r], acc[i][FN - 1][r]};
+            else
+              pout[(int64_t)row * N + n] = acc[i][0][r];
+          }
+        }
+    }
+    return;
+  }
+  // The fp16 tile (bias added in fp32) is staged in LDS over the x buffers, then
+  // written as whole 16-byte pieces of rows.
   constexpr int YLD = BN + 16;  // staged row (halves); rows 4 apart fall in opposite bank halves
   static_assert(BM * YLD <= 2 * BM * kALd, "staged output must fit in the x buffers");
   _Float16* Ys = &As[0][0][0];
@@ -303,20 +322,61 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   }
 }
 
+// y = fp16(sum over splits of partial[s] + bias), 8 columns per thread, splits
+// summed in order (deterministic).
+__global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restrict__ partial,
+                                                          const _Float16* __restrict__ bias, int64_t MN,
+                                                          int N, int splits, _Float16* __restrict__ y) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e >= MN) return;
+  floatx4 a = *reinterpret_cast<const floatx4*>(partial + e);
+  floatx4 b = *reinterpret_cast<const floatx4*>(partial + e + 4);
+  for (int s = 1; s < splits; ++s) {
+    a += *reinterpret_cast<const floatx4*>(partial + s * MN + e);
+    b += *reinterpret_cast<const floatx4*>(partial + s * MN + e + 4);
+  }
+  if (bias != nullptr) {
+    const int n = (int)(e % N);
+    const half8v bv = *reinterpret_cast<const half8v*>(bias + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] += (float)bv[j];
+      b[j] += (float)bv[4 + j];
+    }
+  }
+  half8v o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[j] = (_Float16)a[j];
+    o[4 + j] = (_Float16)b[j];
+  }
+  *reinterpret_cast<half8v*>(y + e) = o;
+}
+
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       int variant, uint16_t* y, hipStream_t stream) {
+                       const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream) {
+  const bool split = p.splits > 1;
   auto go = [&](auto kern, int bm, int bn) {
     const int m_tiles = (M + bm - 1) / bm;
     const int n_tiles = (N + bn - 1) / bn;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles)), dim3(256), 0, stream,
-                       reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(256), 0,
+                       stream, reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles,
-                       reinterpret_cast<_Float16*>(y));
+                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles, p.kps,
+                       split ? partial : nullptr, reinterpret_cast<_Float16*>(y));
   };
-  if (variant == 0) go(tile_kernel<TILE0_FM, TILE0_FN, TILE0_WM, TILE0_MINB>, TILE0_FM * TILE0_WM * 32, TILE0_FN * (4 / TILE0_WM) * 32);
-  else go(tile_kernel<2, 1, 2, 1>, 128, 64);
+  switch (p.variant) {
+    case 0: go(tile_kernel<4, 2, 2, 1>, 256, 128); break;
+    case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64); break;
+    default: go(tile_kernel<2, 1, 1, 1>, 64, 128); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const int64_t MN = (int64_t)M * N;
+  const int64_t blocks = (MN / 8 + 255) / 256;
+  hipLaunchKernelGGL(tile_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partial,
+                     reinterpret_cast<const _Float16*>(bias), MN, N, p.splits, reinterpret_cast<_Float16*>(y));
   return hipGetLastError();
 }
 
