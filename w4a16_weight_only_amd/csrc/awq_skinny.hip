@@ -171,31 +171,47 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     st.a = *reinterpret_cast<const half8v*>(xb + (x_off + (uint32_t)ks * (uint32_t)(kKStep * 2)));
   };
 
-  // 1. Weight loads of the first PF k-steps; group tables into LDS meanwhile.
+  // 1. Group data and weight loads.
+  //   One group per wave (SINGLE): every lane loads the zero words and fp16 scales of
+  //   its two word columns for its wave's group straight into registers, before the
+  //   weights, so that nothing waits for the weights but the multiply itself and no
+  //   workgroup barrier is needed.
+  //   Several groups: the workgroup turns the zero words and scales of every group
+  //   it touches into per-lane LDS tables while the weights are in flight.
+  u32x2 gz = {0u, 0u};
+  half8v gs0 = {}, gs1 = {};
+  if constexpr (SINGLE) {
+    const int gw = min(kb, T - 1) / gsteps;  // a wave without k-steps loads a valid group
+    const int wcc = col_ok ? wc : 0;
+    gz = *reinterpret_cast<const u32x2*>(qzeros + (int64_t)gw * NW + wcc);
+    const _Float16* sp = scales + (int64_t)gw * N + 8 * wcc;
+    gs0 = *reinterpret_cast<const half8v*>(sp);
+    gs1 = *reinterpret_cast<const half8v*>(sp + 8);
+  }
   Step ring[PF];
 #pragma unroll
   for (int j = 0; j < PF; ++j)
     if (kb + j < ke) issue(ring[j], kb + j);
-  {
+  if constexpr (!SINGLE) {
     const int ng = (s1 > s0) ? (s1 - 1) / gsteps - g0 + 1 : 0;  // <= kSkinnyMaxGroups (host)
     for (int i = tid; i < ng * 256; i += THREADS) {
       const int gl = i >> 8, cc = (i >> 4) & 15, v = i & 15;
       const int wcol = tile * kSkinnyWordCols + 2 * cc + (v >> 3);
       const int col = tab_col(v);
       uint32_t zw = 0u;
-      float s = 0.f;
+      float sv = 0.f;
       if (wcol < NW) {
         zw = qzeros[(int64_t)(g0 + gl) * NW + wcol];
-        s = (float)scales[(int64_t)(g0 + gl) * N + 8 * wcol + col];
+        sv = (float)scales[(int64_t)(g0 + gl) * N + 8 * wcol + col];
       }
       const uint32_t z = zero_code(zw, col);
       // fp16 bits of -(1024 + z) (low nibble) or -(64 + z) (high nibble), splatted.
       const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
       sh.u.meta.zsplat[gl][cc][v] = h | (h << 16);
-      sh.u.meta.scale[gl][cc][v] = s;
+      sh.u.meta.scale[gl][cc][v] = sv;
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   floatx4 part[16];
   floatx4 acc[16];
@@ -215,24 +231,29 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       dst[4 * k4 + 3] = v[3];
     }
   };
-  // Scale this group's sums: into acc (several groups) or in place (one group).
+  // Scale this group's sums into acc (several groups).
   auto flush = [&](int gl) {
     uint32_t sb[16];
     load_tab(reinterpret_cast<const uint32_t*>(sh.u.meta.scale[gl][c]), sb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float s = __builtin_bit_cast(float, sb[v]);
-      if (SINGLE) {
-        part[v] *= s;
-      } else {
-        acc[v] += s * part[v];
-        part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+      acc[v] += __builtin_bit_cast(float, sb[v]) * part[v];
+      part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
   const UnpackConsts uk = unpack_consts();
   uint32_t zs[16];
+  if constexpr (SINGLE) {
+    // Entry v: word w = v / 8, column tab_col(v) of it; zero splat as in the tables.
+    const uint32_t zw[2] = {gz[0], gz[1]};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const uint32_t z = zero_code(zw[v >> 3], tab_col(v));
+      const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
+      zs[v] = h | (h << 16);
+    }
+  }
   int cur_g = -1;
   // Ring of PF k-steps in flight: after step ks is consumed its slot loads ks + PF.
   for (int base = kb; base < ke; base += PF) {
@@ -240,19 +261,31 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     for (int j = 0; j < PF; ++j) {
       const int ks = base + j;
       if (ks < ke) {
-        const int gl = ks / gsteps - g0;
-        if (gl != cur_g) {
-          if (!SINGLE && cur_g >= 0) flush(cur_g);
-          load_tab(sh.u.meta.zsplat[gl][c], zs);
-          cur_g = gl;
+        if constexpr (!SINGLE) {
+          const int gl = ks / gsteps - g0;
+          if (gl != cur_g) {
+            if (cur_g >= 0) flush(cur_g);
+            load_tab(sh.u.meta.zsplat[gl][c], zs);
+            cur_g = gl;
+          }
         }
         kstep_mfma(ring[j], zs, uk, part);
         if (ks + PF < ke) issue(ring[j], ks + PF);
       }
     }
   }
-  if (cur_g >= 0) flush(cur_g);
-  __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
+  if constexpr (SINGLE) {
+    // Scale the group's sums; a single row only needs the first element of each.
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float sv = (float)((v >> 3) ? gs1[tab_col(v)] : gs0[tab_col(v)]);
+      if (M == 1) part[v][0] *= sv;
+      else part[v] *= sv;
+    }
+  } else {
+    if (cur_g >= 0) flush(cur_g);
+    __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
+  }
 
   // 2. Waves -> LDS in register order, then sums over waves per slot.  With at most
   // 4 rows only the q = 0 lanes (rows 0..3) hold rows that are ever stored.
