@@ -63,8 +63,8 @@ int device_cus() {
   return cus;
 }
 
-#ifndef AWQ_SKINNY_WG_PER_CU
-#define AWQ_SKINNY_WG_PER_CU 2  // resident 4-wave workgroups per compute unit
+#ifndef AWQ_SKINNY_WG_PER_2CU
+#define AWQ_SKINNY_WG_PER_2CU 4  // 4-wave workgroups per two compute units
 #endif
 
 // Skinny plan for M <= kSkinnyMaxM, or false when no launch shape fits the
@@ -79,13 +79,16 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   s.waves = M <= 4 ? 4 : 8;
   s.mrows = M <= 4 ? 4 : 16;
   const int64_t W = s.waves;
-  // Whole grid resident in one round: 4-wave workgroups fit AWQ_SKINNY_WG_PER_CU per
-  // CU, 8-wave ones (large LDS reduction buffer) one per CU.
-  const int64_t cap = (int64_t)cus * (s.waves == 4 ? AWQ_SKINNY_WG_PER_CU : 1);
+  // Whole grid resident in one round: 4-wave workgroups fit two per CU, 8-wave ones
+  // (large LDS reduction buffer) one per CU.
+  const int64_t cap = s.waves == 4 ? (int64_t)cus * AWQ_SKINNY_WG_PER_2CU / 2 : (int64_t)cus;
   int64_t L = (T * s.n_tiles + W * cap - 1) / (W * cap);
   const int64_t l_min = (T + W * awq::kSkinnyMaxSplits - 1) / (W * awq::kSkinnyMaxSplits);
   if (L < l_min) L = l_min;
-  if (L < 1) L = 1;
+  // At least two k-steps per wave, so that each wave's second step is in flight
+  // while its first is multiplied (measured faster than one step per wave even
+  // at half the workgroups).
+  if (L < 2) L = 2;
   if (L > T) L = T;
   auto splits_of = [&](int64_t l) { return (T + W * l - 1) / (W * l); };
   if (gsteps >= T) {
