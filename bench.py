@@ -1,6 +1,7 @@
 """Benchmark of the fused AWQ W4A16 linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-secondary] [--copy-calibration]
 
 A step is one awq_gemm call (dispatch by M, packed-weight streaming, unpack,
 dequant, multiply-accumulate, reduction, bias, fp16 store) on the workload's
@@ -16,7 +17,8 @@ for the bandwidth-bound workloads or TFLOP/s for the compute-bound prefill
 workload, over the whole timed region.  `roofline` prices the kernel's average
 launch duration (HIP events on the launch stream over the timed region) against
 MI355X's peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+same workload.  `read_ceiling` times a plain streaming read of the same byte count;
+`secondary` repeats the timing (not the CPU leg) for every other workload.
 """
 from __future__ import annotations
 
@@ -43,8 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--secondary", action="store_true",
-                    help="also time the M=16 and M=2048 workloads (reported under 'secondary')")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workloads (reported under 'secondary' by default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 256 MiB device-to-device copies, a plain copy kernel of "
                          "known size that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -55,6 +57,8 @@ def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_weight_only_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not os.path.isfile(os.path.join(csrc, f)):
+            continue  # the probe/ subdirectory is not an AWQ kernel
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -126,6 +130,51 @@ def time_workload(name, steps, warmup, torch, awq, synth):
     torch.cuda.empty_cache()
     return dict(workload=w, wall_s=wall_s, event_s=event_s, copies=copies,
                 plan=awq.plan(w.M, w.K, w.N, w.group_size))
+
+
+def read_ceiling(nbytes, torch, steps=400):
+    """A plain streaming read of the same byte count for comparison: the probe
+    library's read kernel (16-byte nontemporal loads, 16 KiB contiguous per
+    workgroup, no arithmetic), over the same rotation of >= 512 MB of copies and
+    replayed from a HIP graph like the timed steps.  At a few MB per launch it is
+    bound by launch and memory latency rather than by HBM bandwidth."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "w4a16_weight_only_amd", "libawq_probe.so"))
+    probe.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    probe.awq_probe_stream_read.restype = ctypes.c_int
+    n = max(16, nbytes // 16 * 16)
+    copies = max(1, -(-ROTATE_BYTES // n))
+    bufs = [torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(n // 16384 + 1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def go(i):
+        st = probe.awq_probe_stream_read(bufs[i % copies].data_ptr(), n, sink.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"awq_probe_stream_read failed: {st}")
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            go(i)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            go(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        stream.synchronize()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(bytes=n, us_per_launch=round(us, 3), gbs=round(n / (us * 1e-6) / 1e9, 1),
+                how="libawq_probe.so stream read of the same byte count, rotated, graph-replayed")
 
 
 def summarize(r, steps):
@@ -225,15 +274,18 @@ def main():
         "kernel_avg_us": round(per_launch_s * 1e6, 3),
         "source_digest": digest,
     }
-    if args.secondary:
+    out["read_ceiling"] = read_ceiling(w.algorithmic_bytes(), torch)
+    if not args.no_secondary:
+        # Every other workload once, shorter: parity-test shapes, reported for context.
         sec = []
-        for name in ("decode_m16_k4096_n11008_g128", "prefill_m2048_k4096_n4096_g128"):
-            if name == args.workload:
+        for name in synth.WORKLOADS:
+            if name == args.workload or name.startswith("tiny"):
                 continue
-            rs = time_workload(name, min(args.steps, 400), 10, torch, awq, synth)
-            v, u, rf, pl = summarize(rs, min(args.steps, 400))
+            n_steps = min(args.steps, 200)
+            rs = time_workload(name, n_steps, 10, torch, awq, synth)
+            v, u, rf, pl = summarize(rs, n_steps)
             sec.append(dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3),
-                            roofline=rf))
+                            plan=rs["plan"], roofline=rf))
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, synth)

@@ -20,6 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libawq_w4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+PROBE_PATH = os.path.join(HERE, "libawq_probe.so")
 SOURCES = ["awq_api.hip", "awq_dequant.hip", "awq_skinny.hip", "awq_tile.hip"]
 ARCH = "gfx950"
 
@@ -62,6 +63,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    # The streaming-read probe the benchmark times next to awq_gemm: its own library.
+    tmp = PROBE_PATH + ".tmp"
+    _run([cc, *COMPILE_FLAGS, "-shared", os.path.join(CSRC, "probe", "stream_read.hip"), "-o", tmp])
+    os.replace(tmp, PROBE_PATH)
     return LIB_PATH
 
 
