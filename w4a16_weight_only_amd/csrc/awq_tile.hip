@@ -82,17 +82,33 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   const int wc0 = n0 / 8;
 
   // ---- Global -> register staging of one k-tile.  Every thread runs the same
-  // code (no divergent branches): out-of-range rows and columns are clamped and
-  // never stored to y; rows past K are only read by a partial last k-tile's unused
-  // half.
+  // code (no divergent branches).  The x and qweight loads are a uniform base,
+  // advanced per k-tile in scalar registers, plus a per-lane 32-bit byte offset
+  // fixed for the whole kernel; out-of-range rows and columns are clamped into
+  // those offsets and never stored to y.  A partial last k-tile (K % 64 = 32) is
+  // loaded as the full k-tile ending at K, i.e. starting 32 rows early, and only
+  // its upper half is multiplied; when K = 32 (the only k-tile is partial) the
+  // lanes of the upper half re-read the lower half instead.
   constexpr int A_PIECES = BM * kBK * 2 / 16 / 256;  // 16-byte pieces of x per thread
   const int a_chunk = tid & 7;
+  const int a_ch = K < kBK ? (a_chunk & 3) : a_chunk;
   const char* xb = reinterpret_cast<const char*>(x);
+  int a_row0[A_PIECES];         // uniform first row of piece i (clamped)
+  uint32_t a_off[A_PIECES];     // lane's byte offset from that row
+#pragma unroll
+  for (int i = 0; i < A_PIECES; ++i) {
+    a_row0[i] = min(m0 + 32 * i, M - 1);
+    const int t = min(tid >> 3, M - 1 - a_row0[i]);
+    a_off[i] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
+  }
   // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns; with
   // fewer pieces than threads the rest duplicate them.
   constexpr int B_PIECES = BW * kBK / 4;                 // 256 (BW 16) or 128 (BW 8)
   const int b_id = tid % B_PIECES;
   const int b_row = b_id / (BW / 4), b_wc = (b_id % (BW / 4)) * 4;
+  const uint32_t b_off =
+      ((uint32_t)(K < kBK ? (b_row & 31) : b_row) * (uint32_t)NW + (uint32_t)min(wc0 + b_wc, NW - 4)) * 4u;
+  const char* wb = reinterpret_cast<const char*>(qweight);
   // group data: thread t < 2 GP loads piece t % GP of half t / GP.
   const int g_half = tid < GP ? 0 : 1;
   const int g_u = tid - g_half * GP;                     // piece within the half
@@ -102,21 +118,19 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
     u32x4 b;
     u32x4 gd;
   };
+  // First row loaded for the k-tile starting at k0 (see above).
+  auto tile_row = [&](int k0) { return (K - k0 < kBK && K >= kBK) ? k0 - kBK / 2 : k0; };
   auto stage_load = [&](Stage& st, int k0) {
+    const int kl = tile_row(k0);
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
-      const int row = min(m0 + (tid >> 3) + 32 * i, M - 1);
-      const int kk = min(k0 + 8 * a_chunk, K - 8);
-      st.a[i] = *reinterpret_cast<const u32x4*>(xb + ((int64_t)row * K + kk) * 2);
+      const char* base = xb + ((int64_t)a_row0[i] * K + kl) * 2;
+      st.a[i] = *reinterpret_cast<const u32x4*>(base + a_off[i]);
     }
-    {
-      const int r = min(k0 + b_row, K - 1);
-      const int wc = min(wc0 + b_wc, NW - 4);
-      st.b = *reinterpret_cast<const u32x4*>(qweight + (int64_t)r * NW + wc);
-    }
+    st.b = *reinterpret_cast<const u32x4*>(wb + (int64_t)kl * NW * 4 + b_off);
     // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
     // inside the k-tile can only fall between the halves.
-    const int gi = min(k0 + g_half * (kBK / 2), K - 1) / g;
+    const int gi = min(kl + g_half * (kBK / 2), K - 1) / g;
     // Blended operands (z = 0 / 1) rather than selected pointers, so that the
     // compiler makes no branch of it.
     const int64_t z = g_u < ZP;
@@ -176,8 +190,8 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Multiply the k-tile staged in LDS buffer buf: STEPS k16 steps (4, or 2 for a
-  // partial last k-tile).  Straight-line code with the fragments of step s + 1
+  // Multiply the k-tile staged in LDS buffer buf: k16 steps S0..S1-1 (all four, or
+  // the half holding a partial last k-tile's rows).  Straight-line code with the fragments of step s + 1
   // read from LDS while step s is dequantised and multiplied; the group data of
   // half h is applied before steps 2h and 2h + 1.
   struct Frag {
@@ -191,14 +205,14 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
     for (int i = 0; i < FM; ++i)
       f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][16 * s + kq]);
   };
-  auto compute = [&](auto steps_c, int buf) {
-    constexpr int STEPS = decltype(steps_c)::value;
+  auto compute = [&](auto s0_c, auto s1_c, int buf) {
+    constexpr int S0 = decltype(s0_c)::value, S1 = decltype(s1_c)::value;
     Frag fr[2];
-    read_frag(fr[0], buf, 0);
+    read_frag(fr[S0 & 1], buf, S0);
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
+    for (int s = S0; s < S1; ++s) {
       const Frag& f = fr[s & 1];
-      if (s + 1 < STEPS) read_frag(fr[(s + 1) & 1], buf, s + 1);
+      if (s + 1 < S1) read_frag(fr[(s + 1) & 1], buf, s + 1);
       if (s % 2 == 0) apply_group(buf, s / 2);
       const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
       half2v h0[4], h1[4];
@@ -219,8 +233,14 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
-  using Full = std::integral_constant<int, kBK / 16>;
-  using Half = std::integral_constant<int, kBK / 32>;
+  using C0 = std::integral_constant<int, 0>;
+  using C2 = std::integral_constant<int, 2>;
+  using C4 = std::integral_constant<int, 4>;
+  // A partial last k-tile holds its 32 rows in the upper half (K >= 64) or the lower.
+  auto compute_partial = [&](int buf) {
+    if (K >= kBK) compute(C2{}, C4{}, buf);
+    else compute(C0{}, C2{}, buf);
+  };
 
   // k-tile t lives in register set t % 2 (st0 / st1) and LDS buffer t % 2.  After
   // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.  The loop
@@ -241,11 +261,11 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   __syncthreads();
   int kt = 0;
   for (; kt + 2 <= KTF; kt += 2) {
-    compute(Full{}, 0);
+    compute(C0{}, C4{}, 0);
     stage_store(st1, 1);
     stage_load(st1, kofs(kt + 3));
     __syncthreads();
-    compute(Full{}, 1);
+    compute(C0{}, C4{}, 1);
     stage_store(st0, 0);
     stage_load(st0, kofs(kt + 4));
     __syncthreads();
@@ -253,14 +273,14 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   // Left: k-tile kt (in buffer 0) and possibly kt + 1 (in st1), of which at most
   // one is full.
   if (kt < KTF) {
-    compute(Full{}, 0);
+    compute(C0{}, C4{}, 0);
     if (kt + 1 < KT) {
       stage_store(st1, 1);
       __syncthreads();
-      compute(Half{}, 1);
+      compute_partial(1);
     }
   } else if (kt < KT) {
-    compute(Half{}, 0);
+    compute_partial(0);
   }
 
   // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4
