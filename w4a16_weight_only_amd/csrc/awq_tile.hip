@@ -40,6 +40,10 @@
 #include "awq_device.h"
 #include "awq_kernels.h"
 
+#ifndef TILE0_KG
+#define TILE0_KG 2
+#endif
+
 namespace awq {
 
 namespace {
@@ -52,12 +56,13 @@ __device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 
 
 }  // namespace
 
-template <int FM, int FN, int WM, int MINB>
-__global__ __launch_bounds__(256, MINB) void tile_kernel(
+template <int FM, int FN, int WM, int KG>
+__global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
     const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
     float* __restrict__ partial, _Float16* __restrict__ y) {
+  constexpr int THREADS = 256 * KG;   // KG groups of 4 waves; group kg takes k16 steps of its share
   constexpr int WN = 4 / WM;          // waves along N
   constexpr int BM = WM * 32 * FM;    // workgroup rows
   constexpr int BN = WN * 32 * FN;    // workgroup columns
@@ -67,14 +72,28 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   // Group data of one k-tile, per 32-row half: the zero words of the BW word columns
   // then the BN fp16 scales, in 16-byte pieces.
   constexpr int ZP = BW / 4, SP = BN / 8, GP = ZP + SP;  // pieces: zeros, scales, per half
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kALd];
-  __shared__ __attribute__((aligned(16))) uint32_t Bs[2][BW][kBLd];
-  __shared__ __attribute__((aligned(16))) u32x4 Gs[2][2 * GP + 1];  // + 1: sink of idle threads
+  constexpr int ACC = FM * FN * 16;   // accumulator registers per lane
+  struct Staging {
+    _Float16 As[2][BM][kALd];
+    uint32_t Bs[2][BW][kBLd];
+    u32x4 Gs[2][2 * GP + 1];  // + 1: sink of idle threads
+  };
+  // After the k loop the same LDS holds the second k-group's accumulators (KG = 2).
+  union Lds {
+    Staging st;
+    float red[KG == 2 ? 4 * ACC * 64 : 1];
+  };
+  __shared__ __attribute__((aligned(16))) Lds lds;
+  auto& As = lds.st.As;
+  auto& Bs = lds.st.Bs;
+  auto& Gs = lds.st.Gs;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int kg = wave >> 2;           // k-group
+  const int w4 = wave & 3;            // wave within the group
+  const int wm = w4 / WN, wn = w4 % WN;
   const int tile_m = blockIdx.x % m_tiles;
   const int tile_n = blockIdx.x / m_tiles;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
@@ -89,7 +108,8 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   // loaded as the full k-tile ending at K, i.e. starting 32 rows early, and only
   // its upper half is multiplied; when K = 32 (the only k-tile is partial) the
   // lanes of the upper half re-read the lower half instead.
-  constexpr int A_PIECES = BM * kBK * 2 / 16 / 256;  // 16-byte pieces of x per thread
+  constexpr int A_PIECES = BM * kBK * 2 / 16 / THREADS;  // 16-byte pieces of x per thread
+  constexpr int A_ROWS = THREADS / 8;                     // rows covered by one piece index
   const int a_chunk = tid & 7;
   const int a_ch = K < kBK ? (a_chunk & 3) : a_chunk;
   const char* xb = reinterpret_cast<const char*>(x);
@@ -97,13 +117,14 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   uint32_t a_off[A_PIECES];     // lane's byte offset from that row
 #pragma unroll
   for (int i = 0; i < A_PIECES; ++i) {
-    a_row0[i] = min(m0 + 32 * i, M - 1);
+    a_row0[i] = min(m0 + A_ROWS * i, M - 1);
     const int t = min(tid >> 3, M - 1 - a_row0[i]);
     a_off[i] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
   }
   // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns; with
   // fewer pieces than threads the rest duplicate them.
   constexpr int B_PIECES = BW * kBK / 4;                 // 256 (BW 16) or 128 (BW 8)
+  static_assert(B_PIECES <= THREADS, "one qweight piece per thread at most");
   const int b_id = tid % B_PIECES;
   const int b_row = b_id / (BW / 4), b_wc = (b_id % (BW / 4)) * 4;
   const uint32_t b_off =
@@ -144,7 +165,7 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   auto stage_store = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32 * i][8 * a_chunk]) = st.a[i];
+      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + A_ROWS * i][8 * a_chunk]) = st.a[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
     Gs[buf][g_slot] = st.gd;
@@ -198,22 +219,29 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
     half8v a[FM];
     u32x4 wlo, whi;
   };
-  auto read_frag = [&](Frag& f, int buf, int s) {
-    f.wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq]);
-    f.whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][16 * s + kq + 4]);
+  // kh: this wave's first 32-row half of the k-tile (0, or 1 for the second k-group).
+  auto read_frag = [&](Frag& f, int buf, int s, int kh) {
+    const int k = 16 * s + 32 * kh + kq;
+    f.wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k]);
+    f.whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k + 4]);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][16 * s + kq]);
+      f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][k]);
   };
-  auto compute = [&](auto s0_c, auto s1_c, int buf) {
+  // With one wave per SIMD (KG = 1) the fragments of step s + 1 are read while step s
+  // is multiplied; with two (KG = 2) the other wave covers that latency and the
+  // registers go to the second wave instead.
+  constexpr bool kPrefetch = KG == 1;
+  auto compute = [&](auto s0_c, auto s1_c, int buf, int kh) {
     constexpr int S0 = decltype(s0_c)::value, S1 = decltype(s1_c)::value;
-    Frag fr[2];
-    read_frag(fr[S0 & 1], buf, S0);
+    Frag fr[kPrefetch ? 2 : 1];
+    if (kPrefetch) read_frag(fr[S0 & 1], buf, S0, kh);
 #pragma unroll
     for (int s = S0; s < S1; ++s) {
-      const Frag& f = fr[s & 1];
-      if (s + 1 < S1) read_frag(fr[(s + 1) & 1], buf, s + 1);
-      if (s % 2 == 0) apply_group(buf, s / 2);
+      if (!kPrefetch) read_frag(fr[0], buf, s, kh);
+      const Frag& f = fr[kPrefetch ? (s & 1) : 0];
+      if (kPrefetch && s + 1 < S1) read_frag(fr[(s + 1) & 1], buf, s + 1, kh);
+      if (s % 2 == 0) apply_group(buf, s / 2 + kh);
       const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
       half2v h0[4], h1[4];
 #pragma unroll
@@ -235,53 +263,65 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   };
   using C0 = std::integral_constant<int, 0>;
   using C2 = std::integral_constant<int, 2>;
-  using C4 = std::integral_constant<int, 4>;
-  // A partial last k-tile holds its 32 rows in the upper half (K >= 64) or the lower.
-  auto compute_partial = [&](int buf) {
-    if (K >= kBK) compute(C2{}, C4{}, buf);
-    else compute(C0{}, C2{}, buf);
+  // This wave's share of k-tile buf: both 32-row halves (KG = 1) or the half of its
+  // k-group (KG = 2: group kg takes half kg, with that half's group data).  A partial
+  // last k-tile holds its 32 rows in the upper half (K >= 64) or the lower one
+  // (K = 32); only that half is multiplied.
+  const int part_half = K >= kBK ? 1 : 0;
+  auto run = [&](int buf, bool part) {
+#pragma unroll
+    for (int kh = (KG == 1 ? 0 : kg); kh < 2; kh += KG)
+      if (!part || kh == part_half) compute(C0{}, C2{}, buf, kh);
   };
 
-  // k-tile t lives in register set t % 2 (st0 / st1) and LDS buffer t % 2.  After
-  // multiplying k-tile t: store k-tile t + 1 to LDS, load k-tile t + 3.  The loop
-  // covers pairs of full k-tiles with no branches: loads past the last k-tile
-  // re-read it (clamped) and their stores land in a buffer no one reads again.
-  // This workgroup's k-tiles: [kt0, kt0 + KT) of the layer's; the layer's last
-  // k-tile is partial when K % 64 = 32.
+  // One register staging set and two LDS buffers: k-tile t is multiplied from
+  // buffer t % 2 while k-tile t + 1 waits in registers; then t + 1 goes to the other
+  // buffer and the loads of t + 2 are issued, so each load has one k-tile of work to
+  // arrive.  Loads past the last k-tile re-read it (clamped) and their stores land in
+  // a buffer no one reads again, so the loop body has no data-dependent branches.
+  // This workgroup's k-tiles: [kt0, kt0 + KT) of the layer's; the layer's last k-tile
+  // is partial when K % 64 = 32.
   const int KT_all = (K + kBK - 1) / kBK;
   const int kt0 = blockIdx.y * kps;
   const int KT = min(KT_all, kt0 + kps) - kt0;
-  const int KTF = (kt0 + KT == KT_all && K % kBK != 0) ? KT - 1 : KT;  // full k-tiles
   auto kofs = [&](int t) { return (kt0 + min(t, KT - 1)) * kBK; };
-  Stage st0, st1;
-  stage_load(st0, kofs(0));
-  stage_store(st0, 0);
-  stage_load(st1, kofs(1));
-  stage_load(st0, kofs(2));
+  Stage st;
+  stage_load(st, kofs(0));
+  stage_store(st, 0);
+  stage_load(st, kofs(1));
   __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= KTF; kt += 2) {
-    compute(C0{}, C4{}, 0);
-    stage_store(st1, 1);
-    stage_load(st1, kofs(kt + 3));
-    __syncthreads();
-    compute(C0{}, C4{}, 1);
-    stage_store(st0, 0);
-    stage_load(st0, kofs(kt + 4));
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    run(buf, kt0 + kt == KT_all - 1 && K % kBK != 0);
+    stage_store(st, buf ^ 1);
+    stage_load(st, kofs(kt + 2));
     __syncthreads();
   }
-  // Left: k-tile kt (in buffer 0) and possibly kt + 1 (in st1), of which at most
-  // one is full.
-  if (kt < KTF) {
-    compute(C0{}, C4{}, 0);
-    if (kt + 1 < KT) {
-      stage_store(st1, 1);
-      __syncthreads();
-      compute_partial(1);
+
+  // Two k-groups: group 1 hands its sums to group 0 through LDS (register order,
+  // conflict-free), group 0 adds them and finishes the tile.
+  if constexpr (KG == 2) {
+    __syncthreads();  // the staging buffers are dead
+    float* red = lds.red + w4 * ACC * 64 + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
     }
-  } else if (kt < KT) {
-    compute_partial(0);
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
+    }
   }
+  const bool owner = KG == 1 || kg == 0;  // holds finished sums
 
   // Epilogue.  32x32 MFMA output: lane l, register r holds row 8(r/4) + 4(l/32) + r%4
   // of the block, MFMA column l % 32 -> tile column c0 / c1 (for FN = 2 the pair
@@ -291,7 +331,7 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
     // and columns >= N are not stored.
     float* pout = partial + (int64_t)blockIdx.y * M * N;
     const int n = n0 + c0;
-    if (n < N) {
+    if (owner && n < N) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -312,28 +352,30 @@ __global__ __launch_bounds__(256, MINB) void tile_kernel(
   constexpr int YLD = BN + 16;  // staged row (halves); rows 4 apart fall in opposite bank halves
   static_assert(BM * YLD <= 2 * BM * kALd, "staged output must fit in the x buffers");
   _Float16* Ys = &As[0][0][0];
-  __syncthreads();  // every wave is done reading As
-  float bj[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + (j == 0 ? c0 : c1);
-    bj[j] = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (FN == 2)
-        *reinterpret_cast<half2v*>(&Ys[row * YLD + c0]) =
-            half2v{(_Float16)(acc[i][0][r] + bj[0]), (_Float16)(acc[i][FN - 1][r] + bj[FN - 1])};
-      else
-        Ys[row * YLD + c0] = (_Float16)(acc[i][0][r] + bj[0]);
+  __syncthreads();  // every wave is done reading As (and the k-group exchange)
+  if (owner) {
+    float bj[FN];
+  #pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + (j == 0 ? c0 : c1);
+      bj[j] = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
     }
+  #pragma unroll
+    for (int i = 0; i < FM; ++i)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (FN == 2)
+          *reinterpret_cast<half2v*>(&Ys[row * YLD + c0]) =
+              half2v{(_Float16)(acc[i][0][r] + bj[0]), (_Float16)(acc[i][FN - 1][r] + bj[FN - 1])};
+        else
+          Ys[row * YLD + c0] = (_Float16)(acc[i][0][r] + bj[0]);
+      }
+  }
   __syncthreads();
   constexpr int PR = BN / 8;  // 16-byte pieces per row
 #pragma unroll
-  for (int q = tid; q < BM * PR; q += 256) {
+  for (int q = tid; q < BM * PR; q += THREADS) {
     const int row = q / PR, p = q % PR;
     const int grow = m0 + row, gcol = n0 + 8 * p;
     if (grow < M && gcol < N)
@@ -377,19 +419,19 @@ hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t*
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
                        const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream) {
   const bool split = p.splits > 1;
-  auto go = [&](auto kern, int bm, int bn) {
+  auto go = [&](auto kern, int bm, int bn, int threads) {
     const int m_tiles = (M + bm - 1) / bm;
     const int n_tiles = (N + bn - 1) / bn;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(256), 0,
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(threads), 0,
                        stream, reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
                        reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles, p.kps,
                        split ? partial : nullptr, reinterpret_cast<_Float16*>(y));
   };
   switch (p.variant) {
-    case 0: go(tile_kernel<4, 2, 2, 1>, 256, 128); break;
-    case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64); break;
-    default: go(tile_kernel<2, 1, 1, 1>, 64, 128); break;
+    case 0: go(tile_kernel<4, 2, 2, TILE0_KG>, 256, 128, 256 * TILE0_KG); break;
+    case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64, 256); break;
+    default: go(tile_kernel<2, 1, 1, 1>, 64, 128, 256); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
