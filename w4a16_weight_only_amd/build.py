@@ -67,6 +67,10 @@ def build(verbose: bool = False) -> str:
     tmp = PROBE_PATH + ".tmp"
     _run([cc, *COMPILE_FLAGS, "-shared", os.path.join(CSRC, "probe", "stream_read.hip"), "-o", tmp])
     os.replace(tmp, PROBE_PATH)
+    # Resolve every symbol now (a kernel whose host stub was not emitted shows up here).
+    import ctypes
+    for path in (LIB_PATH, PROBE_PATH):
+        ctypes.CDLL(path, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     return LIB_PATH
 
 

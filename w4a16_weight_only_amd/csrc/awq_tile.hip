@@ -49,7 +49,12 @@ namespace awq {
 namespace {
 
 constexpr int kBK = 64;            // k-tile of the x staging
-constexpr int kALd = kBK + 8;      // padded LDS row (halves): 144 B, conflict-free fragment reads
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's data lands at lds + 16 l; lds must be the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 
 // ORDER[p]: column within a packed word held by nibble p.
 __device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 1 : 2 * p; }
@@ -73,15 +78,21 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // then the BN fp16 scales, in 16-byte pieces.
   constexpr int ZP = BW / 4, SP = BN / 8, GP = ZP + SP;  // pieces: zeros, scales, per half
   constexpr int ACC = FM * FN * 16;   // accumulator registers per lane
+  constexpr int YLD = BN + 16;        // staged output row (halves); rows 4 apart in opposite bank halves
   struct Staging {
-    _Float16 As[2][BM][kALd];
+    // x tile: rows of 64 halves (128 B); 16-byte chunk c of row r sits at position
+    // c ^ (r % 8), so that the 8 rows a fragment read touches at once hit 8 distinct
+    // bank groups, and a direct-to-LDS load writes 8 whole rows (1 KB) per wave.
+    _Float16 As[2][BM * kBK];
     uint32_t Bs[2][BW][kBLd];
     u32x4 Gs[2][2 * GP + 1];  // + 1: sink of idle threads
   };
-  // After the k loop the same LDS holds the second k-group's accumulators (KG = 2).
+  // After the k loop the same LDS holds the second k-group's accumulators (KG = 2),
+  // then the fp16 output tile.
   union Lds {
     Staging st;
     float red[KG == 2 ? 4 * ACC * 64 : 1];
+    _Float16 ys[BM * YLD];
   };
   __shared__ __attribute__((aligned(16))) Lds lds;
   auto& As = lds.st.As;
@@ -100,26 +111,30 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
 
-  // ---- Global -> register staging of one k-tile.  Every thread runs the same
-  // code (no divergent branches).  The x and qweight loads are a uniform base,
-  // advanced per k-tile in scalar registers, plus a per-lane 32-bit byte offset
-  // fixed for the whole kernel; out-of-range rows and columns are clamped into
-  // those offsets and never stored to y.  A partial last k-tile (K % 64 = 32) is
-  // loaded as the full k-tile ending at K, i.e. starting 32 rows early, and only
-  // its upper half is multiplied; when K = 32 (the only k-tile is partial) the
-  // lanes of the upper half re-read the lower half instead.
-  constexpr int A_PIECES = BM * kBK * 2 / 16 / THREADS;  // 16-byte pieces of x per thread
-  constexpr int A_ROWS = THREADS / 8;                     // rows covered by one piece index
-  const int a_chunk = tid & 7;
-  const int a_ch = K < kBK ? (a_chunk & 3) : a_chunk;
+  // ---- Staging of one k-tile.  Every thread runs the same code (no divergent
+  // branches).  Loads are a uniform base, advanced per k-tile, plus a per-lane 32-bit
+  // byte offset fixed for the whole kernel; out-of-range rows and columns are clamped
+  // into those offsets and never stored to y.  A partial last k-tile (K % 64 = 32) is
+  // loaded as the full k-tile ending at K, i.e. starting 32 rows early, and only its
+  // upper half is multiplied; when K = 32 (the only k-tile is partial) the lanes of the
+  // upper half re-read the lower half instead.
+  // x goes straight from global memory to LDS (global_load_lds_dwordx4): each wave
+  // instruction fills 8 rows; lane l writes position l % 8 of row l / 8 and so fetches
+  // chunk (l % 8) ^ (l / 8).
+  constexpr int A_GROUPS = BM / 8;              // 8-row groups of the x tile
+  constexpr int IPW = A_GROUPS / (4 * KG);      // direct loads per wave per k-tile
+  static_assert(IPW >= 1 && A_GROUPS % (4 * KG) == 0, "x tile must split evenly over the waves");
+  const int lrow = lane >> 3;
+  const int lch = (lane & 7) ^ lrow;
+  const int a_ch = K < kBK ? (lch & 3) : lch;
   const char* xb = reinterpret_cast<const char*>(x);
-  int a_row0[A_PIECES];         // uniform first row of piece i (clamped)
-  uint32_t a_off[A_PIECES];     // lane's byte offset from that row
+  int a_row0[IPW];              // wave-uniform first row of each 8-row group (clamped)
+  uint32_t a_off[IPW];          // lane's byte offset from that row
 #pragma unroll
-  for (int i = 0; i < A_PIECES; ++i) {
-    a_row0[i] = min(m0 + A_ROWS * i, M - 1);
-    const int t = min(tid >> 3, M - 1 - a_row0[i]);
-    a_off[i] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
+  for (int j = 0; j < IPW; ++j) {
+    a_row0[j] = min(m0 + 8 * (wave * IPW + j), M - 1);
+    const int t = min(lrow, M - 1 - a_row0[j]);
+    a_off[j] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
   }
   // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns; with
   // fewer pieces than threads the rest duplicate them.
@@ -135,19 +150,21 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int g_u = tid - g_half * GP;                     // piece within the half
   const int g_slot = min(tid, 2 * GP);
   struct Stage {
-    u32x4 a[A_PIECES];
     u32x4 b;
     u32x4 gd;
   };
   // First row loaded for the k-tile starting at k0 (see above).
   auto tile_row = [&](int k0) { return (K - k0 < kBK && K >= kBK) ? k0 - kBK / 2 : k0; };
-  auto stage_load = [&](Stage& st, int k0) {
+  auto load_x = [&](int buf, int k0) {
     const int kl = tile_row(k0);
 #pragma unroll
-    for (int i = 0; i < A_PIECES; ++i) {
-      const char* base = xb + ((int64_t)a_row0[i] * K + kl) * 2;
-      st.a[i] = *reinterpret_cast<const u32x4*>(base + a_off[i]);
+    for (int j = 0; j < IPW; ++j) {
+      const char* src = xb + ((int64_t)a_row0[j] * K + kl) * 2 + a_off[j];
+      load_lds16(src, &As[buf][(wave * IPW + j) * 8 * kBK]);
     }
+  };
+  auto stage_load = [&](Stage& st, int k0) {
+    const int kl = tile_row(k0);
     st.b = *reinterpret_cast<const u32x4*>(wb + (int64_t)kl * NW * 4 + b_off);
     // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
     // inside the k-tile can only fall between the halves.
@@ -163,9 +180,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     st.gd = *reinterpret_cast<const u32x4*>(base + byte_off);
   };
   auto stage_store = [&](const Stage& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PIECES; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + A_ROWS * i][8 * a_chunk]) = st.a[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
     Gs[buf][g_slot] = st.gd;
@@ -220,13 +234,15 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     u32x4 wlo, whi;
   };
   // kh: this wave's first 32-row half of the k-tile (0, or 1 for the second k-group).
+  const int rx = lc & 7;  // row % 8 of every x row this lane reads
   auto read_frag = [&](Frag& f, int buf, int s, int kh) {
     const int k = 16 * s + 32 * kh + kq;
     f.wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k]);
     f.whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k + 4]);
+    const int pos = (k >> 3) ^ rx;  // swizzled 16-byte position of chunk k / 8
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][wm * 32 * FM + 32 * i + lc][k]);
+      f.a[i] = *reinterpret_cast<const half8v*>(&As[buf][(wm * 32 * FM + 32 * i + lc) * kBK + 8 * pos]);
   };
   // With one wave per SIMD (KG = 1) the fragments of step s + 1 are read while step s
   // is multiplied; with two (KG = 2) the other wave covers that latency and the
@@ -286,16 +302,17 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int KT = min(KT_all, kt0 + kps) - kt0;
   auto kofs = [&](int t) { return (kt0 + min(t, KT - 1)) * kBK; };
   Stage st;
+  load_x(0, kofs(0));
   stage_load(st, kofs(0));
   stage_store(st, 0);
-  stage_load(st, kofs(1));
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
+    load_x(buf ^ 1, kofs(kt + 1));
+    stage_load(st, kofs(kt + 1));
     run(buf, kt0 + kt == KT_all - 1 && K % kBK != 0);
     stage_store(st, buf ^ 1);
-    stage_load(st, kofs(kt + 2));
-    __syncthreads();
+    __syncthreads();  // also waits for this iteration's direct loads
   }
 
   // Two k-groups: group 1 hands its sums to group 0 through LDS (register order,
@@ -349,9 +366,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   }
   // The fp16 tile (bias added in fp32) is staged in LDS over the x buffers, then
   // written as whole 16-byte pieces of rows.
-  constexpr int YLD = BN + 16;  // staged row (halves); rows 4 apart fall in opposite bank halves
-  static_assert(BM * YLD <= 2 * BM * kALd, "staged output must fit in the x buffers");
-  _Float16* Ys = &As[0][0][0];
+  _Float16* Ys = lds.ys;
   __syncthreads();  // every wave is done reading As (and the k-group exchange)
   if (owner) {
     float bj[FN];
