@@ -49,11 +49,17 @@ namespace awq {
 namespace {
 
 constexpr int kBK = 64;            // k-tile of the x staging
+constexpr int kStages = 3;         // LDS buffers of the k loop
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane l's data lands at lds + 16 l; lds must be the same for the whole wave.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+// lane l's data lands at lds + 16 l; lds must be the same for the whole wave.  Issued
+// as inline assembly, so the compiler does not track these loads: the kernel waits for
+// them itself (vmcnt) before anyone reads what they wrote.  M0 takes the LDS byte
+// address (the low 32 bits of the generic address of a __shared__ object).
+__device__ __forceinline__ void load_lds16(const void* src, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
 }
 
 // ORDER[p]: column within a packed word held by nibble p.
@@ -73,35 +79,40 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   constexpr int BN = WN * 32 * FN;    // workgroup columns
   constexpr int BW = BN / 8;          // packed word columns per workgroup (16 or 8)
   constexpr int WW = 32 * FN / 8;     // packed word columns per wave (8 or 4)
-  constexpr int kBLd = kBK + 4;       // words per staged word column (padded)
   // Group data of one k-tile, per 32-row half: the zero words of the BW word columns
   // then the BN fp16 scales, in 16-byte pieces.
   constexpr int ZP = BW / 4, SP = BN / 8, GP = ZP + SP;  // pieces: zeros, scales, per half
   constexpr int ACC = FM * FN * 16;   // accumulator registers per lane
   constexpr int YLD = BN + 16;        // staged output row (halves); rows 4 apart in opposite bank halves
+  // x tile: rows of 64 halves (128 B); 16-byte chunk c of row r sits at position
+  // c ^ (r % 8), so that the 8 rows a fragment read touches at once hit 8 distinct
+  // bank groups, and a direct-to-LDS load writes 8 whole rows (1 KB) per wave.  It is
+  // its own LDS object: the compiler then knows that the register-staged stores below
+  // cannot overlap the direct loads still in flight, and does not wait for them.
+  // After the k loop it holds the second k-group's sums (KG = 2), then the fp16
+  // output tile.
+  __shared__ __attribute__((aligned(16))) _Float16 As[kStages][BM * kBK];
+  // Packed weights of a k-tile: 64 rows of BW words, row-major as stored, in groups
+  // of 4 words (16 bytes) XOR-swizzled by bit 3 of the row, so that the rows r and
+  // r + 8 a 32-bit fragment read touches at once fall in different banks.  Group data:
+  // 64 slots of 16 bytes, of which 2 GP are used.  sink: target of the padding loads
+  // that keep every wave's count of direct loads equal.
+  constexpr int NG = BW / 4;          // 16-byte groups per weight row
   struct Staging {
-    // x tile: rows of 64 halves (128 B); 16-byte chunk c of row r sits at position
-    // c ^ (r % 8), so that the 8 rows a fragment read touches at once hit 8 distinct
-    // bank groups, and a direct-to-LDS load writes 8 whole rows (1 KB) per wave.
-    _Float16 As[2][BM * kBK];
-    uint32_t Bs[2][BW][kBLd];
-    u32x4 Gs[2][2 * GP + 1];  // + 1: sink of idle threads
+    uint32_t Bs[kStages][kBK * BW];
+    u32x4 Gs[kStages][64];
+    u32x4 sink[64];
   };
-  // After the k loop the same LDS holds the second k-group's accumulators (KG = 2),
-  // then the fp16 output tile.
-  union Lds {
-    Staging st;
-    float red[KG == 2 ? 4 * ACC * 64 : 1];
-    _Float16 ys[BM * YLD];
-  };
-  __shared__ __attribute__((aligned(16))) Lds lds;
-  auto& As = lds.st.As;
-  auto& Bs = lds.st.Bs;
-  auto& Gs = lds.st.Gs;
+  __shared__ __attribute__((aligned(16))) Staging stg;
+  auto& Bs = stg.Bs;
+  auto& Gs = stg.Gs;
+  static_assert(2 * GP <= 64, "group data must fit one wave load");
+  static_assert(BM * YLD <= kStages * BM * kBK, "staged output tile must fit in the x buffers");
+  static_assert(KG == 1 || 4 * (ACC / 2) * 64 * 4 <= kStages * BM * kBK * 2, "half of the k-group exchange must fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int kg = wave >> 2;           // k-group
   const int w4 = wave & 3;            // wave within the group
   const int wm = w4 / WN, wn = w4 % WN;
@@ -136,53 +147,58 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const int t = min(lrow, M - 1 - a_row0[j]);
     a_off[j] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
   }
-  // qweight: BW word columns x 64 rows as 16-byte pieces of 4 word columns; with
-  // fewer pieces than threads the rest duplicate them.
-  constexpr int B_PIECES = BW * kBK / 4;                 // 256 (BW 16) or 128 (BW 8)
-  static_assert(B_PIECES <= THREADS, "one qweight piece per thread at most");
-  const int b_id = tid % B_PIECES;
-  const int b_row = b_id / (BW / 4), b_wc = (b_id % (BW / 4)) * 4;
-  const uint32_t b_off =
-      ((uint32_t)(K < kBK ? (b_row & 31) : b_row) * (uint32_t)NW + (uint32_t)min(wc0 + b_wc, NW - 4)) * 4u;
+  // Packed weights and group data also go straight to LDS: NB wave loads of 16 rows
+  // (BW = 16) or 32 rows (BW = 8) for the weights, one for the group data, spread over
+  // the waves; waves with fewer real loads issue padding loads into sink, so that every
+  // wave issues IPW + XPW direct loads per k-tile (the barrier counts them).
+  constexpr int RPI = 256 / BW;                // weight rows per wave load
+  constexpr int NB = kBK / RPI;                // weight loads per k-tile
+  constexpr int NWAVES = 4 * KG;
+  constexpr int XPW = (NB + 1 + NWAVES - 1) / NWAVES;  // extra loads per wave
+  constexpr int DPW = IPW + XPW;               // direct loads per wave per k-tile
   const char* wb = reinterpret_cast<const char*>(qweight);
-  // group data: thread t < 2 GP loads piece t % GP of half t / GP.
-  const int g_half = tid < GP ? 0 : 1;
-  const int g_u = tid - g_half * GP;                     // piece within the half
-  const int g_slot = min(tid, 2 * GP);
-  struct Stage {
-    u32x4 b;
-    u32x4 gd;
-  };
+  const char* sb = reinterpret_cast<const char*>(scales);
+  const int64_t to_z = reinterpret_cast<const char*>(qzeros) - sb;
+  // Weight load: lane l covers row l / NG of the load's RPI rows and position l % NG,
+  // which holds word group (l % NG) ^ swz(row).
+  auto swz = [](int r) { return ((r >> 3) & 1) * (NG / 2); };
+  const int b_rl = lane / NG;
+  // Group data: lane l < 2 GP loads piece l % GP of half l / GP (others repeat piece 0).
+  const int g_lane = lane < 2 * GP ? lane : 0;
+  const int g_half = g_lane < GP ? 0 : 1;
+  const int g_u = g_lane - g_half * GP;
   // First row loaded for the k-tile starting at k0 (see above).
   auto tile_row = [&](int k0) { return (K - k0 < kBK && K >= kBK) ? k0 - kBK / 2 : k0; };
-  auto load_x = [&](int buf, int k0) {
+  auto load_tile = [&](int buf, int k0) {
     const int kl = tile_row(k0);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const char* src = xb + ((int64_t)a_row0[j] * K + kl) * 2 + a_off[j];
       load_lds16(src, &As[buf][(wave * IPW + j) * 8 * kBK]);
     }
-  };
-  auto stage_load = [&](Stage& st, int k0) {
-    const int kl = tile_row(k0);
-    st.b = *reinterpret_cast<const u32x4*>(wb + (int64_t)kl * NW * 4 + b_off);
-    // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
-    // inside the k-tile can only fall between the halves.
-    const int gi = min(kl + g_half * (kBK / 2), K - 1) / g;
-    // Blended operands (z = 0 / 1) rather than selected pointers, so that the
-    // compiler makes no branch of it.
-    const int64_t z = g_u < ZP;
-    const int64_t zcol = min(wc0 + 4 * g_u, NW - 4), scol = min(n0 + 8 * (g_u - ZP), N - 8);
-    const int64_t zrow = (int64_t)gi * NW, srow = (int64_t)gi * N;
-    const int64_t byte_off = ((srow + scol) << 1) + z * (((zrow + zcol) << 2) - ((srow + scol) << 1));
-    const int64_t base = reinterpret_cast<int64_t>(scales) +
-                         z * (reinterpret_cast<int64_t>(qzeros) - reinterpret_cast<int64_t>(scales));
-    st.gd = *reinterpret_cast<const u32x4*>(base + byte_off);
-  };
-  auto stage_store = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Bs[buf][b_wc + j][b_row] = st.b[j];
-    Gs[buf][g_slot] = st.gd;
+    for (int xs = 0; xs < XPW; ++xs) {
+      const int e = wave + NWAVES * xs;  // wave-uniform: which extra load this is
+      if (e < NB) {
+        const int row = e * RPI + b_rl;                 // row within the k-tile
+        const int grp = (lane % NG) ^ swz(row);
+        const int r = K < kBK ? (row & 31) : row;       // K = 32: re-read the real half
+        const char* src = wb + ((int64_t)(kl + r) * NW + min(wc0 + 4 * grp, NW - 4)) * 4;
+        load_lds16(src, &Bs[buf][e * RPI * BW]);
+      } else if (e == NB) {
+        // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
+        // inside the k-tile can only fall between the halves.
+        const int gi = min(kl + g_half * (kBK / 2), K - 1) / g;
+        // Blended operands (z = 0 / 1) rather than selected pointers; offsets from the
+        // scales pointer keep the address a global one.
+        const int64_t z = g_u < ZP;
+        const int64_t zcol = min(wc0 + 4 * g_u, NW - 4), scol = min(n0 + 8 * (g_u - ZP), N - 8);
+        const int64_t zoff = ((int64_t)gi * NW + zcol) << 2, soff = ((int64_t)gi * N + scol) << 1;
+        load_lds16(sb + (soff + z * (zoff + to_z - soff)), &Gs[buf][0]);
+      } else {
+        load_lds16(xb + ((int64_t)a_row0[0] * K + kl) * 2 + a_off[0], &stg.sink[0]);
+      }
+    }
   };
 
   // ---- This lane's column(s) of the B operand.
@@ -237,8 +253,13 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int rx = lc & 7;  // row % 8 of every x row this lane reads
   auto read_frag = [&](Frag& f, int buf, int s, int kh) {
     const int k = 16 * s + 32 * kh + kq;
-    f.wlo = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k]);
-    f.whi = *reinterpret_cast<const u32x4*>(&Bs[buf][wloc][k + 4]);
+    // Word wloc of rows k..k+7; swz(row) is the same for all 8 (k % 8 == 0).
+    const uint32_t* brow = &Bs[buf][k * BW + (((wloc >> 2) ^ swz(k)) << 2) + (wloc & 3)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.wlo[j] = brow[j * BW];
+      f.whi[j] = brow[(4 + j) * BW];
+    }
     const int pos = (k >> 3) ^ rx;  // swizzled 16-byte position of chunk k / 8
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -290,52 +311,67 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (!part || kh == part_half) compute(C0{}, C2{}, buf, kh);
   };
 
-  // One register staging set and two LDS buffers: k-tile t is multiplied from
-  // buffer t % 2 while k-tile t + 1 waits in registers; then t + 1 goes to the other
-  // buffer and the loads of t + 2 are issued, so each load has one k-tile of work to
-  // arrive.  Loads past the last k-tile re-read it (clamped) and their stores land in
-  // a buffer no one reads again, so the loop body has no data-dependent branches.
-  // This workgroup's k-tiles: [kt0, kt0 + KT) of the layer's; the layer's last k-tile
-  // is partial when K % 64 = 32.
+  // Three LDS buffers.  While k-tile t is multiplied from buffer t % 3, everything
+  // k-tile t + 2 needs streams straight into buffer (t + 2) % 3; the barrier at the end
+  // of a k-tile waits only for the direct loads of k-tile t + 1 (vmcnt may still count
+  // the DPW loads of t + 2, issued last), so each load has two k-tiles of work to
+  // arrive.  Loads past the last k-tile re-read it (clamped) into a buffer no one reads
+  // again, so the loop body has no data-dependent branches.  This workgroup's k-tiles:
+  // [kt0, kt0 + KT) of the layer's; the layer's last k-tile is partial when K % 64 = 32.
   const int KT_all = (K + kBK - 1) / kBK;
   const int kt0 = blockIdx.y * kps;
   const int KT = min(KT_all, kt0 + kps) - kt0;
   auto kofs = [&](int t) { return (kt0 + min(t, KT - 1)) * kBK; };
-  Stage st;
-  load_x(0, kofs(0));
-  stage_load(st, kofs(0));
-  stage_store(st, 0);
-  __syncthreads();
+  // LDS reads done and all but the last DPW vector-memory operations (the direct
+  // loads of k-tile t + 2) complete, then the workgroup barrier.
+  auto barrier_keep_last = [] { asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DPW) : "memory"); };
+  load_tile(0, kofs(0));
+  load_tile(1, kofs(1));
+  barrier_keep_last();
+  int b0 = 0, b1 = 1, b2 = 2;  // buffers of k-tiles t, t + 1, t + 2
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    load_x(buf ^ 1, kofs(kt + 1));
-    stage_load(st, kofs(kt + 1));
-    run(buf, kt0 + kt == KT_all - 1 && K % kBK != 0);
-    stage_store(st, buf ^ 1);
-    __syncthreads();  // also waits for this iteration's direct loads
+    load_tile(b2, kofs(kt + 2));
+    run(b0, kt0 + kt == KT_all - 1 && K % kBK != 0);
+    barrier_keep_last();
+    const int bt = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = bt;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped extra loads have landed too
+  __syncthreads();  // every wave is done with the buffers
 
   // Two k-groups: group 1 hands its sums to group 0 through LDS (register order,
   // conflict-free), group 0 adds them and finishes the tile.
   if constexpr (KG == 2) {
-    __syncthreads();  // the staging buffers are dead
-    float* red = lds.red + w4 * ACC * 64 + lane;
-    if (kg == 1) {
+    // In two rounds of half the accumulators each (the x buffers hold one half).
+    float* red = reinterpret_cast<float*>(&As[0][0]) + w4 * (ACC / 2) * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int round = 0; round < 2; ++round) {
+      if (kg == 1) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
-    }
-    __syncthreads();
-    if (kg == 0) {
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+            for (int r = 0; r < 16; ++r) {
+              const int v = (i * FN + j) * 16 + r;
+              if (v / (ACC / 2) == round) red[(v % (ACC / 2)) * 64] = acc[i][j][r];
+            }
+      }
+      __syncthreads();
+      if (kg == 0) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int v = (i * FN + j) * 16 + r;
+              if (v / (ACC / 2) == round) acc[i][j][r] += red[(v % (ACC / 2)) * 64];
+            }
+      }
+      __syncthreads();
     }
   }
   const bool owner = KG == 1 || kg == 0;  // holds finished sums
@@ -366,7 +402,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   }
   // The fp16 tile (bias added in fp32) is staged in LDS over the x buffers, then
   // written as whole 16-byte pieces of rows.
-  _Float16* Ys = lds.ys;
+  _Float16* Ys = &As[0][0];
   __syncthreads();  // every wave is done reading As (and the k-group exchange)
   if (owner) {
     float bj[FN];
