@@ -63,6 +63,10 @@ int device_cus() {
   return cus;
 }
 
+#ifndef AWQ_SKINNY_MAX_M
+#define AWQ_SKINNY_MAX_M awq::kSkinnyMaxM  // largest M planned on the skinny family
+#endif
+
 #ifndef AWQ_SKINNY_WG_PER_2CU
 #define AWQ_SKINNY_WG_PER_2CU 4  // 4-wave workgroups per two compute units
 #endif
@@ -117,7 +121,7 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
 
 Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
   Plan p;
-  if (M <= awq::kSkinnyMaxM && plan_skinny(M, K, N, g, cus, p.sk)) {
+  if (M <= AWQ_SKINNY_MAX_M && plan_skinny(M, K, N, g, cus, p.sk)) {
     p.family = 0;
     p.grid_x = p.sk.n_tiles;
     p.grid_y = p.sk.splits;

@@ -49,7 +49,10 @@ namespace awq {
 namespace {
 
 constexpr int kBK = 64;            // k-tile of the x staging
-constexpr int kStages = 3;         // LDS buffers of the k loop
+#ifndef TILE_STAGES
+#define TILE_STAGES 4
+#endif
+constexpr int kStages = TILE_STAGES;  // LDS buffers of the k loop
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l's data lands at lds + 16 l; lds must be the same for the whole wave.  Issued
@@ -311,32 +314,29 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (!part || kh == part_half) compute(C0{}, C2{}, buf, kh);
   };
 
-  // Three LDS buffers.  While k-tile t is multiplied from buffer t % 3, everything
-  // k-tile t + 2 needs streams straight into buffer (t + 2) % 3; the barrier at the end
-  // of a k-tile waits only for the direct loads of k-tile t + 1 (vmcnt may still count
-  // the DPW loads of t + 2, issued last), so each load has two k-tiles of work to
-  // arrive.  Loads past the last k-tile re-read it (clamped) into a buffer no one reads
+  // kStages LDS buffers.  While k-tile t is multiplied from buffer t % kStages,
+  // everything k-tile t + kStages - 1 needs streams straight into its buffer; the
+  // barrier at the end of a k-tile waits only for the direct loads of k-tile t + 1
+  // (vmcnt may still count the DPW loads of each later k-tile, issued last), so each
+  // load has kStages - 1 k-tiles of work to arrive.  Loads past the last k-tile re-read it (clamped) into a buffer no one reads
   // again, so the loop body has no data-dependent branches.  This workgroup's k-tiles:
   // [kt0, kt0 + KT) of the layer's; the layer's last k-tile is partial when K % 64 = 32.
   const int KT_all = (K + kBK - 1) / kBK;
   const int kt0 = blockIdx.y * kps;
   const int KT = min(KT_all, kt0 + kps) - kt0;
   auto kofs = [&](int t) { return (kt0 + min(t, KT - 1)) * kBK; };
-  // LDS reads done and all but the last DPW vector-memory operations (the direct
-  // loads of k-tile t + 2) complete, then the workgroup barrier.
-  auto barrier_keep_last = [] { asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DPW) : "memory"); };
-  load_tile(0, kofs(0));
-  load_tile(1, kofs(1));
+  // LDS reads done and all but the last (kStages - 2) DPW vector-memory operations
+  // (the direct loads of k-tiles t + 2 ...) complete, then the workgroup barrier.
+  auto barrier_keep_last = [] {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kStages - 2) * DPW) : "memory");
+  };
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) load_tile(t, kofs(t));
   barrier_keep_last();
-  int b0 = 0, b1 = 1, b2 = 2;  // buffers of k-tiles t, t + 1, t + 2
   for (int kt = 0; kt < KT; ++kt) {
-    load_tile(b2, kofs(kt + 2));
-    run(b0, kt0 + kt == KT_all - 1 && K % kBK != 0);
+    load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
+    run(kt % kStages, kt0 + kt == KT_all - 1 && K % kBK != 0);
     barrier_keep_last();
-    const int bt = b0;
-    b0 = b1;
-    b1 = b2;
-    b2 = bt;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped extra loads have landed too
   __syncthreads();  // every wave is done with the buffers
