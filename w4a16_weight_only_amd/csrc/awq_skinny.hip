@@ -382,23 +382,34 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 }
 
 // Sums the fp32 partials of the 8-wave skinny kernel in split order, adds bias,
-// rounds once to fp16.  One thread per (tile, entry); entry 4 * slot + i is row
-// 4 (slot / 256) + i of the slot's column.
+// rounds once to fp16.  One workgroup per (tile, group of 4 rows): thread t reads the
+// 4 rows of slot 256 q + t (16 contiguous bytes per split), and the rounded values
+// meet in LDS in output order so that y is written as whole 16-byte row pieces.
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             const _Float16* __restrict__ bias, int M, int N,
                                                             int splits, _Float16* __restrict__ y) {
   constexpr int TILE_ENTRIES = 16 * kSkinnyCols;
-  const int tile = blockIdx.x / (TILE_ENTRIES / 256);
-  const int e = (blockIdx.x % (TILE_ENTRIES / 256)) * 256 + threadIdx.x;
-  const int s = e >> 2, i = e & 3;
-  const int row = 4 * (s >> 8) + i;
-  const int sv = (s >> 4) & 15, sc = s & 15;
-  const int n = tile * kSkinnyCols + 8 * (2 * sc + (sv >> 3)) + tab_col(sv);
-  if (row >= M || n >= N) return;
-  const float* p = partial + (int64_t)tile * splits * TILE_ENTRIES + e;
-  float acc = 0.f;
-  for (int sp = 0; sp < splits; ++sp) acc += p[(int64_t)sp * TILE_ENTRIES];
-  y[(int64_t)row * N + n] = (_Float16)(acc + (bias ? (float)bias[n] : 0.f));
+  __shared__ __attribute__((aligned(16))) _Float16 ys[4][kSkinnyCols + 8];
+  const int tile = blockIdx.x / 4, q = blockIdx.x % 4;
+  if (4 * q >= M) return;  // whole workgroup: rows beyond M
+  const int t = threadIdx.x;
+  const int slot = q * 256 + t;
+  const float* p = partial + (int64_t)tile * splits * TILE_ENTRIES + 4 * slot;
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  for (int sp = 1; sp < splits; ++sp) a += *reinterpret_cast<const floatx4*>(p + (int64_t)sp * TILE_ENTRIES);
+  const int sv = (t >> 4) & 15, sc = t & 15;
+  const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
+  const int n = tile * kSkinnyCols + ct;
+  const float b = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ys[i][ct] = (_Float16)(a[i] + b);
+  __syncthreads();
+  if (t < 4 * (kSkinnyCols / 8)) {
+    const int i = t / (kSkinnyCols / 8), pc = t % (kSkinnyCols / 8);
+    const int row = 4 * q + i, n0 = tile * kSkinnyCols + 8 * pc;
+    if (row < M && n0 < N)
+      *reinterpret_cast<half8v*>(y + (int64_t)row * N + n0) = *reinterpret_cast<const half8v*>(&ys[i][8 * pc]);
+  }
 }
 
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
@@ -422,7 +433,7 @@ hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_
     if (p.splits > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(p.n_tiles * 16), dim3(256), 0, stream,
+      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(p.n_tiles * 4), dim3(256), 0, stream,
                          partial, reinterpret_cast<const _Float16*>(bias), M, N,
                          p.splits, reinterpret_cast<_Float16*>(y));
     }
