@@ -236,3 +236,30 @@ def test_bad_arguments_raise_before_launch():
         awq.awq_gemm(t["x"].float(), t["qweight"], t["qzeros"], t["scales"], t["bias"], 64)
     with pytest.raises(ValueError):
         awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"][:100].contiguous(), 64)
+
+
+@pytest.mark.parametrize("M,K,N,g", [(1, 4096, 4096, 128), (16, 4096, 2048, 128), (64, 4096, 1024, 64),
+                                     (300, 2048, 1024, -1)])
+def test_graph_replays_match_eager(M, K, N, g):
+    """awq_gemm captured in a HIP graph (after an eager call has sized the workspace)
+    and replayed several times, with eager calls of other shapes in between: every
+    replay equals the eager result bit for bit (the split-K accumulators are left zero
+    by each call, partial buffers are fully rewritten)."""
+    d = synth.make_custom(M, K, N, g, seed=11)
+    t = dev(d)
+    other = dev(synth.make_custom(3, 2048, 512, 64, seed=12))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g).clone()
+        y = torch.empty_like(eager)
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g, out=y)
+    for rep in range(3):
+        y.zero_()
+        with torch.cuda.stream(s):
+            graph.replay()
+            awq.awq_gemm(other["x"], other["qweight"], other["qzeros"], other["scales"], other["bias"], 64)
+        s.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
