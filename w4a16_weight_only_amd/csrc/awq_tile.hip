@@ -88,8 +88,10 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   constexpr int ACC = FM * FN * 16;   // accumulator registers per lane
   constexpr int YLD = BN + 16;        // staged output row (halves); rows 4 apart in opposite bank halves
   // x tile: rows of 64 halves (128 B); 16-byte chunk c of row r sits at position
-  // c ^ (r % 8), so that the 8 rows a fragment read touches at once hit 8 distinct
-  // bank groups, and a direct-to-LDS load writes 8 whole rows (1 KB) per wave.  It is
+  // c ^ ((r / 2) % 8).  A 16-byte fragment read serves 16 lanes (16 consecutive rows)
+  // per pass from the 64 banks (256 B): rows of one parity share a bank half, and the
+  // swizzle gives the 8 rows of each parity 8 distinct positions, so the pass is
+  // conflict-free; a direct-to-LDS load still writes 8 whole rows (1 KB) per wave.  It is
   // its own LDS object: the compiler then knows that the register-staged stores below
   // cannot overlap the direct loads still in flight, and does not wait for them.
   // After the k loop it holds the second k-group's sums (KG = 2), then the fp16
@@ -133,20 +135,21 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // upper half is multiplied; when K = 32 (the only k-tile is partial) the lanes of the
   // upper half re-read the lower half instead.
   // x goes straight from global memory to LDS (global_load_lds_dwordx4): each wave
-  // instruction fills 8 rows; lane l writes position l % 8 of row l / 8 and so fetches
-  // chunk (l % 8) ^ (l / 8).
+  // instruction fills 8 rows; lane l writes position l % 8 of row r = l / 8 (of the
+  // group) and so fetches chunk (l % 8) ^ ((r / 2) % 8).
   constexpr int A_GROUPS = BM / 8;              // 8-row groups of the x tile
   constexpr int IPW = A_GROUPS / (4 * KG);      // direct loads per wave per k-tile
   static_assert(IPW >= 1 && A_GROUPS % (4 * KG) == 0, "x tile must split evenly over the waves");
   const int lrow = lane >> 3;
-  const int lch = (lane & 7) ^ lrow;
-  const int a_ch = K < kBK ? (lch & 3) : lch;
   const char* xb = reinterpret_cast<const char*>(x);
   int a_row0[IPW];              // wave-uniform first row of each 8-row group (clamped)
   uint32_t a_off[IPW];          // lane's byte offset from that row
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    a_row0[j] = min(m0 + 8 * (wave * IPW + j), M - 1);
+    const int grp = wave * IPW + j;
+    const int lch = (lane & 7) ^ (((8 * grp + lrow) >> 1) & 7);
+    const int a_ch = K < kBK ? (lch & 3) : lch;
+    a_row0[j] = min(m0 + 8 * grp, M - 1);
     const int t = min(lrow, M - 1 - a_row0[j]);
     a_off[j] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
   }
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     u32x4 wlo, whi;
   };
   // kh: this wave's first 32-row half of the k-tile (0, or 1 for the second k-group).
-  const int rx = lc & 7;  // row % 8 of every x row this lane reads
+  const int rx = (lc >> 1) & 7;  // (row / 2) % 8 of every x row this lane reads
   auto read_frag = [&](Frag& f, int buf, int s, int kh) {
     const int k = 16 * s + 32 * kh + kq;
     // Word wloc of rows k..k+7; swz(row) is the same for all 8 (k % 8 == 0).
