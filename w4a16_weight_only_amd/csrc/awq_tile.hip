@@ -227,15 +227,18 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const _Float16 zbase = hi_nib ? (_Float16)64.f : (_Float16)1024.f;
 
   half2v off0, off1, sc0, sc1;
-  auto apply_group = [&](int buf, int h) {
+  // Group data of half h of k-tile buf.  keep = false zeroes the scales: the half then
+  // contributes x . 0 = 0 (for finite x), which is how the unused half of a partial
+  // last k-tile is skipped without a branch around the multiply.
+  auto apply_group = [&](int buf, int h, bool keep) {
     const uint32_t* gz = reinterpret_cast<const uint32_t*>(&Gs[buf][h * GP]);
     const _Float16* gs = reinterpret_cast<const _Float16*>(&Gs[buf][h * GP + ZP]);
     const uint32_t zw = gz[wloc];
     off0 = splat(-(zbase + (_Float16)(float)((zw >> (4 * p0)) & 0xFu)));
-    sc0 = splat(gs[c0]);
+    sc0 = splat(keep ? gs[c0] : (_Float16)0.f);
     if (FN == 2) {
       off1 = splat(-(zbase + (_Float16)(float)((zw >> (4 * (p0 + 4))) & 0xFu)));
-      sc1 = splat(gs[c1]);
+      sc1 = splat(keep ? gs[c1] : (_Float16)0.f);
     }
   };
 
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // is multiplied; with two (KG = 2) the other wave covers that latency and the
   // registers go to the second wave instead.
   constexpr bool kPrefetch = KG == 1;
-  auto compute = [&](auto s0_c, auto s1_c, int buf, int kh) {
+  auto compute = [&](auto s0_c, auto s1_c, int buf, int kh, bool keep) {
     constexpr int S0 = decltype(s0_c)::value, S1 = decltype(s1_c)::value;
     Frag fr[kPrefetch ? 2 : 1];
     if (kPrefetch) read_frag(fr[S0 & 1], buf, S0, kh);
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (!kPrefetch) read_frag(fr[0], buf, s, kh);
       const Frag& f = fr[kPrefetch ? (s & 1) : 0];
       if (kPrefetch && s + 1 < S1) read_frag(fr[(s + 1) & 1], buf, s + 1, kh);
-      if (s % 2 == 0) apply_group(buf, s / 2 + kh);
+      if (s % 2 == 0) apply_group(buf, s / 2 + kh, keep);
       const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
       half2v h0[4], h1[4];
 #pragma unroll
@@ -309,12 +312,11 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // This wave's share of k-tile buf: both 32-row halves (KG = 1) or the half of its
   // k-group (KG = 2: group kg takes half kg, with that half's group data).  A partial
   // last k-tile holds its 32 rows in the upper half (K >= 64) or the lower one
-  // (K = 32); only that half is multiplied.
+  // (K = 32); the other half is multiplied with zero scales.
   const int part_half = K >= kBK ? 1 : 0;
   auto run = [&](int buf, bool part) {
 #pragma unroll
-    for (int kh = (KG == 1 ? 0 : kg); kh < 2; kh += KG)
-      if (!part || kh == part_half) compute(C0{}, C2{}, buf, kh);
+    for (int kh = (KG == 1 ? 0 : kg); kh < 2; kh += KG) compute(C0{}, C2{}, buf, kh, !part || kh == part_half);
   };
 
   // kStages LDS buffers.  While k-tile t is multiplied from buffer t % kStages,
