@@ -98,6 +98,21 @@ int awq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scale
                 struct ihipStream_t* stream);
 
 /*
+ * Dequantise the packed weight to fp16:  out[k, n] = fp16((float)(q - z) * (float)s),
+ * the exact product of awq_dequant rounded once to nearest even.  This is the weight
+ * of the dequantize-then-dense-matmul path the pages use for large batches (vLLM
+ * article, section 5.3; GPTQModel wiki "AWQ", section "Native GEMM": above its row
+ * limit the native path dequantises and calls a dense matmul), provided so that a
+ * caller can run that path, or compare it with awq_gemm, on the same layout.
+ *   qweight, qzeros, scales_f16   device, layouts as above
+ *   out_f16                       device fp16 [K, N], written in full
+ * Returns AWQ_OK or an error status (nothing enqueued on error).
+ */
+int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                    int64_t K, int64_t N, int64_t group_size, void* out_f16,
+                    struct ihipStream_t* stream);
+
+/*
  * Fused linear y = x . dequant(W) + bias, accumulated in float32 and rounded once
  * to fp16 (round to nearest even) after the bias is added.
  * Source: GPU LLM serving-stack blog, section 1.2 (W4A16: packed weights are

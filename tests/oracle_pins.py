@@ -261,6 +261,25 @@ def pin_format_rules(o):
         raise AssertionError("pack accepted an invalid code matrix")
 
 
-ALL_PINS = [pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
+def pin_fp16_rounding(o):
+    """fp16_rne rounds once to the nearest binary16, ties to even, checked against
+    values built from their definition: the binary16 neighbours of 1 are 1 and
+    1 + 2^-10, so 1 + 2^-11 (a tie) goes to the even 1 and 1 + 3 * 2^-11 (a tie) to the
+    even 1 + 2^-9; 0.1 lies in [2^-4, 2^-3) where the step is 2^-14, and 0.1 / 2^-14 =
+    1638.4 rounds to 1638; exactly representable values, the signed zero and the largest
+    finite value pass unchanged; just above the halfway point to 2^16 overflows."""
+    from fractions import Fraction
+    cases = [(1 + 2.0 ** -11, 1.0), (1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9), (1 + 2.0 ** -11 + 2.0 ** -20, 1 + 2.0 ** -10),
+             (-(1 + 2.0 ** -11), -1.0), (0.1, float(Fraction(1638, 2 ** 14))), (65504.0, 65504.0),
+             (2.0 ** -24, 2.0 ** -24), (3 * 2.0 ** -26, 2.0 ** -24), (-0.0, -0.0)]
+    got = o.fp16_rne(np.array([c for c, _ in cases], dtype=np.float32))
+    for (c, want), g in zip(cases, got):
+        assert g.dtype == np.float16
+        assert float(g) == want and np.signbit(g) == np.signbit(want), (c, float(g), want)
+    with np.errstate(over="ignore"):
+        assert np.isinf(o.fp16_rne(np.float32(65520.0)))  # halfway to 2^16 rounds to even: overflow
+
+
+ALL_PINS = [pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
             pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
             pin_special_cases, pin_entries_agree, pin_format_rules]

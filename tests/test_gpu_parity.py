@@ -263,3 +263,25 @@ def test_graph_replays_match_eager(M, K, N, g):
             awq.awq_gemm(other["x"], other["qweight"], other["qzeros"], other["scales"], other["bias"], 64)
         s.synchronize()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("name", ["decode_m1_k4096_n4096_g128", "prefill_m2048_k4096_n4096_g128",
+                                  "down_proj_m64_k11008_n4096_g64", "down_proj_m64_k11008_n4096_g-1"])
+def test_dequant_f16_bit_exact(name):
+    """awq_dequant_f16 = the exact product rounded once to fp16, bit for bit."""
+    w = synth.WORKLOADS[name]
+    d = synth.make_inputs(w)
+    t = dev(d)
+    W = awq.awq_dequant(t["qweight"], t["qzeros"], t["scales"], w.group_size, dtype=torch.float16)
+    torch.cuda.synchronize()
+    ref = oracle.fp16_rne(oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], w.group_size))
+    assert np.array_equal(bits(W.cpu().numpy()), bits(ref))
+
+
+def test_dequant_f16_negative_scales():
+    d = synth.make_custom(5, 352, 800, 32, seed=13)
+    d["scales"] = (-d["scales"].astype(np.float32)).astype(np.float16)
+    t = dev(d)
+    W = awq.awq_dequant(t["qweight"], t["qzeros"], t["scales"], 32, dtype=torch.float16).cpu().numpy()
+    ref = oracle.fp16_rne(oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], 32))
+    assert np.array_equal(bits(W), bits(ref))

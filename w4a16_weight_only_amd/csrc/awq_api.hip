@@ -268,16 +268,28 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* fami
   return AWQ_OK;
 }
 
-int awq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K,
-                int64_t N, int64_t group_size, float* out, struct ihipStream_t* stream) {
+namespace {
+int dequant_common(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K, int64_t N,
+                   int64_t group_size, void* out, bool f16, hipStream_t stream) {
   const int st = limits_check(0, K, N, group_size);
   if (st != AWQ_OK) return st;
   if (!qweight || !qzeros || !scales_f16 || !out) return AWQ_ERR_NULL;
   if (!aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16) || !aligned16(out))
     return AWQ_ERR_ALIGN;
   hipError_t e = awq::launch_dequant(qweight, qzeros, static_cast<const uint16_t*>(scales_f16), (int)K,
-                                     (int)N, eff_group(K, group_size), out, stream);
+                                     (int)N, eff_group(K, group_size), out, f16, stream);
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+}  // namespace
+
+int awq_dequant(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K,
+                int64_t N, int64_t group_size, float* out, struct ihipStream_t* stream) {
+  return dequant_common(qweight, qzeros, scales_f16, K, N, group_size, out, false, stream);
+}
+
+int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K,
+                    int64_t N, int64_t group_size, void* out_f16, struct ihipStream_t* stream) {
+  return dequant_common(qweight, qzeros, scales_f16, K, N, group_size, out_f16, true, stream);
 }
 
 int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,

@@ -1,23 +1,26 @@
-// awq_dequant: packed AWQ GEMM weight -> float32 [K, N], exact.
+// awq_dequant / awq_dequant_f16: packed AWQ GEMM weight -> float32 or fp16 [K, N].
 //
 // W[k, n] = (float)(q[k, n] - z[k / g, n]) * (float)s[k / g, n]
 // (tensref.org "AWQ" format page, Reader; rule AWQ-005: the zero is subtracted as
 // stored).  The product of a 4-bit difference and an fp16 scale is exact in fp32,
-// so this kernel's output is the unique correct bit pattern.
+// so the float32 output is the unique correct bit pattern, and the fp16 output is
+// that value rounded once to nearest even (the weight a dequantize-then-matmul path
+// feeds to a dense fp16 GEMM: vLLM article, section 5.3).
 //
 // Bandwidth-bound: per packed word it reads 4 B of qweight (+ the group's zero word
-// and 16 B of scales, mostly L2 hits) and writes 32 B.  One thread per word, eight
-// consecutive float32 outputs written as two 16-byte stores; consecutive threads
-// own consecutive words of a row, so both loads and stores are coalesced.
+// and 16 B of scales, mostly L2 hits) and writes 32 B (float32) or 16 B (fp16).  One
+// thread per word, eight consecutive outputs written as 16-byte stores; consecutive
+// threads own consecutive words of a row, so both loads and stores are coalesced.
 #include "awq_device.h"
 #include "awq_kernels.h"
 
 namespace awq {
 
+template <typename T>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ qweight,
                                                       const uint32_t* __restrict__ qzeros,
                                                       const _Float16* __restrict__ scales, int K,
-                                                      int N, int g, float* __restrict__ out) {
+                                                      int N, int g, T* __restrict__ out) {
   const int NW = N >> 3;
   const int64_t total = (int64_t)K * NW;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -37,21 +40,33 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
     o[j] = (float)(q - z) * s;
   }
-  float4* dst = reinterpret_cast<float4*>(out + (int64_t)k * N + 8 * c);
-  dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-  dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+  if constexpr (sizeof(T) == 4) {
+    float4* dst = reinterpret_cast<float4*>(out + (int64_t)k * N + 8 * c);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+  } else {
+    half8v h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)o[j];  // one rounding of the exact product
+    *reinterpret_cast<half8v*>(out + (int64_t)k * N + 8 * c) = h;
+  }
   }
 }
 
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
-                          int K, int N, int g, float* out, hipStream_t stream) {
+                          int K, int N, int g, void* out, bool f16, hipStream_t stream) {
   const int64_t words = (int64_t)K * (N / 8);
   int64_t blocks = (words + 255) / 256;
   if (blocks > (1 << 20)) blocks = 1 << 20;  // grid-stride beyond ~268M words
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const uint32_t*>(qweight),
-                     reinterpret_cast<const uint32_t*>(qzeros),
-                     reinterpret_cast<const _Float16*>(scales), K, N, g, out);
+  const auto* qw = reinterpret_cast<const uint32_t*>(qweight);
+  const auto* qz = reinterpret_cast<const uint32_t*>(qzeros);
+  const auto* sc = reinterpret_cast<const _Float16*>(scales);
+  if (f16)
+    hipLaunchKernelGGL(dequant_kernel<_Float16>, dim3((unsigned)blocks), dim3(256), 0, stream, qw, qz, sc, K, N,
+                       g, static_cast<_Float16*>(out));
+  else
+    hipLaunchKernelGGL(dequant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, qw, qz, sc, K, N, g,
+                       static_cast<float*>(out));
   return hipGetLastError();
 }
 

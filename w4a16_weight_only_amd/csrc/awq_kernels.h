@@ -41,8 +41,9 @@ struct TilePlan {
   int kps;     // k-tiles of kTileBK per split
 };
 
+// out: float32 [K, N] (f16 = false) or fp16 [K, N] (f16 = true).
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
-                          int K, int N, int g, float* out, hipStream_t stream);
+                          int K, int N, int g, void* out, bool f16, hipStream_t stream);
 
 // With p.splits > 1: 4-wave plans use accum, [n_tiles][mrows * 256] 64-bit
 // accumulators that are zero before the call and left zero by it; 8-wave plans use

@@ -75,8 +75,11 @@ def plan(M: int, K: int, N: int, group_size: int) -> dict:
 
 
 def awq_dequant(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
-                group_size: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
-    """float32 [K, N] = (q - z) * s, bit-exact."""
+                group_size: int = 128, out: torch.Tensor | None = None,
+                dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """[K, N] = (q - z) * s: float32 bit-exact, or fp16 rounded once (dtype=torch.float16)."""
+    if dtype not in (torch.float32, torch.float16):
+        raise TypeError("dtype must be torch.float32 or torch.float16")
     _check_tensor("qweight", qweight, torch.int32)
     dev = qweight.device
     _check_tensor("qzeros", qzeros, torch.int32, dev)
@@ -84,15 +87,15 @@ def awq_dequant(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tenso
     K, N = qweight.shape[0], qweight.shape[1] * 8
     validate(K, N, group_size, qweight, qzeros, scales)
     if out is None:
-        out = torch.empty((K, N), dtype=torch.float32, device=dev)
+        out = torch.empty((K, N), dtype=dtype, device=dev)
     else:
-        _check_tensor("out", out, torch.float32, dev)
+        _check_tensor("out", out, dtype, dev)
         if tuple(out.shape) != (K, N):
             raise ValueError(f"out must be [{K}, {N}]")
+    fn = _lib.load().awq_dequant if dtype == torch.float32 else _lib.load().awq_dequant_f16
     with torch.cuda.device(dev):
-        st = _lib.load().awq_dequant(_ptr(qweight), _ptr(qzeros), _ptr(scales), K, N, group_size,
-                                     _ptr(out), _stream(dev))
-    _lib.check(st, "awq_dequant")
+        st = fn(_ptr(qweight), _ptr(qzeros), _ptr(scales), K, N, group_size, _ptr(out), _stream(dev))
+    _lib.check(st, "awq_dequant" if dtype == torch.float32 else "awq_dequant_f16")
     return out
 
 
