@@ -18,7 +18,9 @@ workload, over the whole timed region.  `roofline` prices the kernel's average
 launch duration (HIP events on the launch stream over the timed region) against
 MI355X's peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
 same workload.  `read_ceiling` times a plain streaming read of the same byte count;
-`secondary` repeats the timing (not the CPU leg) for every other workload.
+`secondary` repeats the timing (not the CPU leg) for every other workload, and for
+the large-M (tile family) ones also times the dequantize-then-dense alternative
+(awq_dequant_f16 + torch's fp16 GEMM) under the same protocol.
 """
 from __future__ import annotations
 
@@ -130,6 +132,53 @@ def time_workload(name, steps, warmup, torch, awq, synth):
     torch.cuda.empty_cache()
     return dict(workload=w, wall_s=wall_s, event_s=event_s, copies=copies,
                 plan=awq.plan(w.M, w.K, w.N, w.group_size))
+
+
+def time_dequant_dense(name, steps, torch, awq, synth):
+    """The pages' large-batch alternative on the same inputs and protocol: awq_dequant_f16
+    into one fp16 [K, N] buffer, then torch's dense fp16 GEMM (hipBLASLt) with the bias
+    folded in (addmm).  Returns us per call; a comparison point, not the product path."""
+    w = synth.WORKLOADS[name]
+    d = synth.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    layer_bytes = d["qweight"].nbytes + d["qzeros"].nbytes + d["scales"].nbytes
+    copies = max(1, -(-ROTATE_BYTES // layer_bytes))
+    x = torch.from_numpy(d["x"]).to(dev)
+    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+    weights = [tuple(torch.from_numpy(d[k]).to(dev) for k in ("qweight", "qzeros", "scales")) for _ in range(copies)]
+    wf = torch.empty((w.K, w.N), dtype=torch.float16, device=dev)
+    y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(dev)
+
+    def step(i):
+        qw, qz, sc = weights[i % copies]
+        awq.awq_dequant(qw, qz, sc, w.group_size, out=wf, dtype=torch.float16)
+        if bias is None:
+            torch.matmul(x, wf, out=y)
+        else:
+            torch.addmm(bias, x, wf, out=y)
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            step(i)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        stream.synchronize()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    del weights, graph
+    torch.cuda.empty_cache()
+    return round(us, 3)
 
 
 def read_ceiling(nbytes, torch, steps=400):
@@ -284,8 +333,12 @@ def main():
             n_steps = min(args.steps, 200)
             rs = time_workload(name, n_steps, 10, torch, awq, synth)
             v, u, rf, pl = summarize(rs, n_steps)
-            sec.append(dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3),
-                            plan=rs["plan"], roofline=rf))
+            entry = dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3),
+                         plan=rs["plan"], roofline=rf)
+            if rs["plan"]["family"] == "tile":
+                dd = time_dequant_dense(name, n_steps, torch, awq, synth)
+                entry["dequant_then_dense_us"] = dd  # awq_dequant_f16 + hipBLASLt fp16 GEMM
+            sec.append(entry)
         out["secondary"] = sec
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, synth)
