@@ -6,5 +6,5 @@ this package.  The HIP library and its Python binding never do.
 from .awq_ref import (  # noqa: F401
     AWQ_ORDER, AWQ_REVERSE, AwqFormatError, resolve_groups, validate_pack,
     pack_awq, unpack_awq, unpack_awq_gather, dequant_ref, dequant_ref_T,
-    gemm_ref, gemm_ref_entries, fp16_rne,
+    gemm_ref, gemm_ref_entries, fp16_rne, quantize_rtn,
 )

@@ -26,6 +26,10 @@ Sources (cited by page and section):
               pack order [0,4,1,5,2,6,3,7]) and 5.3 (kernels unpack with
               (w >> shift) & 0xF, then (w - z) * s, before the matmul).
 
+The RTN writer `quantize_rtn` (the step before this path: dense fp16 weights to
+the GEMM layout) follows [GPTQM] "Group quantization and zero points", the table of
+the asymmetric and symmetric quantizers.
+
 Readings where the pages are silent (each is listed in the design notes):
   * group_size == -1 means G = 1 (one group spanning all K rows).
   * N % 8 != 0 and K % group_size != 0 are rejected, never truncated.
@@ -234,3 +238,48 @@ def gemm_ref_entries(x, qweight, qzeros, scales, bias, group_size, rows, cols) -
 def fp16_rne(a) -> np.ndarray:
     """Round to IEEE binary16, nearest-even (numpy's cast), for exact-output pins."""
     return np.asarray(a).astype(np.float16)
+
+
+def quantize_rtn(W, group_size: int, sym: bool = False):
+    """Round-to-nearest writer: fp16 W [K, N] -> (qweight [K, N/8], qzeros [G, N/8],
+    scales fp16 [G, N]) in the GEMM layout, so that dequant_ref gives back
+    (code - zero) * scale.
+
+    [GPTQM] "Group quantization and zero points", per group of g input rows k and
+    per output column n (W is in the orientation of dequant_ref, [K, N]):
+      asymmetric: scale = max(max - min, 1e-5) / 15,  zero = clamp(-round(min / scale), 0, 15),
+                  code  = clamp(round(w / scale) + zero, 0, 15);
+      symmetric:  scale = max(max |w|, 1e-5) / 7, signed code = clamp(round(w / scale), -8, 7),
+                  stored as code + 8 with zero = 8.
+    Readings (the pages give the formulas, not the arithmetic): the scale is
+    computed in float32 and rounded once to the stored fp16 value, and every later
+    step (min / scale, w / scale) divides by that stored value in float32; round is
+    to nearest, ties to even.  A writer thus picks the codes for the scale a reader
+    will actually use.
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float16 or W.ndim != 2:
+        raise AwqFormatError("W must be a 2-D fp16 array [K, N]")
+    K, N = W.shape
+    if N % 8 != 0:
+        raise AwqFormatError(f"N={N} is not a multiple of 8")
+    g, G = resolve_groups(K, group_size)
+    Wg = W.astype(np.float32).reshape(G, g, N)
+    if sym:
+        amax = np.abs(Wg).max(axis=1)
+        s32 = np.maximum(amax, np.float32(1e-5)) / np.float32(7)
+        scales = s32.astype(np.float16)
+        sf = scales.astype(np.float32)
+        codes = np.clip(np.rint(Wg / sf[:, None, :]), -8, 7) + 8
+        zeros = np.full((G, N), 8.0, dtype=np.float32)
+    else:
+        mx = Wg.max(axis=1)
+        mn = Wg.min(axis=1)
+        s32 = np.maximum(mx - mn, np.float32(1e-5)) / np.float32(15)
+        scales = s32.astype(np.float16)
+        sf = scales.astype(np.float32)
+        zeros = np.clip(-np.rint(mn / sf), 0, 15)
+        codes = np.clip(np.rint(Wg / sf[:, None, :]) + zeros[:, None, :], 0, 15)
+    qweight = pack_awq(codes.reshape(K, N).astype(np.int64))
+    qzeros = pack_awq(zeros.astype(np.int64))
+    return qweight, qzeros, scales

@@ -280,6 +280,71 @@ def pin_fp16_rounding(o):
         assert np.isinf(o.fp16_rne(np.float32(65520.0)))  # halfway to 2^16 rounds to even: overflow
 
 
-ALL_PINS = [pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
+def pin_rtn_hand_example(o):
+    """tests/golden/rtn_example.json: one group of 4 rows, 8 equal columns, worked by hand
+    from the quantizer table (asymmetric and symmetric)."""
+    import json
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rtn_example.json")))
+    W = np.tile(np.array(gold["W_column"], dtype=np.float16)[:, None], (1, 8))
+    for mode, sym in (("asymmetric", False), ("symmetric", True)):
+        qw, qz, sc = o.quantize_rtn(W, gold["group_size"], sym=sym)
+        codes = o.unpack_awq(qw)
+        assert (codes == np.array(gold[mode]["codes"])[:, None]).all(), (mode, codes[:, 0])
+        assert (o.unpack_awq(qz) == gold[mode]["zero"]).all(), mode
+        assert (sc.view(np.uint16) == int(gold[mode]["scale_bits"], 16)).all(), (mode, hex(sc.view(np.uint16)[0, 0]))
+
+
+def pin_rtn_roundtrip(o):
+    """A layer that is already on the quantizer's grid comes back unchanged: if every
+    group column holds codes 0 and 15 and a normal fp16 scale s, its max - min is 15 s
+    exactly, so the scale, the zero (-round(-z) = z) and every code (round(q - z) + z)
+    are recovered: quantize(dequant(q, z, s)) == (q, z, s).  (Scales are chosen so that
+    the dequantised weights are fp16 values.)"""
+    rng = _rng(21)
+    for K, N, g in ((64, 16, 32), (128, 24, -1), (96, 8, 32)):
+        _, G = o.resolve_groups(K, g)
+        gl = K // G
+        codes = rng.integers(0, 16, (K, N))
+        codes.reshape(G, gl, N)[:, 0, :] = 0
+        codes.reshape(G, gl, N)[:, 1, :] = 15
+        zeros = rng.integers(0, 16, (G, N))
+        # Scales with 7 significant bits, so every (q - z) s (<= 11 bits) is an fp16 value.
+        scales = (rng.integers(64, 128, (G, N)) * 2.0 ** -13).astype(np.float16)
+        qw, qz = o.pack_awq(codes), o.pack_awq(zeros)
+        with np.errstate(over="ignore"):  # (a planted mistake may overflow)
+            W = o.dequant_ref(qw, qz, scales, g).astype(np.float16)
+        assert (W.astype(np.float32) == o.dequant_ref(qw, qz, scales, g)).all()  # values fit fp16
+        qw2, qz2, sc2 = o.quantize_rtn(W, g)
+        assert np.array_equal(sc2.view(np.uint16), scales.view(np.uint16))
+        assert np.array_equal(o.unpack_awq(qz2), zeros)
+        assert np.array_equal(o.unpack_awq(qw2), codes)
+
+
+def pin_rtn_error_bound(o):
+    """Round to nearest: every code that is not clamped reconstructs its weight to within
+    half a step, |w - (q - z) s| <= s / 2 (plus the float32 division's rounding); clamped
+    codes sit at 0 or 15.  Symmetric: zero is 8 and codes span the signed range."""
+    rng = _rng(22)
+    for K, N, g in ((256, 32, 64), (128, 16, -1)):
+        W = rng.normal(0, 0.02, (K, N)).astype(np.float16)
+        _, G = o.resolve_groups(K, g)
+        gl = K // G
+        for sym in (False, True):
+            qw, qz, sc = o.quantize_rtn(W, g, sym=sym)
+            q = o.unpack_awq(qw).astype(np.float64)
+            z = np.repeat(o.unpack_awq(qz), gl, axis=0).astype(np.float64)
+            s = np.repeat(sc.astype(np.float64), gl, axis=0)
+            w = W.astype(np.float64)
+            err = np.abs(w - (q - z) * s)
+            free = (q > 0) & (q < 15)
+            assert (err[free] <= s[free] * (0.5 + 2.0 ** -20) + np.abs(w[free]) * 2.0 ** -23).all(), sym
+            if sym:
+                assert (z == 8).all()
+            else:
+                # The group's max and min are reconstructed within one step of the grid.
+                assert (sc.astype(np.float64) > 0).all()
+
+
+ALL_PINS = [pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
             pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
             pin_special_cases, pin_entries_agree, pin_format_rules]

@@ -54,6 +54,16 @@ MUTANTS = [
      "    _, G", 0),
     ("pack shifts by the column index",
      "<< np.uint32(4 * i)", "<< np.uint32(4 * AWQ_ORDER[i])", 0),
+    ("RTN codes truncated instead of rounded",
+     "codes = np.clip(np.rint(Wg / sf[:, None, :]) + zeros", "codes = np.clip(np.floor(Wg / sf[:, None, :]) + zeros", 0),
+    ("RTN zero not negated",
+     "zeros = np.clip(-np.rint(mn / sf), 0, 15)", "zeros = np.clip(np.rint(mn / sf), 0, 15)", 0),
+    ("RTN scale over 16 levels instead of 15 steps",
+     "np.maximum(mx - mn, np.float32(1e-5)) / np.float32(15)", "np.maximum(mx - mn, np.float32(1e-5)) / np.float32(16)", 0),
+    ("RTN scale from the max alone",
+     "np.maximum(mx - mn, np.float32(1e-5))", "np.maximum(mx, np.float32(1e-5))", 0),
+    ("RTN symmetric scale over 8",
+     "np.maximum(amax, np.float32(1e-5)) / np.float32(7)", "np.maximum(amax, np.float32(1e-5)) / np.float32(8)", 0),
 ]
 
 
