@@ -181,6 +181,49 @@ def time_dequant_dense(name, steps, torch, awq, synth):
     return round(us, 3)
 
 
+def time_quantize_rtn(K, N, g, sym, steps, torch, awq, synth):
+    """The RTN writer on a [K, N] fp16 weight, same protocol (rotated copies, one graph
+    replay timed with HIP events on the launch stream).  Algorithmic bytes: the fp16
+    weight read once, the packed codes written, plus 2.5 bytes per (group, column)
+    of scales and zeros."""
+    G = 1 if g == -1 else K // g
+    nbytes = K * N * 2 + K * N // 2 + G * N * 2 + G * N // 2
+    dev = torch.device("cuda", 0)
+    W = torch.from_numpy(synth.make_weights(K, N, seed=1)).to(dev)
+    copies = max(1, -(-ROTATE_BYTES // (K * N * 2)))
+    ws = [W.clone() for _ in range(copies)]
+    outs = [awq.awq_quantize_rtn(ws[i], g, sym) for i in range(copies)]
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        awq.awq_quantize_rtn(ws[i % copies], g, sym, out=outs[i % copies])
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            step(i)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        stream.synchronize()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    s_per = ev0.elapsed_time(ev1) / 1e3 / steps
+    del ws, outs, graph
+    torch.cuda.empty_cache()
+    gbs = nbytes / s_per / 1e9
+    return dict(K=K, N=N, group_size=g, sym=bool(sym), kernel_avg_us=round(s_per * 1e6, 3),
+                algorithmic_bytes=nbytes, achieved_gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
 def read_ceiling(nbytes, torch, steps=400):
     """A plain streaming read of the same byte count for comparison: the probe
     library's read kernel (16-byte nontemporal loads, 16 KiB contiguous per
@@ -340,6 +383,10 @@ def main():
                 entry["dequant_then_dense_us"] = dd  # awq_dequant_f16 + hipBLASLt fp16 GEMM
             sec.append(entry)
         out["secondary"] = sec
+        # The RTN writer (fp16 weight -> GEMM pack), HBM-bound.
+        out["writer"] = [time_quantize_rtn(K, N, g, sym, min(args.steps, 100), torch, awq, synth)
+                         for (K, N, g, sym) in ((4096, 4096, 128, False), (4096, 4096, 128, True),
+                                                (4096, 14336, 128, False), (4096, 4096, -1, False))]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, synth)
     print(json.dumps(out), flush=True)

@@ -142,6 +142,34 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
              void* y_f16, struct ihipStream_t* stream);
 
 /*
+ * Round-to-nearest writer of the GEMM pack: quantise an fp16 weight in groups of
+ * group_size input rows per output column.  Source: GPTQModel wiki "AWQ", section
+ * "Group quantization and zero points" (both quantizers, the clamp of the zero, the
+ * 1e-5 floor of the range, -1 = one group) and section "Saved formats and packing"
+ * (the nibble order above).  With w the weights of one (group, column):
+ *   sym == 0 (asymmetric): s = fp16(max(max w - min w, 1e-5) / 15),
+ *                          z = clamp(-round(min w / s), 0, 15),
+ *                          q = clamp(round(w / s) + z, 0, 15)
+ *   sym == 1 (symmetric):  s = fp16(max(max |w|, 1e-5) / 7), z = 8,
+ *                          q = clamp(round(w / s), -8, 7) + 8
+ * The scale is computed in float32 and rounded once (to nearest even) to the stored
+ * fp16 value; both divisions are float32 divisions, correctly rounded, by that
+ * stored value; round() is to nearest with ties to even.  The output is therefore
+ * unique: awq_dequant of it gives (q - z) * s for the scale a reader actually uses.
+ *   w_f16        device fp16 [K, N], row-major, in the orientation x . W multiplies
+ *                (input features by output features; a [N, K] nn.Linear weight must
+ *                be transposed first); finite values
+ *   K, N, group_size   the format rules of awq_validate_pack (K, N <= 2^24)
+ *   sym          0 or 1
+ *   qweight      device int32 [K, N/8];  qzeros int32 [G, N/8];  scales_f16 fp16 [G, N];
+ *                all written in full
+ * Returns AWQ_OK or an error status (nothing enqueued on error).
+ */
+int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size, int sym,
+                     int32_t* qweight, int32_t* qzeros, void* scales_f16,
+                     struct ihipStream_t* stream);
+
+/*
  * The launch plan awq_gemm would use for this shape (host-only, no device work).
  *   family   0 = skinny split-K family, 1 = MFMA tile family
  *   splits   number of K splits across workgroups (1 = none)

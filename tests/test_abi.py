@@ -130,6 +130,23 @@ def test_gemm_argument_errors_touch_no_device(lib):
     assert lib.awq_dequant(p, p, odd, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
 
 
+def test_quantize_rtn_argument_errors_touch_no_device(lib):
+    """The writer checks the format rules, sym, pointers and alignment before any HIP call."""
+    p = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    q = lib.awq_quantize_rtn
+    assert q(p, 4096, 4100, 128, 0, p, p, p, None) == _lib.AWQ_ERR_SHAPE
+    assert q(p, 4096, 4096, 100, 0, p, p, p, None) == _lib.AWQ_ERR_GROUP
+    assert q(p, 4096, 4096, 0, 0, p, p, p, None) == _lib.AWQ_ERR_GROUP
+    assert q(p, 0, 4096, -1, 0, p, p, p, None) == _lib.AWQ_ERR_SHAPE
+    assert q(p, 4096, 4096, 128, 2, p, p, p, None) == _lib.AWQ_ERR_SHAPE
+    assert q(p, (1 << 24) + 128, 4096, 128, 0, p, p, p, None) == _lib.AWQ_ERR_UNSUPPORTED
+    assert q(None, 4096, 4096, 128, 0, p, p, p, None) == _lib.AWQ_ERR_NULL
+    assert q(p, 4096, 4096, 128, 0, p, p, None, None) == _lib.AWQ_ERR_NULL
+    assert q(odd, 4096, 4096, 128, 0, p, p, p, None) == _lib.AWQ_ERR_ALIGN
+    assert q(p, 4096, 4096, 128, 1, p, odd, p, None) == _lib.AWQ_ERR_ALIGN
+
+
 def test_quantization_config():
     cfg = {"quant_method": "awq", "bits": 4, "group_size": 64, "zero_point": True, "version": "gemm"}
     assert awq.group_size_from_config(cfg) == 64

@@ -292,6 +292,24 @@ int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* s
   return dequant_common(qweight, qzeros, scales_f16, K, N, group_size, out_f16, true, stream);
 }
 
+int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size, int sym, int32_t* qweight,
+                     int32_t* qzeros, void* scales_f16, struct ihipStream_t* stream) {
+  int st = format_check(K, N, group_size);
+  if (st != AWQ_OK) return st;
+  if (sym != 0 && sym != 1) return AWQ_ERR_SHAPE;
+  if (K > kMaxDim || N > kMaxDim) return AWQ_ERR_UNSUPPORTED;
+  const int g = eff_group(K, group_size);
+  int block, cols;
+  awq::rtn_plan(g, (int)N, &block, &cols);
+  if ((K / g) * ((N + cols - 1) / cols) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  if (!w_f16 || !qweight || !qzeros || !scales_f16) return AWQ_ERR_NULL;
+  if (!aligned16(w_f16) || !aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16))
+    return AWQ_ERR_ALIGN;
+  hipError_t e = awq::launch_quantize_rtn(static_cast<const uint16_t*>(w_f16), (int)K, (int)N, g, sym != 0, qweight,
+                                          qzeros, static_cast<uint16_t*>(scales_f16), stream);
+  return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+
 int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
              const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
              struct ihipStream_t* stream) {

@@ -45,6 +45,13 @@ struct TilePlan {
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, void* out, bool f16, hipStream_t stream);
 
+// RTN writer: fp16 w [K, N] -> qweight [K, N/8], qzeros [K/g, N/8], scales fp16 [K/g, N].
+// rtn_plan reports the variant (0: groups of up to 128 rows, 1: longer groups), the
+// block size and the output columns one workgroup covers.
+int rtn_plan(int g, int N, int* block, int* cols_per_block);
+hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
+                               int32_t* qzeros, uint16_t* scales, hipStream_t stream);
+
 // With p.splits > 1: 4-wave plans use accum, [n_tiles][mrows * 256] 64-bit
 // accumulators that are zero before the call and left zero by it; 8-wave plans use
 // partial, [n_tiles][splits][16 * 256] fp32 scratch, and a second reduce kernel.

@@ -99,6 +99,40 @@ def awq_dequant(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tenso
     return out
 
 
+def awq_quantize_rtn(w: torch.Tensor, group_size: int = 128, sym: bool = False,
+                     out: tuple | None = None) -> tuple:
+    """Round-to-nearest writer: fp16 w [K, N] (input by output features) ->
+    (qweight int32 [K, N/8], qzeros int32 [G, N/8], scales fp16 [G, N]) in the GEMM
+    layout.  out, if given, is such a triple to write into."""
+    _check_tensor("w", w, torch.float16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [K, N]")
+    dev = w.device
+    K, N = w.shape
+    lib = _lib.load()
+    if N % 8 != 0:
+        _lib.check(_lib.AWQ_ERR_SHAPE, "awq_quantize_rtn")
+    if group_size != -1 and (group_size <= 0 or K % group_size != 0):
+        _lib.check(_lib.AWQ_ERR_GROUP, "awq_quantize_rtn")
+    G = 1 if group_size == -1 else K // group_size
+    if out is None:
+        out = (torch.empty((K, N // 8), dtype=torch.int32, device=dev),
+               torch.empty((G, N // 8), dtype=torch.int32, device=dev),
+               torch.empty((G, N), dtype=torch.float16, device=dev))
+    qweight, qzeros, scales = out
+    for name, t, dt, shape in (("qweight", qweight, torch.int32, (K, N // 8)),
+                               ("qzeros", qzeros, torch.int32, (G, N // 8)),
+                               ("scales", scales, torch.float16, (G, N))):
+        _check_tensor(name, t, dt, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    with torch.cuda.device(dev):
+        st = lib.awq_quantize_rtn(_ptr(w), K, N, group_size, int(bool(sym)), _ptr(qweight), _ptr(qzeros),
+                                  _ptr(scales), _stream(dev))
+    _lib.check(st, "awq_quantize_rtn")
+    return qweight, qzeros, scales
+
+
 def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
              bias: torch.Tensor | None = None, group_size: int = 128,
              out: torch.Tensor | None = None) -> torch.Tensor:

@@ -99,3 +99,19 @@ def make_custom(M, K, N, group_size, bias=True, seed=0, outlier_count=0) -> dict
     """Same distributions at an arbitrary shape (ragged and edge-case tests)."""
     return make_inputs(Workload(f"custom_m{M}_k{K}_n{N}_g{group_size}", M, K, N, group_size,
                                 bias, outlier_count=outlier_count, seed=seed))
+
+
+def make_weights(K: int, N: int, seed: int = 0, std: float = 0.02, outlier_cols: int = 0,
+                 outlier_gain: float = 20.0) -> np.ndarray:
+    """fp16 dense weight [K, N] (input by output features) for the RTN writer.
+
+    Draw order: normal(0, std) float64 [K, N]; then, if outlier_cols > 0, that many
+    output columns (rng.choice without replacement) scaled by outlier_gain (the
+    salient channels that make per-column ranges differ); rounded to fp16 last.
+    std 0.02 is the usual initialisation scale of transformer linear layers."""
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0.0, std, size=(K, N))
+    if outlier_cols:
+        idx = rng.choice(N, size=outlier_cols, replace=False)
+        w[:, idx] *= outlier_gain
+    return w.astype(np.float16)
