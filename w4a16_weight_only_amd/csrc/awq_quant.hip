@@ -5,7 +5,7 @@
 //   asymmetric: s = fp16(max(max - min, 1e-5) / 15), z = clamp(-rint(min / s), 0, 15),
 //               q = clamp(rint(w / s) + z, 0, 15)
 //   symmetric:  s = fp16(max(max |w|, 1e-5) / 7),   z = 8,
-//               q = clamp(rint(w / s), -8, 7) + 8
+//               q = clamp(rint(w / s), -8, 7) + 8 = clamp(rint(w / s) + 8, 0, 15)
 // The scale is computed in fp32 and rounded once to the stored fp16 value; every
 // later division uses that stored value, in fp32, correctly rounded, and rint rounds
 // half to even.  Codes are packed with nibble i of word c holding column
@@ -16,9 +16,11 @@
 // word column c (8 weights wide) and a strided slice of the group's rows; the
 // lanes of a wave cover CL adjacent word columns and 64 / CL row slices, so every
 // row load is a contiguous 16*CL-byte run.  The rows of a group are read once into
-// registers, reduced to the per-column min and max (lane shuffles, then LDS across
-// the waves), and coded from the registers; groups longer than the register cache
-// are read a second time for the coding pass.
+// registers, reduced to the per-column min and max (packed fp16, exact: the inputs
+// are fp16), across lanes by shuffles and across waves through LDS, and coded from
+// the registers.  Small workgroups let several groups share a CU at different
+// phases, so one group's coding overlaps another's loads.  Groups longer than the
+// register cache are read a second time for the coding pass.
 #include "awq_device.h"
 #include "awq_kernels.h"
 
@@ -26,37 +28,83 @@ namespace awq {
 
 namespace {
 
-struct ColStats {
-  float mn[8], mx[8];
+// Packed fp16 min / max.  The NaN-propagating forms need no canonicalising of
+// their inputs (the inputs are finite), and chains of two fold into gfx950's
+// three-operand v_pk_minimum3_f16 / v_pk_maximum3_f16.  They order -0 below +0,
+// which changes no output: a zero min or max only enters max(range, 1e-5),
+// max(|w|, 1e-5) and a zero point rounded from +-0.
+__device__ __forceinline__ half2v hmin2(half2v a, half2v b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ half2v hmax2(half2v a, half2v b) { return __builtin_elementwise_maximum(a, b); }
+
+// Per-thread running min / max of 8 columns as 4 packed fp16 pairs (column pairs
+// (0,1), (2,3), (4,5), (6,7) of the 16-byte row chunk).
+struct PairStats {
+  half2v mn[4], mx[4];
 };
 
-__device__ __forceinline__ void unpack8(const u32x4& v, float f[8]) {
+__device__ __forceinline__ void accumulate(PairStats& st, const u32x4& v) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    f[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
-}
-
-__device__ __forceinline__ void accumulate(ColStats& st, const u32x4& v) {
-  float f[8];
-  unpack8(v, f);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    st.mn[j] = fminf(st.mn[j], f[j]);
-    st.mx[j] = fmaxf(st.mx[j], f[j]);
+  for (int p = 0; p < 4; ++p) {
+    st.mn[p] = hmin2(st.mn[p], as_h2(v[p]));
+    st.mx[p] = hmax2(st.mx[p], as_h2(v[p]));
   }
 }
 
-// Codes of one row (8 columns) packed into one word.
-__device__ __forceinline__ uint32_t code_word(const u32x4& v, const float sf[8], const float zf[8], bool sym) {
-  float f[8];
-  unpack8(v, f);
+__device__ __forceinline__ void accumulate2(PairStats& st, const u32x4& v, const u32x4& u) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    st.mn[p] = hmin2(hmin2(st.mn[p], as_h2(v[p])), as_h2(u[p]));
+    st.mx[p] = hmax2(hmax2(st.mx[p], as_h2(v[p])), as_h2(u[p]));
+  }
+}
+
+__device__ __forceinline__ float col_of(const u32x4& v, int j) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
+}
+
+// Codes of one row (8 columns) packed into one word.  q = rint(fl32(w / s)) needs
+// the division rounded as IEEE fp32 division.
+//
+// Fast path.  With P = w * rcp(s) (exact product): v_rcp_f32 is within 1 ulp, so P
+// is within about 1.5 * 2^-23 |w / s| of w / s, and fl32(w / s) within 2^-24 |w / s|:
+// together less than 2^-18 while |w / s| < 16.  One fma, x = fl32(P + (M + z)) with
+// M = 1.5 * 2^23, rounds P + z to an integer held in the low mantissa bits of x
+// (values in [2^23, 2^24) are spaced 1 apart); the clamp to [M, M + 15] and
+// bits(x) - bits(M) then give the code.  A second fma measures d = P - (x - M - z).
+// If |d| < 1/2 - 2^-16, P is not near a half-integer, so x - M - z = rint(P) =
+// rint(w / s) = rint(fl32(w / s)).  If |w / s| >= 16, both the fast and the exact
+// value of rint(w / s) + z lie beyond the clamp range on the same side (z is in
+// 0..15; x is monotone in P), so the clamped code agrees whatever d is.  A row in
+// which some |d| reaches 1/2 - 2^-16 (ties included) is flagged, and the caller
+// redoes it with correctly rounded divisions (code_word_exact).  zf holds z (8
+// when symmetric), mzf holds M + z.
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kMagicBits = 0x4B400000u;
+
+__device__ __forceinline__ uint32_t code_word_exact(const u32x4& v, const float sf[8], const float zf[8]) {
   uint32_t word = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float r = rintf(f[j] / sf[j]);
-    const float q = sym ? fminf(fmaxf(r, -8.0f), 7.0f) + 8.0f : fminf(fmaxf(r + zf[j], 0.0f), 15.0f);
-    word |= (uint32_t)(int)q << (4 * nibble_of_col(j));
+    const float q = __builtin_amdgcn_fmed3f(rintf(col_of(v, j) / sf[j]) + zf[j], 0.0f, 15.0f);
+    word |= (uint32_t)q << (4 * nibble_of_col(j));
   }
+  return word;
+}
+
+__device__ __forceinline__ uint32_t code_word_fast(const u32x4& v, const float rf[8], const float mzf[8],
+                                                   bool& near) {
+  uint32_t word = 0;
+  float dmax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float wj = col_of(v, j);
+    const float x = __builtin_fmaf(wj, rf[j], mzf[j]);
+    const float d = __builtin_fmaf(wj, rf[j], mzf[j] - x);
+    dmax = fmaxf(dmax, fabsf(d));
+    const float y = __builtin_amdgcn_fmed3f(x, kMagic, kMagic + 15.0f);
+    word |= (__builtin_bit_cast(uint32_t, y) - kMagicBits) << (4 * nibble_of_col(j));
+  }
+  near = dmax >= 0.5f - 0x1p-16f;
   return word;
 }
 
@@ -72,7 +120,7 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
                                                         u32x4* __restrict__ scales) {
   constexpr int RL = 64 / CL;     // row slices per wave
   constexpr int S = WAVES * RL;   // row slices per workgroup
-  __shared__ float red[2][WAVES][CL][8];
+  __shared__ u32x4 red[2][WAVES][CL];  // per-wave min / max, packed fp16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,72 +133,69 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
   const int64_t row0 = (int64_t)grp * g;
   const bool resident = g <= S * CACHE;
 
-  ColStats st;
+  PairStats st;
+  const _Float16 inf = (_Float16)__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    st.mn[j] = __builtin_inff();
-    st.mx[j] = -__builtin_inff();
+  for (int p = 0; p < 4; ++p) {
+    st.mn[p] = half2v{inf, inf};
+    st.mx[p] = half2v{-inf, -inf};
   }
+  // Loads are unconditional so that they issue back to back (a load under a branch
+  // waits for the previous one): a row index past the group is clamped to the
+  // group's last row, whose repeat leaves min and max unchanged, and a column past
+  // N to the last column, whose lanes never store.
+  const int cc = cvalid ? c : N8 - 1;
   u32x4 buf[CACHE];
   for (int base = slice; base < g; base += S * CACHE) {
 #pragma unroll
     for (int i = 0; i < CACHE; ++i) {
-      const int r = base + S * i;
-      if (cvalid && r < g) buf[i] = w[(row0 + r) * N8 + c];
+      const int r = min(base + S * i, g - 1);
+      buf[i] = w[(row0 + r) * N8 + cc];
     }
 #pragma unroll
-    for (int i = 0; i < CACHE; ++i)
-      if (cvalid && base + S * i < g) accumulate(st, buf[i]);
+    for (int i = 0; i + 1 < CACHE; i += 2) accumulate2(st, buf[i], buf[i + 1]);
+    if constexpr (CACHE % 2 == 1) accumulate(st, buf[CACHE - 1]);
   }
 
   // Min / max across the row slices of a wave (lanes cl, cl + CL, ...), then across waves.
 #pragma unroll
   for (int off = CL; off < 64; off <<= 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      st.mn[j] = fminf(st.mn[j], __shfl_xor(st.mn[j], off));
-      st.mx[j] = fmaxf(st.mx[j], __shfl_xor(st.mx[j], off));
+    for (int p = 0; p < 4; ++p) {
+      st.mn[p] = hmin2(st.mn[p], as_h2(__shfl_xor(as_u32(st.mn[p]), off)));
+      st.mx[p] = hmax2(st.mx[p], as_h2(__shfl_xor(as_u32(st.mx[p]), off)));
     }
   }
   if (lane < CL) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      red[0][wave][cl][j] = st.mn[j];
-      red[1][wave][cl][j] = st.mx[j];
-    }
+    red[0][wave][cl] = u32x4{as_u32(st.mn[0]), as_u32(st.mn[1]), as_u32(st.mn[2]), as_u32(st.mn[3])};
+    red[1][wave][cl] = u32x4{as_u32(st.mx[0]), as_u32(st.mx[1]), as_u32(st.mx[2]), as_u32(st.mx[3])};
   }
   __syncthreads();
-  float mn[8], mx[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    mn[j] = red[0][0][cl][j];
-    mx[j] = red[1][0][cl][j];
-  }
+  u32x4 mnw = red[0][0][cl], mxw = red[1][0][cl];
 #pragma unroll
   for (int v = 1; v < WAVES; ++v) {
+    const u32x4 a = red[0][v][cl], b = red[1][v][cl];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      mn[j] = fminf(mn[j], red[0][v][cl][j]);
-      mx[j] = fmaxf(mx[j], red[1][v][cl][j]);
+    for (int p = 0; p < 4; ++p) {
+      mnw[p] = as_u32(hmin2(as_h2(mnw[p]), as_h2(a[p])));
+      mxw[p] = as_u32(hmax2(as_h2(mxw[p]), as_h2(b[p])));
     }
   }
   if (!cvalid) return;
 
-  float sf[8], zf[8];
+  float sf[8], rf[8], zf[8], mzf[8];
   uint32_t zword = 0;
   u32x4 sbits;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float s32;
-    if (sym) {
-      s32 = fmaxf(fmaxf(mx[j], -mn[j]), 1e-5f) / 7.0f;
-    } else {
-      s32 = fmaxf(mx[j] - mn[j], 1e-5f) / 15.0f;
-    }
+    const float mn = col_of(mnw, j), mx = col_of(mxw, j);
+    const float s32 = sym ? fmaxf(fmaxf(mx, -mn), 1e-5f) / 7.0f : fmaxf(mx - mn, 1e-5f) / 15.0f;
     const _Float16 s16 = (_Float16)s32;  // the stored scale, rounded once
     sf[j] = (float)s16;
-    zf[j] = sym ? 8.0f : fminf(fmaxf(-rintf(mn[j] / sf[j]), 0.0f), 15.0f);
-    zword |= (uint32_t)(int)zf[j] << (4 * nibble_of_col(j));
+    rf[j] = __builtin_amdgcn_rcpf(sf[j]);
+    zf[j] = sym ? 8.0f : __builtin_amdgcn_fmed3f(-rintf(mn / sf[j]), 0.0f, 15.0f);
+    mzf[j] = kMagic + zf[j];
+    zword |= (uint32_t)zf[j] << (4 * nibble_of_col(j));
     const uint32_t b = __builtin_bit_cast(uint16_t, s16);
     if (j & 1) sbits[j >> 1] |= b << 16;
     else sbits[j >> 1] = b;
@@ -160,29 +205,59 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
     scales[(int64_t)grp * N8 + c] = sbits;
   }
 
-  const bool s = sym != 0;
   if (resident) {
+    uint32_t redo = 0;  // rows i whose fast codes must be recomputed exactly
 #pragma unroll
     for (int i = 0; i < CACHE; ++i) {
       const int r = slice + S * i;
-      if (r < g) qweight[(row0 + r) * N8 + c] = code_word(buf[i], sf, zf, s);
+      bool near = false;
+      const uint32_t word = code_word_fast(buf[i], rf, mzf, near);
+      if (r < g) {
+        qweight[(row0 + r) * N8 + c] = word;
+        redo |= (uint32_t)near << i;
+      }
+    }
+    // Rare: the row is read again (an L2 hit) so that buf needs no runtime index;
+    // the exact word overwrites the fast one written above by this same thread.
+    while (redo) {
+      const int i = __builtin_ctz(redo);
+      redo &= redo - 1;
+      const int64_t idx = (row0 + slice + S * i) * N8 + c;
+      qweight[idx] = code_word_exact(w[idx], sf, zf);
     }
   } else {
-    for (int r = slice; r < g; r += S) qweight[(row0 + r) * N8 + c] = code_word(w[(row0 + r) * N8 + c], sf, zf, s);
+    for (int r = slice; r < g; r += S) {
+      const int64_t idx = (row0 + r) * N8 + c;
+      const u32x4 v = w[idx];
+      bool near = false;
+      const uint32_t word = code_word_fast(v, rf, mzf, near);
+      qweight[idx] = near ? code_word_exact(v, sf, zf) : word;
+    }
   }
 }
 
 namespace {
-constexpr int kSmallCL = 64, kSmallWaves = 4, kSmallCache = 32;  // groups of up to 128 rows
-constexpr int kLargeCL = 8, kLargeWaves = 8, kLargeCache = 16;   // resident up to 1024 rows
+// Groups of up to 128 rows: 4 waves of 4 row slices x 16 word columns (256-byte row
+// runs), CACHE = ceil(g / 16) rows per thread rounded up to a power of two.  Longer
+// groups: 8 waves of 8 row slices x 8 word columns, 16 rows per thread resident
+// (groups up to 1024 rows), otherwise read twice.
+constexpr int kSmallCL = 16, kSmallWaves = 4;
+constexpr int kSmallS = kSmallWaves * (64 / kSmallCL);
+constexpr int kLargeCL = 8, kLargeWaves = 8, kLargeCache = 16;
 }  // namespace
 
 int rtn_plan(int g, int N, int* block, int* cols_per_block) {
-  const bool small = g <= kSmallWaves * (64 / kSmallCL) * kSmallCache;
+  (void)N;
+  int variant;
+  if (g <= kSmallS) variant = 0;
+  else if (g <= 2 * kSmallS) variant = 1;
+  else if (g <= 4 * kSmallS) variant = 2;
+  else if (g <= 8 * kSmallS) variant = 3;
+  else variant = 4;
+  const bool small = variant < 4;
   *block = 64 * (small ? kSmallWaves : kLargeWaves);
   *cols_per_block = 8 * (small ? kSmallCL : kLargeCL);
-  (void)N;
-  return small ? 0 : 1;
+  return variant;
 }
 
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
@@ -191,17 +266,34 @@ hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym,
   const int variant = rtn_plan(g, N, &block, &cols);
   const int N8 = N / 8;
   const int ncb = (N + cols - 1) / cols;
-  const int64_t blocks = (int64_t)(K / g) * ncb;
+  const dim3 grid((unsigned)((int64_t)(K / g) * ncb));
   const auto* src = reinterpret_cast<const u32x4*>(w);
   auto* qw = reinterpret_cast<uint32_t*>(qweight);
   auto* qz = reinterpret_cast<uint32_t*>(qzeros);
   auto* sc = reinterpret_cast<u32x4*>(scales);
-  if (variant == 0)
-    hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, kSmallCache>), dim3((unsigned)blocks), dim3(block), 0,
-                       stream, src, K, N8, g, ncb, (int)sym, qw, qz, sc);
-  else
-    hipLaunchKernelGGL((rtn_kernel<kLargeCL, kLargeWaves, kLargeCache>), dim3((unsigned)blocks), dim3(block), 0,
-                       stream, src, K, N8, g, ncb, (int)sym, qw, qz, sc);
+  const int sy = sym ? 1 : 0;
+  switch (variant) {
+    case 0:
+      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 1>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
+                         sy, qw, qz, sc);
+      break;
+    case 1:
+      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 2>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
+                         sy, qw, qz, sc);
+      break;
+    case 2:
+      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 4>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
+                         sy, qw, qz, sc);
+      break;
+    case 3:
+      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 8>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
+                         sy, qw, qz, sc);
+      break;
+    default:
+      hipLaunchKernelGGL((rtn_kernel<kLargeCL, kLargeWaves, kLargeCache>), grid, dim3(block), 0, stream, src, K,
+                         N8, g, ncb, sy, qw, qz, sc);
+      break;
+  }
   return hipGetLastError();
 }
 
