@@ -163,6 +163,11 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
  *   sym          0 or 1
  *   qweight      device int32 [K, N/8];  qzeros int32 [G, N/8];  scales_f16 fp16 [G, N];
  *                all written in full
+ * Groups of up to 256 rows are quantised in one pass over w.  Longer groups
+ * (including group_size == -1 on K > 256) read w twice and keep per-chunk minima
+ * and maxima (K/128 x N x 4 bytes) in the same library-owned per-(device, stream)
+ * workspace awq_gemm uses, with the same allocation rule: the first call that needs
+ * a larger buffer allocates it and synchronises the stream.
  * Returns AWQ_OK or an error status (nothing enqueued on error).
  */
 int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size, int sym,

@@ -39,8 +39,9 @@ def run_both(W: np.ndarray, g: int, sym: bool, label: str):
 
 
 SHAPES = [
-    # (K, N, group_size): small-group variant (g <= 128), long groups resident in
-    # registers (129..1024 rows), longer ones read twice; ragged column blocks.
+    # (K, N, group_size): groups of up to 256 rows in one fused pass (1..16 rows per
+    # thread), longer groups in two passes over 128-row chunks (ragged last chunk
+    # for 288, 500, 1000 and 3000 rows); N not a multiple of the 128-column block.
     (128, 512, 128),
     (4096, 4096, 128),
     (4096, 1024, 64),
@@ -53,6 +54,8 @@ SHAPES = [
     (4096, 512, -1),
     (3000, 128, -1),
     (1000, 40, 500),
+    (600, 64, 200),
+    (864, 24, 288),
 ]
 
 

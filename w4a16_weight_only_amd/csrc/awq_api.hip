@@ -214,6 +214,19 @@ int get_workspace(const Plan& p, hipStream_t stream, uint64_t** accum, float** p
   return AWQ_OK;
 }
 
+// Scratch that is fully written before it is read within one call: the partial
+// buffer of the same (device, stream) workspace.
+int get_scratch(int64_t bytes, hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& ws = g_ws[{dev, stream}];
+  const int st = ensure(ws.partial, bytes, false, stream);
+  if (st != AWQ_OK) return st;
+  *out = ws.partial.ptr;
+  return AWQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,14 +312,18 @@ int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size
   if (sym != 0 && sym != 1) return AWQ_ERR_SHAPE;
   if (K > kMaxDim || N > kMaxDim) return AWQ_ERR_UNSUPPORTED;
   const int g = eff_group(K, group_size);
-  int block, cols;
-  awq::rtn_plan(g, (int)N, &block, &cols);
-  if ((K / g) * ((N + cols - 1) / cols) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  const awq::RtnPlan p = awq::rtn_plan(K, N, g);
+  if (p.grid >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
   if (!w_f16 || !qweight || !qzeros || !scales_f16) return AWQ_ERR_NULL;
   if (!aligned16(w_f16) || !aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16))
     return AWQ_ERR_ALIGN;
+  void* scratch = nullptr;
+  if (p.scratch_bytes > 0) {
+    st = get_scratch(p.scratch_bytes, stream, &scratch);
+    if (st != AWQ_OK) return st;
+  }
   hipError_t e = awq::launch_quantize_rtn(static_cast<const uint16_t*>(w_f16), (int)K, (int)N, g, sym != 0, qweight,
-                                          qzeros, static_cast<uint16_t*>(scales_f16), stream);
+                                          qzeros, static_cast<uint16_t*>(scales_f16), scratch, stream);
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
 }
 

@@ -46,11 +46,18 @@ hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const u
                           int K, int N, int g, void* out, bool f16, hipStream_t stream);
 
 // RTN writer: fp16 w [K, N] -> qweight [K, N/8], qzeros [K/g, N/8], scales fp16 [K/g, N].
-// rtn_plan reports the variant (0: groups of up to 128 rows, 1: longer groups), the
-// block size and the output columns one workgroup covers.
-int rtn_plan(int g, int N, int* block, int* cols_per_block);
+// Groups of up to 256 rows take one fused pass (cache = rows per thread); longer
+// groups take two passes over chunks of 128 rows (cpg chunks per group) and need
+// scratch_bytes of device scratch for the chunks' min / max, fully written by the
+// first pass before the second reads it.  grid = workgroups per launch.
+struct RtnPlan {
+  int cache = 1, block = 0, cols = 0, cpg = 1;
+  bool two_pass = false;
+  int64_t grid = 0, scratch_bytes = 0;
+};
+RtnPlan rtn_plan(int64_t K, int64_t N, int g);
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
-                               int32_t* qzeros, uint16_t* scales, hipStream_t stream);
+                               int32_t* qzeros, uint16_t* scales, void* scratch, hipStream_t stream);
 
 // With p.splits > 1: 4-wave plans use accum, [n_tiles][mrows * 256] 64-bit
 // accumulators that are zero before the call and left zero by it; 8-wave plans use

@@ -110,16 +110,25 @@ __device__ __forceinline__ uint32_t code_word_fast(const u32x4& v, const float r
 
 }  // namespace
 
-// CL word columns per wave, WAVES waves per workgroup, CACHE rows kept in registers
-// per thread.  Workgroup b handles group b / ncb and word columns
-// (b % ncb) * CL .. + CL - 1.
-template <int CL, int WAVES, int CACHE>
-__global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict__ w, int K, int N8, int g,
+// Work item = (span of rows, block of CL word columns).  A span is a whole group
+// (kFused) or one chunk of up to S * CACHE rows of a group (kStats, kCode; cpg
+// chunks per group).  Workgroup b takes item b / ncb and word columns
+// (b % ncb) * CL .. + CL - 1; CACHE rows per thread stay in registers.
+//   kFused  min / max of the group, then scales, zeros and codes: one pass.
+//   kStats  min / max of the chunk, stored to part (packed fp16, 2 x 16 bytes per
+//           word column and chunk: part[(item * 2 + {0: min, 1: max}) * N8 + c]).
+//   kCode   min / max of the group from its chunks' part entries, then scales and
+//           zeros (first chunk only) and the chunk's codes.
+enum RtnMode { kFused = 0, kStats = 1, kCode = 2 };
+
+template <int CL, int WAVES, int CACHE, int MODE>
+__global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict__ w, int N8, int g, int cpg,
                                                         int ncb, int sym, uint32_t* __restrict__ qweight,
-                                                        uint32_t* __restrict__ qzeros,
-                                                        u32x4* __restrict__ scales) {
+                                                        uint32_t* __restrict__ qzeros, u32x4* __restrict__ scales,
+                                                        u32x4* __restrict__ part) {
   constexpr int RL = 64 / CL;     // row slices per wave
   constexpr int S = WAVES * RL;   // row slices per workgroup
+  constexpr int CH = S * CACHE;   // rows per chunk (kStats, kCode)
   __shared__ u32x4 red[2][WAVES][CL];  // per-wave min / max, packed fp16
 
   const int tid = threadIdx.x;
@@ -127,61 +136,84 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
   const int wave = tid >> 6;
   const int cl = lane % CL;
   const int slice = wave * RL + lane / CL;
-  const int grp = blockIdx.x / ncb;
+  const int item = blockIdx.x / ncb;
+  const int grp = item / cpg;
+  const int chunk = item - grp * cpg;
   const int c = (blockIdx.x % ncb) * CL + cl;
   const bool cvalid = c < N8;
-  const int64_t row0 = (int64_t)grp * g;
-  const bool resident = g <= S * CACHE;
+  const int rows = MODE == kFused ? g : min(CH, g - chunk * CH);  // 1 <= rows <= S * CACHE
+  const int64_t row0 = (int64_t)grp * g + (int64_t)chunk * CH;
 
-  PairStats st;
-  const _Float16 inf = (_Float16)__builtin_inff();
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    st.mn[p] = half2v{inf, inf};
-    st.mx[p] = half2v{-inf, -inf};
-  }
   // Loads are unconditional so that they issue back to back (a load under a branch
-  // waits for the previous one): a row index past the group is clamped to the
-  // group's last row, whose repeat leaves min and max unchanged, and a column past
+  // waits for the previous one): a row index past the span is clamped to the
+  // span's last row, whose repeat leaves min and max unchanged, and a column past
   // N to the last column, whose lanes never store.
   const int cc = cvalid ? c : N8 - 1;
   u32x4 buf[CACHE];
-  for (int base = slice; base < g; base += S * CACHE) {
 #pragma unroll
-    for (int i = 0; i < CACHE; ++i) {
-      const int r = min(base + S * i, g - 1);
-      buf[i] = w[(row0 + r) * N8 + cc];
+  for (int i = 0; i < CACHE; ++i) buf[i] = w[(row0 + min(slice + S * i, rows - 1)) * N8 + cc];
+
+  u32x4 mnw, mxw;
+  if constexpr (MODE == kCode) {
+    const _Float16 inf = (_Float16)__builtin_inff();
+    const uint32_t pinf = as_u32(half2v{inf, inf}), ninf = as_u32(half2v{-inf, -inf});
+    mnw = u32x4{pinf, pinf, pinf, pinf};
+    mxw = u32x4{ninf, ninf, ninf, ninf};
+    const u32x4* pg = part + (int64_t)grp * cpg * 2 * N8 + cc;
+    for (int k = 0; k < cpg; ++k) {
+      const u32x4 a = pg[(int64_t)(2 * k) * N8], b = pg[(int64_t)(2 * k + 1) * N8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        mnw[p] = as_u32(hmin2(as_h2(mnw[p]), as_h2(a[p])));
+        mxw[p] = as_u32(hmax2(as_h2(mxw[p]), as_h2(b[p])));
+      }
+    }
+  } else {
+    PairStats st;
+    const _Float16 inf = (_Float16)__builtin_inff();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      st.mn[p] = half2v{inf, inf};
+      st.mx[p] = half2v{-inf, -inf};
     }
 #pragma unroll
     for (int i = 0; i + 1 < CACHE; i += 2) accumulate2(st, buf[i], buf[i + 1]);
     if constexpr (CACHE % 2 == 1) accumulate(st, buf[CACHE - 1]);
-  }
 
-  // Min / max across the row slices of a wave (lanes cl, cl + CL, ...), then across waves.
+    // Min / max across the row slices of a wave (lanes cl, cl + CL, ...), then across waves.
 #pragma unroll
-  for (int off = CL; off < 64; off <<= 1) {
+    for (int off = CL; off < 64; off <<= 1) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      st.mn[p] = hmin2(st.mn[p], as_h2(__shfl_xor(as_u32(st.mn[p]), off)));
-      st.mx[p] = hmax2(st.mx[p], as_h2(__shfl_xor(as_u32(st.mx[p]), off)));
+      for (int p = 0; p < 4; ++p) {
+        st.mn[p] = hmin2(st.mn[p], as_h2(__shfl_xor(as_u32(st.mn[p]), off)));
+        st.mx[p] = hmax2(st.mx[p], as_h2(__shfl_xor(as_u32(st.mx[p]), off)));
+      }
     }
-  }
-  if (lane < CL) {
-    red[0][wave][cl] = u32x4{as_u32(st.mn[0]), as_u32(st.mn[1]), as_u32(st.mn[2]), as_u32(st.mn[3])};
-    red[1][wave][cl] = u32x4{as_u32(st.mx[0]), as_u32(st.mx[1]), as_u32(st.mx[2]), as_u32(st.mx[3])};
-  }
-  __syncthreads();
-  u32x4 mnw = red[0][0][cl], mxw = red[1][0][cl];
+    if (lane < CL) {
+      red[0][wave][cl] = u32x4{as_u32(st.mn[0]), as_u32(st.mn[1]), as_u32(st.mn[2]), as_u32(st.mn[3])};
+      red[1][wave][cl] = u32x4{as_u32(st.mx[0]), as_u32(st.mx[1]), as_u32(st.mx[2]), as_u32(st.mx[3])};
+    }
+    __syncthreads();
+    mnw = red[0][0][cl];
+    mxw = red[1][0][cl];
 #pragma unroll
-  for (int v = 1; v < WAVES; ++v) {
-    const u32x4 a = red[0][v][cl], b = red[1][v][cl];
+    for (int v = 1; v < WAVES; ++v) {
+      const u32x4 a = red[0][v][cl], b = red[1][v][cl];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      mnw[p] = as_u32(hmin2(as_h2(mnw[p]), as_h2(a[p])));
-      mxw[p] = as_u32(hmax2(as_h2(mxw[p]), as_h2(b[p])));
+      for (int p = 0; p < 4; ++p) {
+        mnw[p] = as_u32(hmin2(as_h2(mnw[p]), as_h2(a[p])));
+        mxw[p] = as_u32(hmax2(as_h2(mxw[p]), as_h2(b[p])));
+      }
     }
   }
   if (!cvalid) return;
+  if constexpr (MODE == kStats) {
+    if (slice == 0) {
+      part[(int64_t)(2 * item) * N8 + c] = mnw;
+      part[(int64_t)(2 * item + 1) * N8 + c] = mxw;
+    }
+    return;
+  }
 
   float sf[8], rf[8], zf[8], mzf[8];
   uint32_t zword = 0;
@@ -200,99 +232,96 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
     if (j & 1) sbits[j >> 1] |= b << 16;
     else sbits[j >> 1] = b;
   }
-  if (slice == 0) {
+  if (slice == 0 && chunk == 0) {
     qzeros[(int64_t)grp * N8 + c] = zword;
     scales[(int64_t)grp * N8 + c] = sbits;
   }
 
-  if (resident) {
-    uint32_t redo = 0;  // rows i whose fast codes must be recomputed exactly
+  uint32_t redo = 0;  // rows i whose fast codes must be recomputed exactly
 #pragma unroll
-    for (int i = 0; i < CACHE; ++i) {
-      const int r = slice + S * i;
-      bool near = false;
-      const uint32_t word = code_word_fast(buf[i], rf, mzf, near);
-      if (r < g) {
-        qweight[(row0 + r) * N8 + c] = word;
-        redo |= (uint32_t)near << i;
-      }
+  for (int i = 0; i < CACHE; ++i) {
+    const int r = slice + S * i;
+    bool near = false;
+    const uint32_t word = code_word_fast(buf[i], rf, mzf, near);
+    if (r < rows) {
+      qweight[(row0 + r) * N8 + c] = word;
+      redo |= (uint32_t)near << i;
     }
-    // Rare: the row is read again (an L2 hit) so that buf needs no runtime index;
-    // the exact word overwrites the fast one written above by this same thread.
-    while (redo) {
-      const int i = __builtin_ctz(redo);
-      redo &= redo - 1;
-      const int64_t idx = (row0 + slice + S * i) * N8 + c;
-      qweight[idx] = code_word_exact(w[idx], sf, zf);
-    }
-  } else {
-    for (int r = slice; r < g; r += S) {
-      const int64_t idx = (row0 + r) * N8 + c;
-      const u32x4 v = w[idx];
-      bool near = false;
-      const uint32_t word = code_word_fast(v, rf, mzf, near);
-      qweight[idx] = near ? code_word_exact(v, sf, zf) : word;
-    }
+  }
+  // Rare: the row is read again (an L2 hit) so that buf needs no runtime index;
+  // the exact word overwrites the fast one written above by this same thread.
+  while (redo) {
+    const int i = __builtin_ctz(redo);
+    redo &= redo - 1;
+    const int64_t idx = (row0 + slice + S * i) * N8 + c;
+    qweight[idx] = code_word_exact(w[idx], sf, zf);
   }
 }
 
 namespace {
-// Groups of up to 128 rows: 4 waves of 4 row slices x 16 word columns (256-byte row
-// runs), CACHE = ceil(g / 16) rows per thread rounded up to a power of two.  Longer
-// groups: 8 waves of 8 row slices x 8 word columns, 16 rows per thread resident
-// (groups up to 1024 rows), otherwise read twice.
-constexpr int kSmallCL = 16, kSmallWaves = 4;
-constexpr int kSmallS = kSmallWaves * (64 / kSmallCL);
-constexpr int kLargeCL = 8, kLargeWaves = 8, kLargeCache = 16;
+// 4 waves of 4 row slices x 16 word columns: every row load is a 256-byte run.
+constexpr int kCL = 16, kWaves = 4;
+constexpr int kS = kWaves * (64 / kCL);  // row slices per workgroup
+constexpr int kMaxFusedCache = 16;       // fused pass for groups of up to 256 rows
+constexpr int kChunkCache = 8;           // longer groups: chunks of 128 rows
 }  // namespace
 
-int rtn_plan(int g, int N, int* block, int* cols_per_block) {
-  (void)N;
-  int variant;
-  if (g <= kSmallS) variant = 0;
-  else if (g <= 2 * kSmallS) variant = 1;
-  else if (g <= 4 * kSmallS) variant = 2;
-  else if (g <= 8 * kSmallS) variant = 3;
-  else variant = 4;
-  const bool small = variant < 4;
-  *block = 64 * (small ? kSmallWaves : kLargeWaves);
-  *cols_per_block = 8 * (small ? kSmallCL : kLargeCL);
-  return variant;
+RtnPlan rtn_plan(int64_t K, int64_t N, int g) {
+  RtnPlan p;
+  p.block = 64 * kWaves;
+  p.cols = 8 * kCL;
+  const int64_t ncb = (N + p.cols - 1) / p.cols;
+  const int64_t G = K / g;
+  if (g <= kS * kMaxFusedCache) {
+    int cache = 1;
+    while (kS * cache < g) cache *= 2;
+    p.cache = cache;
+    p.two_pass = false;
+    p.cpg = 1;
+    p.scratch_bytes = 0;
+  } else {
+    p.cache = kChunkCache;
+    p.two_pass = true;
+    p.cpg = (g + kS * kChunkCache - 1) / (kS * kChunkCache);
+    p.scratch_bytes = G * p.cpg * 2 * (N / 8) * 16;
+  }
+  p.grid = G * p.cpg * ncb;
+  return p;
 }
 
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
-                               int32_t* qzeros, uint16_t* scales, hipStream_t stream) {
-  int block, cols;
-  const int variant = rtn_plan(g, N, &block, &cols);
+                               int32_t* qzeros, uint16_t* scales, void* scratch, hipStream_t stream) {
+  const RtnPlan p = rtn_plan(K, N, g);
   const int N8 = N / 8;
-  const int ncb = (N + cols - 1) / cols;
-  const dim3 grid((unsigned)((int64_t)(K / g) * ncb));
+  const int ncb = (N + p.cols - 1) / p.cols;
+  const dim3 grid((unsigned)p.grid), block(p.block);
   const auto* src = reinterpret_cast<const u32x4*>(w);
   auto* qw = reinterpret_cast<uint32_t*>(qweight);
   auto* qz = reinterpret_cast<uint32_t*>(qzeros);
   auto* sc = reinterpret_cast<u32x4*>(scales);
+  auto* part = static_cast<u32x4*>(scratch);
   const int sy = sym ? 1 : 0;
-  switch (variant) {
-    case 0:
-      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 1>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
-                         sy, qw, qz, sc);
-      break;
-    case 1:
-      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 2>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
-                         sy, qw, qz, sc);
-      break;
-    case 2:
-      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 4>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
-                         sy, qw, qz, sc);
-      break;
-    case 3:
-      hipLaunchKernelGGL((rtn_kernel<kSmallCL, kSmallWaves, 8>), grid, dim3(block), 0, stream, src, K, N8, g, ncb,
-                         sy, qw, qz, sc);
-      break;
+  if (p.two_pass) {
+    hipLaunchKernelGGL((rtn_kernel<kCL, kWaves, kChunkCache, kStats>), grid, block, 0, stream, src, N8, g, p.cpg,
+                       ncb, sy, qw, qz, sc, part);
+    hipLaunchKernelGGL((rtn_kernel<kCL, kWaves, kChunkCache, kCode>), grid, block, 0, stream, src, N8, g, p.cpg,
+                       ncb, sy, qw, qz, sc, part);
+    return hipGetLastError();
+  }
+  switch (p.cache) {
+#define AWQ_RTN_FUSED(C)                                                                                    \
+  case C:                                                                                                   \
+    hipLaunchKernelGGL((rtn_kernel<kCL, kWaves, C, kFused>), grid, block, 0, stream, src, N8, g, 1, ncb, sy, \
+                       qw, qz, sc, part);                                                                   \
+    break;
+    AWQ_RTN_FUSED(1)
+    AWQ_RTN_FUSED(2)
+    AWQ_RTN_FUSED(4)
+    AWQ_RTN_FUSED(8)
+    AWQ_RTN_FUSED(16)
+#undef AWQ_RTN_FUSED
     default:
-      hipLaunchKernelGGL((rtn_kernel<kLargeCL, kLargeWaves, kLargeCache>), grid, dim3(block), 0, stream, src, K,
-                         N8, g, ncb, sy, qw, qz, sc);
-      break;
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
