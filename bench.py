@@ -386,7 +386,8 @@ def main():
         # The RTN writer (fp16 weight -> GEMM pack), HBM-bound.
         out["writer"] = [time_quantize_rtn(K, N, g, sym, min(args.steps, 100), torch, awq, synth)
                          for (K, N, g, sym) in ((4096, 4096, 128, False), (4096, 4096, 128, True),
-                                                (4096, 14336, 128, False), (4096, 4096, -1, False))]
+                                                (4096, 14336, 128, False), (4096, 4096, -1, False),
+                                                (11008, 4096, 256, False))]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, synth)
     print(json.dumps(out), flush=True)
