@@ -134,7 +134,6 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
     }
   } else {
     p.family = 1;
-    p.block = awq::kTileThreads;
     auto tiles = [&](int v) {
       return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
     };
@@ -154,6 +153,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
     const int64_t kps = (KT + splits - 1) / splits;
     splits = (KT + kps - 1) / kps;
     p.tp.variant = v;
+    p.block = awq::kTileThreads[v];
     p.tp.splits = (int)splits;
     p.tp.kps = (int)kps;
     p.grid_x = (int)tiles(v);

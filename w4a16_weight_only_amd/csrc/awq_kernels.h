@@ -26,14 +26,14 @@ struct SkinnyPlan {
   bool single_group; // every wave's k-steps lie in one quantization group
 };
 
-// MFMA tile family: 4 waves per workgroup.  Variants (rows x columns per workgroup):
-// 0: 256 x 128, 1: 128 x 64, 2: 64 x 128.  With splits > 1 each workgroup covers kps
-// k-tiles of 64 and writes fp32 sums to partial, [splits][M][N]; a second kernel
-// adds the splits and the bias.
-constexpr int kTileThreads = 256;
+// MFMA tile family.  Variants (rows x columns per workgroup, threads):
+// 0: 256 x 128 (512: two k-groups of 4 waves), 1: 128 x 64 (256), 2: 64 x 128 (256).
+// With splits > 1 each workgroup covers kps k-tiles of 64 and writes fp32 sums to
+// partial, [splits][M][N]; a second kernel adds the splits and the bias.
 constexpr int kTileVariants = 3;
 constexpr int kTileBM[kTileVariants] = {256, 128, 64};
 constexpr int kTileBN[kTileVariants] = {128, 64, 128};
+constexpr int kTileThreads[kTileVariants] = {512, 256, 256};
 constexpr int kTileBK = 64;
 struct TilePlan {
   int variant;

@@ -40,9 +40,6 @@
 #include "awq_device.h"
 #include "awq_kernels.h"
 
-#ifndef TILE0_KG
-#define TILE0_KG 2
-#endif
 
 namespace awq {
 
@@ -234,11 +231,14 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint32_t* gz = reinterpret_cast<const uint32_t*>(&Gs[buf][h * GP]);
     const _Float16* gs = reinterpret_cast<const _Float16*>(&Gs[buf][h * GP + ZP]);
     const uint32_t zw = gz[wloc];
+    // Loads first, then a select: a conditional load would split the loop body.
+    const _Float16 s0v = gs[c0];
     off0 = splat(-(zbase + (_Float16)(float)((zw >> (4 * p0)) & 0xFu)));
-    sc0 = splat(keep ? gs[c0] : (_Float16)0.f);
+    sc0 = splat(keep ? s0v : (_Float16)0.f);
     if (FN == 2) {
+      const _Float16 s1v = gs[c1];
       off1 = splat(-(zbase + (_Float16)(float)((zw >> (4 * (p0 + 4))) & 0xFu)));
-      sc1 = splat(keep ? gs[c1] : (_Float16)0.f);
+      sc1 = splat(keep ? s1v : (_Float16)0.f);
     }
   };
 
@@ -338,10 +338,96 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) load_tile(t, kofs(t));
   barrier_keep_last();
-  for (int kt = 0; kt < KT; ++kt) {
-    load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
-    run(kt % kStages, kt0 + kt == KT_all - 1 && K % kBK != 0);
-    barrier_keep_last();
+  if constexpr (KG == 2) {
+    // Software-pipelined k loop: a wave's share of a k-tile is two k16 steps of one
+    // 32-row half (kh = kg), with that half's group data.  The B operand of the next
+    // step is dequantised while the MFMAs of the current one run, across the barrier
+    // too: the barrier sits between the two steps, because a buffer only has to stay
+    // intact until its fragments are in registers.  Per k-tile t:
+    //   issue the direct loads of k-tile t + kStages - 1 (into the buffer of k-tile
+    //     t - 1, whose fragments every wave read before the previous barrier);
+    //   MFMAs of step 0 of t, interleaved with the dequant of step 1 of t;
+    //   barrier (k-tile t + 1 has landed);
+    //   read the fragments and group data of k-tile t + 1;
+    //   MFMAs of step 1 of t, interleaved with the dequant of step 0 of t + 1.
+    // After the last k-tile the reads of "k-tile KT" hit the clamped re-load of the
+    // last one (valid data); what is dequantised from them is never multiplied.
+    const int kh = kg;
+    auto keep_of = [&](int t) { return !(kt0 + t == KT_all - 1 && K % kBK != 0) || kh == part_half; };
+    auto read_a = [&](half8v(&a)[FM], int buf, int s) {
+      const int k = 16 * s + 32 * kh + kq;
+      const int pos = (k >> 3) ^ rx;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const half8v*>(&As[buf][(wm * 32 * FM + 32 * i + lc) * kBK + 8 * pos]);
+    };
+    auto read_w = [&](u32x4& wlo, u32x4& whi, int buf, int s) {
+      const int k = 16 * s + 32 * kh + kq;
+      const uint32_t* brow = &Bs[buf][k * BW + (((wloc >> 2) ^ swz(k)) << 2) + (wloc & 3)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wlo[j] = brow[j * BW];
+        whi[j] = brow[(4 + j) * BW];
+      }
+    };
+    auto dequant = [&](const u32x4& wlo, const u32x4& whi, half8v(&bf)[2]) {
+      const uint32_t w[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
+      half2v h0[4], h1[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
+        h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
+        h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
+      }
+      bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
+      bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+    };
+    auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+    // One MFMA, then a few VALU instructions, FM * FN times: the dequant issues while
+    // the matrix core works.
+    auto interleave = [] {
+#pragma unroll
+      for (int i = 0; i < FM * FN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      }
+    };
+    static_assert(FN == 2, "the pipelined loop dequantises two N-tiles per step");
+    half8v a0[FM], a1[FM], b0[2], b1[2];
+    u32x4 w0lo, w0hi, w1lo, w1hi;
+    read_a(a0, 0, 0);
+    read_w(w0lo, w0hi, 0, 0);
+    read_w(w1lo, w1hi, 0, 1);
+    apply_group(0, kh, keep_of(0));
+    dequant(w0lo, w0hi, b0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt % kStages, nbuf = (kt + 1) % kStages;
+      load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
+      read_a(a1, buf, 1);
+      mfma_step(a0, b0);
+      dequant(w1lo, w1hi, b1);
+      interleave();
+      barrier_keep_last();
+      read_a(a0, nbuf, 0);
+      read_w(w0lo, w0hi, nbuf, 0);
+      read_w(w1lo, w1hi, nbuf, 1);
+      apply_group(nbuf, kh, keep_of(kt + 1));
+      mfma_step(a1, b1);
+      dequant(w0lo, w0hi, b0);
+      interleave();
+    }
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
+      run(kt % kStages, kt0 + kt == KT_all - 1 && K % kBK != 0);
+      barrier_keep_last();
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the clamped extra loads have landed too
   __syncthreads();  // every wave is done with the buffers
@@ -485,7 +571,7 @@ hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t*
                        split ? partial : nullptr, reinterpret_cast<_Float16*>(y));
   };
   switch (p.variant) {
-    case 0: go(tile_kernel<4, 2, 2, TILE0_KG>, 256, 128, 256 * TILE0_KG); break;
+    case 0: go(tile_kernel<4, 2, 2, 2>, 256, 128, 512); break;
     case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64, 256); break;
     default: go(tile_kernel<2, 1, 1, 1>, 64, 128, 256); break;
   }
