@@ -5,10 +5,11 @@
 // section 1.2: large batches are compute-bound, so the dequant work must hide under
 // the matrix products).
 //
-// Workgroup: 4 waves as 2 (M) x 2 (N); wave tile (32 FM) x (32 FN) of
-// v_mfma_f32_32x32x16_f16 accumulators.  Instantiations: FM = 4, FN = 2 (workgroup
-// 256 x 128) for large M, FM = 2, FN = 1 (128 x 64) when fewer rows would leave
-// compute units idle.
+// Workgroup: KG groups of 4 waves as WM (M) x 4/WM (N); wave tile (32 FM) x (32 FN)
+// of v_mfma_f32_32x32x16_f16 accumulators.  Instantiations: FM = 8, FN = 1, WM = 1,
+// KG = 2 (workgroup 256 x 128, 8 waves; each B column is dequantised by one wave of
+// a k-group) for large M; FM = 2, FN = 1 with 2 x 2 waves (128 x 64) or 1 x 4
+// (64 x 128) when fewer rows would leave compute units idle.
 //
 // Staging, per k-tile of 64 rows: two LDS buffers and two register sets in
 // ping-pong.  The global loads of k-tile t + 3 are issued right after k-tile t is
@@ -377,10 +378,12 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       for (int pr = 0; pr < 4; ++pr) {
         const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
         h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
-        h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
+        if constexpr (FN == 2)
+          h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
       }
       bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
-      bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+      if constexpr (FN == 2)
+        bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
     };
     auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
 #pragma unroll
@@ -398,7 +401,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
       }
     };
-    static_assert(FN == 2, "the pipelined loop dequantises two N-tiles per step");
     half8v a0[FM], a1[FM], b0[2], b1[2];
     u32x4 w0lo, w0hi, w1lo, w1hi;
     read_a(a0, 0, 0);
@@ -571,7 +573,7 @@ hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t*
                        split ? partial : nullptr, reinterpret_cast<_Float16*>(y));
   };
   switch (p.variant) {
-    case 0: go(tile_kernel<4, 2, 2, 2>, 256, 128, 512); break;
+    case 0: go(tile_kernel<8, 1, 1, 2>, 256, 128, 512); break;
     case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64, 256); break;
     default: go(tile_kernel<2, 1, 1, 1>, 64, 128, 256); break;
   }
