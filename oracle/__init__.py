@@ -7,4 +7,5 @@ from .awq_ref import (  # noqa: F401
     AWQ_ORDER, AWQ_REVERSE, AwqFormatError, resolve_groups, validate_pack,
     pack_awq, unpack_awq, unpack_awq_gather, dequant_ref, dequant_ref_T,
     gemm_ref, gemm_ref_entries, fp16_rne, quantize_rtn,
+    bf16_to_f64, f32_to_bf16_rne, gemm_ref_bf16,
 )

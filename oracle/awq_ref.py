@@ -240,6 +240,44 @@ def fp16_rne(a) -> np.ndarray:
     return np.asarray(a).astype(np.float16)
 
 
+# bfloat16 activations.  The GEMM kernel's declared contract takes FP16 or BF16
+# inputs ([GPTQM] "Selection and compatibility", kernel table).  bfloat16 is the
+# upper half of an IEEE binary32: sign, 8 exponent bits, 7 fraction bits.  numpy
+# has no bfloat16 type, so values travel as their 16-bit patterns (uint16).
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns: the pattern is the top half of a binary32."""
+    b = np.asarray(bits).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_rne(a) -> np.ndarray:
+    """Round binary32 values to bfloat16, nearest with ties to even, as bit patterns.
+
+    The 16 low bits are dropped after adding 0x7FFF plus the lowest kept bit: below
+    halfway the carry never reaches the kept bits, above it always does, and at
+    exactly halfway it does only when the kept value is odd.  Overflow of the
+    largest finite values goes to infinity through the exponent, as in IEEE.  NaN
+    inputs keep their sign and become the quiet NaN 0x7FC0."""
+    f = np.asarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint32) & np.uint32(0xFFFF)
+    nan = np.isnan(f)
+    sign = (u >> np.uint64(16)).astype(np.uint32) & np.uint32(0x8000)
+    r = np.where(nan, sign | np.uint32(0x7FC0), r)
+    return r.astype(np.uint16)
+
+
+def gemm_ref_bf16(x_bits, qweight, qzeros, scales, bias_bits, group_size) -> np.ndarray:
+    """gemm_ref with bfloat16 x and bias (bit patterns): both widen exactly to float64;
+    the weights are the same fp16-scaled dequant, and the product is float64."""
+    x = bf16_to_f64(x_bits)
+    bias = None if bias_bits is None else bf16_to_f64(bias_bits)
+    return gemm_ref(x, qweight, qzeros, scales, bias, group_size)
+
+
 def quantize_rtn(W, group_size: int, sym: bool = False):
     """Round-to-nearest writer: fp16 W [K, N] -> (qweight [K, N/8], qzeros [G, N/8],
     scales fp16 [G, N]) in the GEMM layout, so that dequant_ref gives back

@@ -280,6 +280,54 @@ def pin_fp16_rounding(o):
         assert np.isinf(o.fp16_rne(np.float32(65520.0)))  # halfway to 2^16 rounds to even: overflow
 
 
+def pin_bf16_conversion(o):
+    """bfloat16 = the top 16 bits of a binary32 (sign, 8 exponent bits, 7 fraction
+    bits).  Values below are built from that definition: 1.0 = 0x3F80 and the next
+    value up is 1 + 2^-7 = 0x3F81, so 1 + 2^-8 is a tie that goes to the even 0x3F80
+    and 1 + 3 * 2^-8 a tie that goes to the even 0x3F82; -2.5 = -1.25 * 2 = 0xC020;
+    the smallest subnormal 0x0001 is 2^-133; the largest finite 0x7F7F is
+    (2 - 2^-7) 2^127, and (2 - 2^-8) 2^127, halfway to 2^128, rounds to the even
+    infinity 0x7F80."""
+    wide = {0x3F80: 1.0, 0xC020: -2.5, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+            0x3F81: 1 + 2.0 ** -7, 0x0000: 0.0}
+    for b, v in wide.items():
+        assert float(o.bf16_to_f64(np.uint16(b))) == v, hex(b)
+    assert np.signbit(o.bf16_to_f64(np.uint16(0x8000))) and float(o.bf16_to_f64(np.uint16(0x8000))) == 0.0
+    assert np.isinf(o.bf16_to_f64(np.uint16(0x7F80)))
+    cases = [(1.0, 0x3F80), (-2.5, 0xC020), (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+             (1 + 2.0 ** -8 + 2.0 ** -20, 0x3F81), (1 + 2.0 ** -9, 0x3F80), (-(1 + 3 * 2.0 ** -8), 0xBF82),
+             (2.0 ** -133, 0x0001), (1.5 * 2.0 ** -133, 0x0002), ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),
+             ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F), (-0.0, 0x8000), (float("inf"), 0x7F80)]
+    got = o.f32_to_bf16_rne(np.array([c for c, _ in cases], dtype=np.float32))
+    for (c, want), g in zip(cases, got):
+        assert int(g) == want, (c, hex(int(g)), hex(want))
+    assert int(o.f32_to_bf16_rne(np.float32("nan"))) & 0x7FFF == 0x7FC0
+    # Every non-NaN pattern survives widen -> round unchanged (widening is exact).
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ok = ~np.isnan(o.bf16_to_f64(allb))
+    back = o.f32_to_bf16_rne(o.bf16_to_f64(allb).astype(np.float32))
+    assert np.array_equal(back[ok], allb[ok])
+
+
+def pin_gemm_bf16_widening(o):
+    """gemm_ref_bf16 = gemm_ref on the exact values of the bit patterns: with x the
+    bf16 patterns of small integers (exact in bf16) the two references agree bit for
+    bit, and an identity x returns the dequantised weight."""
+    rng = _rng(31)
+    K, N, g = 64, 16, 32
+    codes = rng.integers(0, 16, (K, N))
+    zeros = rng.integers(0, 16, (K // g, N))
+    scales = rng.uniform(1e-3, 2e-2, (K // g, N)).astype(np.float16)
+    qw, qz = o.pack_awq(codes), o.pack_awq(zeros)
+    xi = rng.integers(-3, 4, (5, K)).astype(np.float32)
+    xb = (xi.view(np.uint32) >> np.uint32(16)).astype(np.uint16)  # small integers: exact top halves
+    bias = rng.integers(-2, 3, N).astype(np.float32)
+    bb = (bias.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal(o.gemm_ref_bf16(xb, qw, qz, scales, bb, g), o.gemm_ref(xi, qw, qz, scales, bias, g))
+    eye = (np.eye(K, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal(o.gemm_ref_bf16(eye, qw, qz, scales, None, g), o.dequant_ref(qw, qz, scales, g))
+
+
 def pin_rtn_hand_example(o):
     """tests/golden/rtn_example.json: one group of 4 rows, 8 equal columns, worked by hand
     from the quantizer table (asymmetric and symmetric)."""
@@ -345,6 +393,6 @@ def pin_rtn_error_bound(o):
                 assert (sc.astype(np.float64) > 0).all()
 
 
-ALL_PINS = [pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
+ALL_PINS = [pin_bf16_conversion, pin_gemm_bf16_widening, pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
             pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
             pin_special_cases, pin_entries_agree, pin_format_rules]

@@ -54,6 +54,12 @@ MUTANTS = [
      "    _, G", 0),
     ("pack shifts by the column index",
      "<< np.uint32(4 * i)", "<< np.uint32(4 * AWQ_ORDER[i])", 0),
+    ("bf16 widened with a 15-bit shift",
+     "(b.astype(np.uint32) << np.uint32(16))", "(b.astype(np.uint32) << np.uint32(15))", 0),
+    ("bf16 rounding truncates",
+     "((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16))", "((u) >> np.uint64(16))", 0),
+    ("bf16 ties away from zero",
+     "((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16))", "((u + np.uint64(0x8000)) >> np.uint64(16))", 0),
     ("RTN codes truncated instead of rounded",
      "codes = np.clip(np.rint(Wg / sf[:, None, :]) + zeros", "codes = np.clip(np.floor(Wg / sf[:, None, :]) + zeros", 0),
     ("RTN zero not negated",
