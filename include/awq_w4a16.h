@@ -142,6 +142,27 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
              void* y_f16, struct ihipStream_t* stream);
 
 /*
+ * awq_gemm with bfloat16 activations: x, bias and y are bfloat16 (raw 16-bit
+ * patterns); qweight, qzeros and the fp16 scales are the same GEMM pack.  The GEMM
+ * kernel's declared contract takes FP16 or BF16 inputs (GPTQModel wiki "AWQ",
+ * section "Selection and compatibility").  Accumulation is fp32; y is rounded once
+ * (to nearest even) to bfloat16 after the bias is added.  Small M multiplies
+ * x . (q - z) exactly and scales each group in fp32; large M feeds the MFMA with the
+ * weight rounded once to bfloat16, bf16((q - z) s).  Limits, plans, determinism and
+ * the workspace rule are those of awq_gemm, except that small-M plans with K splits
+ * always combine them through fp32 partials and a second kernel (the fixed-point
+ * accumulation of awq_gemm relies on fp16's range).
+ *   x_bf16      device bfloat16 [M, K]
+ *   bias_bf16   device bfloat16 [N], or NULL
+ *   y_bf16      device bfloat16 [M, N], written in full
+ * Returns AWQ_OK or an error status.
+ */
+int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qzeros,
+                  const void* scales_f16, const void* bias_bf16,
+                  int64_t M, int64_t K, int64_t N, int64_t group_size,
+                  void* y_bf16, struct ihipStream_t* stream);
+
+/*
  * Round-to-nearest writer of the GEMM pack: quantise an fp16 weight in groups of
  * group_size input rows per output column.  Source: GPTQModel wiki "AWQ", section
  * "Group quantization and zero points" (both quantizers, the clamp of the zero, the

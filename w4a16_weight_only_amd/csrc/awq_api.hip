@@ -119,17 +119,17 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   return true;
 }
 
-Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus) {
+Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = false) {
   Plan p;
   if (M <= AWQ_SKINNY_MAX_M && plan_skinny(M, K, N, g, cus, p.sk)) {
     p.family = 0;
     p.grid_x = p.sk.n_tiles;
     p.grid_y = p.sk.splits;
     p.block = 64 * p.sk.waves;
-    // 4-wave plans: 64-bit fixed-point accumulators per tile entry; 8-wave plans:
-    // fp32 partials per (tile, split, entry).
+    // 4-wave fp16 plans: 64-bit fixed-point accumulators per tile entry; 8-wave
+    // plans and every bfloat16 plan: fp32 partials per (tile, split, entry).
     if (p.sk.splits > 1) {
-      if (p.sk.waves == 4) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+      if (p.sk.waves == 4 && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
       else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * awq::kSkinnyCols * 4;
     }
   } else {
@@ -327,9 +327,10 @@ int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
 }
 
-int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
-             const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
-             struct ihipStream_t* stream) {
+namespace {
+int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
+                bool bf16, hipStream_t stream) {
   const int st = limits_check(M, K, N, group_size);
   if (st != AWQ_OK) return st;
   if (M == 0) return AWQ_OK;
@@ -338,7 +339,7 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
       !aligned16(y_f16) || (bias_f16 && !aligned16(bias_f16)))
     return AWQ_ERR_ALIGN;
   const int g = eff_group(K, group_size);
-  const Plan p = make_plan(M, K, N, g, device_cus());
+  const Plan p = make_plan(M, K, N, g, device_cus(), bf16);
   const auto* x = static_cast<const uint16_t*>(x_f16);
   const auto* sc = static_cast<const uint16_t*>(scales_f16);
   const auto* b = static_cast<const uint16_t*>(bias_f16);
@@ -351,7 +352,7 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
       const int ws = get_workspace(p, stream, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
-    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, accum, partial, y,
+    e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, bf16, accum, partial, y,
                            stream);
   } else {
     uint64_t* accum = nullptr;
@@ -360,9 +361,22 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
       const int ws = get_workspace(p, stream, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
-    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tp, partial, y, stream);
+    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tp, bf16, partial, y, stream);
   }
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+}  // namespace
+
+int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+             const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
+             struct ihipStream_t* stream) {
+  return gemm_common(x_f16, qweight, qzeros, scales_f16, bias_f16, M, K, N, group_size, y_f16, false, stream);
+}
+
+int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                  const void* bias_bf16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_bf16,
+                  struct ihipStream_t* stream) {
+  return gemm_common(x_bf16, qweight, qzeros, scales_f16, bias_bf16, M, K, N, group_size, y_bf16, true, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,40 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 <-> float.  A bfloat16 is the top half of a binary32, so widening is a
+// shift; narrowing rounds to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two floats -> packed bfloat16 pair (low half = a), rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const float __attribute__((ext_vector_type(2))) f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Activations as raw 16-bit patterns: fp16 or (BF16) bfloat16.
+template <bool BF16>
+__device__ __forceinline__ float act_to_float(uint16_t b) {
+  if constexpr (BF16) return bf16_bits_to_float(b);
+  else return (float)__builtin_bit_cast(_Float16, b);
+}
+template <bool BF16>
+__device__ __forceinline__ uint16_t float_to_act(float f) {
+  if constexpr (BF16) return float_to_bf16_bits(f);
+  else return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// Two rounded activations packed in one word (low half = a).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack_act2(float a, float b) {
+  if constexpr (BF16) return pack_bf16x2(a, b);
+  else return __builtin_bit_cast(uint32_t, half2v{(_Float16)a, (_Float16)b});
+}
 
 // Column held by the low / high nibble of byte t (see the table above).
 __host__ __device__ constexpr int lo_col(int t) { return ((t & 1) << 2) | (t >> 1); }
@@ -53,12 +87,20 @@ __device__ __forceinline__ uint32_t pair_byte(uint32_t a, uint32_t b) {
 // constants, so with literals the compiler splits (p & mask) | magic into two
 // instructions; opaque register copies let it emit one v_and_or_b32.
 struct UnpackConsts {
-  uint32_t magic, mlo, mhi;
+  uint32_t magic, mlo, mhi, bmagic;
 };
 __device__ __forceinline__ UnpackConsts unpack_consts() {
-  UnpackConsts k{0x64006400u, 0x000F000Fu, 0x00F000F0u};
-  asm volatile("" : "+v"(k.magic), "+v"(k.mlo), "+v"(k.mhi));
+  UnpackConsts k{0x64006400u, 0x000F000Fu, 0x00F000F0u, 0x43004300u};
+  asm volatile("" : "+v"(k.magic), "+v"(k.mlo), "+v"(k.mhi), "+v"(k.bmagic));
   return k;
+}
+
+// bfloat16 pair (128 + lo_a, 128 + lo_b): 0x4300 is 128.0 and 128..255 are exact in
+// bfloat16 (7 fraction bits), so the nibble ORed into the fraction is exact.  A
+// high nibble (bits 4-7 would reach the exponent) is shifted down first.
+__device__ __forceinline__ uint32_t lo_magic_bf16(uint32_t p, const UnpackConsts& k) { return (p & k.mlo) | k.bmagic; }
+__device__ __forceinline__ uint32_t hi_magic_bf16(uint32_t p, const UnpackConsts& k) {
+  return ((p >> 4) & k.mlo) | k.bmagic;
 }
 
 // fp16 pair (1024 + lo_a, 1024 + lo_b): the nibble ORed into the mantissa of 1024.0

@@ -62,13 +62,16 @@ hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym,
 // With p.splits > 1: 4-wave plans use accum, [n_tiles][mrows * 256] 64-bit
 // accumulators that are zero before the call and left zero by it; 8-wave plans use
 // partial, [n_tiles][splits][16 * 256] fp32 scratch, and a second reduce kernel.
+// x, bias and y are fp16 or (bf16 = true) bfloat16 bit patterns; scales are fp16.
+// bfloat16 skinny plans with splits > 1 always use partial (fp32 partials and the
+// reduce kernel), never accum.
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         const SkinnyPlan& p, uint64_t* accum, float* partial, uint16_t* y,
+                         const SkinnyPlan& p, bool bf16, uint64_t* accum, float* partial, uint16_t* y,
                          hipStream_t stream);
 
 hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                        const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream);
+                       const TilePlan& p, bool bf16, float* partial, uint16_t* y, hipStream_t stream);
 
 }  // namespace awq

@@ -68,11 +68,47 @@ __host__ __device__ constexpr int tab_col(int v) {  // column within the word
   return (v & 1) ? hi_col((v >> 1) & 3) : lo_col((v >> 1) & 3);
 }
 
-// The 16 MFMAs of one k-step for one lane's 2 word-columns.  zs holds, per entry,
-// the fp16 splat to add: -(1024 + z) for low-nibble columns, -(64 + z) for
-// high-nibble columns.
+// The 16 MFMAs of one k-step for one lane's 2 word-columns.
+// fp16 x: zs holds, per entry, the fp16 splat to add: -(1024 + z) for low-nibble
+// columns, -(64 + z) for high-nibble columns, so B = (q - z) exactly.
+// bfloat16 x (no packed bfloat16 add on this chip): B = 128 + q, exact in
+// bfloat16, and one more MFMA against a B of ones adds the k-step's sum of x per row
+// to sx; the group's sum is then corrected by -(128 + z) sx in fp32 (flush).
+template <bool BF16>
 __device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[16], const UnpackConsts& uk,
-                                           floatx4 (&part)[16]) {
+                                           floatx4 (&part)[16], floatx4& sx) {
+  if constexpr (BF16) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, st.a);
+    const uint32_t one2 = 0x3F803F80u;  // bfloat16 pair (1, 1)
+    sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2}), sx,
+                                                 0, 0, 0);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t ra = st.v[2 * p][w];
+          const uint32_t rb = st.v[2 * p + 1][w];
+          uint32_t pb;
+          if (t == 0) pb = pair_byte<0>(ra, rb);
+          else if (t == 1) pb = pair_byte<1>(ra, rb);
+          else if (t == 2) pb = pair_byte<2>(ra, rb);
+          else pb = pair_byte<3>(ra, rb);
+          lo[p] = lo_magic_bf16(pb, uk);
+          hi[p] = hi_magic_bf16(pb, uk);
+        }
+        const int il = tab_idx(w, t, 0), ih = tab_idx(w, t, 1);
+        part[il] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), part[il], 0, 0, 0);
+        part[ih] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), part[ih], 0, 0, 0);
+      }
+    }
+    return;
+  }
+  (void)sx;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
@@ -116,19 +152,21 @@ struct SkinnyLds {
 
 // Workspace: per tile, 64-bit accumulator 4 * slot + i holds row 4 (slot / 256) + i
 // of the slot's column, slot = q * 256 + accumulator * 16 + c.  All zero between calls.
-template <int WAVES, int MROWS, bool SINGLE>
+template <int WAVES, int MROWS, bool SINGLE, bool BF16>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const _Float16* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
-    uint64_t* __restrict__ accum, float* __restrict__ partial, _Float16* __restrict__ y) {
+    const uint16_t* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
+    uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
   // k-steps in flight per wave, and how K splits meet: 4-wave workgroups (M <= 4)
   // combine splits with fixed-point atomics; 8-wave ones (up to 16 rows, where the
   // atomic count M * N * S gets large) store fp32 partials for skinny_reduce_kernel.
+  // bfloat16 always takes the partials: the fixed-point format relies on fp16's
+  // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
   constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
-  constexpr bool ATOMIC = WAVES == 4;
+  constexpr bool ATOMIC = WAVES == 4 && !BF16;
   __shared__ SkinnyLds<WAVES> sh;
 
   const int tid = threadIdx.x;
@@ -205,9 +243,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
         sv = (float)scales[(int64_t)(g0 + gl) * N + 8 * wcol + col];
       }
       const uint32_t z = zero_code(zw, col);
-      // fp16 bits of -(1024 + z) (low nibble) or -(64 + z) (high nibble), splatted.
-      const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
-      sh.u.meta.zsplat[gl][cc][v] = h | (h << 16);
+      if constexpr (BF16) {
+        sh.u.meta.zsplat[gl][cc][v] = __builtin_bit_cast(uint32_t, 128.0f + (float)z);  // 128 + z, fp32
+      } else {
+        // fp16 bits of -(1024 + z) (low nibble) or -(64 + z) (high nibble), splatted.
+        const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
+        sh.u.meta.zsplat[gl][cc][v] = h | (h << 16);
+      }
       sh.u.meta.scale[gl][cc][v] = sv;
     }
     __syncthreads();
@@ -215,6 +257,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 
   floatx4 part[16];
   floatx4 acc[16];
+  floatx4 sx = floatx4{0.f, 0.f, 0.f, 0.f};  // bfloat16: sum of x over the group's k, per row
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -231,27 +274,35 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       dst[4 * k4 + 3] = v[3];
     }
   };
-  // Scale this group's sums into acc (several groups).
+  uint32_t zs[16];
+  // Scale this group's sums into acc (several groups); bfloat16 first subtracts
+  // (128 + z) times the group's sum of x (zs holds 128 + z as fp32 bits).
   auto flush = [&](int gl) {
     uint32_t sb[16];
     load_tab(reinterpret_cast<const uint32_t*>(sh.u.meta.scale[gl][c]), sb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      acc[v] += __builtin_bit_cast(float, sb[v]) * part[v];
+      floatx4 pv = part[v];
+      if constexpr (BF16) pv -= __builtin_bit_cast(float, zs[v]) * sx;
+      acc[v] += __builtin_bit_cast(float, sb[v]) * pv;
       part[v] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    sx = floatx4{0.f, 0.f, 0.f, 0.f};
   };
 
   const UnpackConsts uk = unpack_consts();
-  uint32_t zs[16];
   if constexpr (SINGLE) {
-    // Entry v: word w = v / 8, column tab_col(v) of it; zero splat as in the tables.
+    // Entry v: word w = v / 8, column tab_col(v) of it; zero term as in the tables.
     const uint32_t zw[2] = {gz[0], gz[1]};
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const uint32_t z = zero_code(zw[v >> 3], tab_col(v));
-      const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
-      zs[v] = h | (h << 16);
+      if constexpr (BF16) {
+        zs[v] = __builtin_bit_cast(uint32_t, 128.0f + (float)z);
+      } else {
+        const uint32_t h = (v & 1) ? (0xD400u | (z << 4)) : (0xE400u | z);
+        zs[v] = h | (h << 16);
+      }
     }
   }
   int cur_g = -1;
@@ -269,7 +320,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
             cur_g = gl;
           }
         }
-        kstep_mfma(ring[j], zs, uk, part);
+        kstep_mfma<BF16>(ring[j], zs, uk, part, sx);
         if (ks + PF < ke) issue(ring[j], ks + PF);
       }
     }
@@ -279,8 +330,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float sv = (float)((v >> 3) ? gs1[tab_col(v)] : gs0[tab_col(v)]);
-      if (M == 1) part[v][0] *= sv;
-      else part[v] *= sv;
+      if constexpr (BF16) {
+        const float zc = __builtin_bit_cast(float, zs[v]);
+        if (M == 1) part[v][0] = (part[v][0] - zc * sx[0]) * sv;
+        else part[v] = (part[v] - zc * sx) * sv;
+      } else {
+        if (M == 1) part[v][0] *= sv;
+        else part[v] *= sv;
+      }
     }
   } else {
     if (cur_g >= 0) flush(cur_g);
@@ -321,11 +378,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       const int s = tid + k * THREADS;
       const int n = slot_n(s);
       if (s < nslots && n < N) {
-        const float b = bias ? (float)bias[n] : 0.f;
+        const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * (s >> 8) + i;
-          if (row < rows) y[(int64_t)row * N + n] = (_Float16)(sum[k][i] + b);
+          if (row < rows) y[(int64_t)row * N + n] = float_to_act<BF16>(sum[k][i] + b);
         }
       }
     }
@@ -373,23 +430,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       if (count == (uint64_t)splits) {
         __hip_atomic_store(tile_acc + 4 * s + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n < N) {
-          const float b = bias ? (float)bias[n] : 0.f;
-          y[(int64_t)row * N + n] = (_Float16)((float)value * (1.0f / kToFixed) + b);
+          const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
+          y[(int64_t)row * N + n] = float_to_act<BF16>((float)value * (1.0f / kToFixed) + b);
         }
       }
     }
   }
 }
 
-// Sums the fp32 partials of the 8-wave skinny kernel in split order, adds bias,
-// rounds once to fp16.  One workgroup per (tile, group of 4 rows): thread t reads the
+// Sums the fp32 partials of the skinny kernel in split order, adds bias, rounds once
+// to fp16 or bfloat16.  One workgroup per (tile, group of 4 rows): thread t reads the
 // 4 rows of slot 256 q + t (16 contiguous bytes per split), and the rounded values
 // meet in LDS in output order so that y is written as whole 16-byte row pieces.
+// tile_entries: rows kept per tile (4 or 16) x 256.
+template <bool BF16>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
-                                                            const _Float16* __restrict__ bias, int M, int N,
-                                                            int splits, _Float16* __restrict__ y) {
-  constexpr int TILE_ENTRIES = 16 * kSkinnyCols;
-  __shared__ __attribute__((aligned(16))) _Float16 ys[4][kSkinnyCols + 8];
+                                                            const uint16_t* __restrict__ bias, int M, int N,
+                                                            int splits, int tile_entries, uint16_t* __restrict__ y) {
+  const int TILE_ENTRIES = tile_entries;
+  __shared__ __attribute__((aligned(16))) uint16_t ys[4][kSkinnyCols + 8];
   const int tile = blockIdx.x / 4, q = blockIdx.x % 4;
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
@@ -400,45 +459,52 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   const int sv = (t >> 4) & 15, sc = t & 15;
   const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
   const int n = tile * kSkinnyCols + ct;
-  const float b = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
+  const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ys[i][ct] = (_Float16)(a[i] + b);
+  for (int i = 0; i < 4; ++i) ys[i][ct] = float_to_act<BF16>(a[i] + b);
   __syncthreads();
   if (t < 4 * (kSkinnyCols / 8)) {
     const int i = t / (kSkinnyCols / 8), pc = t % (kSkinnyCols / 8);
     const int row = 4 * q + i, n0 = tile * kSkinnyCols + 8 * pc;
     if (row < M && n0 < N)
-      *reinterpret_cast<half8v*>(y + (int64_t)row * N + n0) = *reinterpret_cast<const half8v*>(&ys[i][8 * pc]);
+      *reinterpret_cast<u32x4*>(y + (int64_t)row * N + n0) = *reinterpret_cast<const u32x4*>(&ys[i][8 * pc]);
   }
+}
+
+template <bool BF16>
+static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                                  const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
+                                  const SkinnyPlan& p, uint64_t* accum, float* partial, uint16_t* y,
+                                  hipStream_t stream) {
+  const dim3 grid(p.n_tiles, p.splits);
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, x, reinterpret_cast<const uint32_t*>(qweight),
+                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), bias,
+                       M, K, N, g, p.L, p.splits, accum, partial, y);
+  };
+  if (p.waves == 4) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, BF16>, 256);
+    else go(skinny_kernel<4, 4, false, BF16>, 256);
+  } else {
+    if (p.single_group) go(skinny_kernel<8, 16, true, BF16>, 512);
+    else go(skinny_kernel<8, 16, false, BF16>, 512);
+  }
+  // Partials (8-wave plans, and every bfloat16 plan) are summed by the reduce kernel.
+  if (p.splits > 1 && (p.waves == 8 || BF16)) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(skinny_reduce_kernel<BF16>, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N,
+                       p.splits, p.mrows * kSkinnyCols, y);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_skinny(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                          const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                         const SkinnyPlan& p, uint64_t* accum, float* partial, uint16_t* y,
+                         const SkinnyPlan& p, bool bf16, uint64_t* accum, float* partial, uint16_t* y,
                          hipStream_t stream) {
-  const dim3 grid(p.n_tiles, p.splits);
-  auto go = [&](auto kern, int threads) {
-    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream,
-                       reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
-                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, p.L, p.splits, accum, partial,
-                       reinterpret_cast<_Float16*>(y));
-  };
-  if (p.waves == 4) {
-    if (p.single_group) go(skinny_kernel<4, 4, true>, 256);
-    else go(skinny_kernel<4, 4, false>, 256);
-  } else {
-    if (p.single_group) go(skinny_kernel<8, 16, true>, 512);
-    else go(skinny_kernel<8, 16, false>, 512);
-    if (p.splits > 1) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(p.n_tiles * 4), dim3(256), 0, stream,
-                         partial, reinterpret_cast<const _Float16*>(bias), M, N,
-                         p.splits, reinterpret_cast<_Float16*>(y));
-    }
-  }
-  return hipGetLastError();
+  return bf16 ? launch_skinny_t<true>(x, qweight, qzeros, scales, bias, M, K, N, g, p, accum, partial, y, stream)
+              : launch_skinny_t<false>(x, qweight, qzeros, scales, bias, M, K, N, g, p, accum, partial, y, stream);
 }
 
 }  // namespace awq

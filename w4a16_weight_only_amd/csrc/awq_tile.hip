@@ -68,12 +68,31 @@ __device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 
 
 }  // namespace
 
-template <int FM, int FN, int WM, int KG>
+// MFMA of one 32x32x16 block; a and b hold fp16 or (BF16) bfloat16 bit patterns.
+template <bool BF16>
+__device__ __forceinline__ floatx16 mfma32(const half8v& a, const half8v& b, const floatx16& c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// One B pair (rows k, k + 1 of a column) from the magic form: fp16 x gets
+// fp16((q - z) s), rounded once; bfloat16 x gets bf16((q - z) s), rounded once from
+// the exact fp32 product ((q - z) has at most 5 significant bits and s 11).
+template <bool BF16>
+__device__ __forceinline__ uint32_t b_pair(uint32_t magic_pair, half2v mult, half2v off, half2v sc) {
+  const half2v qz = __builtin_elementwise_fma(as_h2(magic_pair), mult, off);  // (q - z) exactly
+  if constexpr (BF16) return pack_bf16x2((float)qz[0] * (float)sc[0], (float)qz[1] * (float)sc[1]);
+  else return as_u32(qz * sc);
+}
+
+template <int FM, int FN, int WM, int KG, bool BF16>
 __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const _Float16* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
-    float* __restrict__ partial, _Float16* __restrict__ y) {
+    const uint16_t* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
+    float* __restrict__ partial, uint16_t* __restrict__ y) {
   constexpr int THREADS = 256 * KG;   // KG groups of 4 waves; group kg takes k16 steps of its share
   constexpr int WN = 4 / WM;          // waves along N
   constexpr int BM = WM * 32 * FM;    // workgroup rows
@@ -290,22 +309,21 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (kPrefetch && s + 1 < S1) read_frag(fr[(s + 1) & 1], buf, s + 1, kh);
       if (s % 2 == 0) apply_group(buf, s / 2 + kh, keep);
       const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
-      half2v h0[4], h1[4];
+      u32x4 b0w, b1w;
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
         const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
-        h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
-        if (FN == 2)
-          h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
+        b0w[pr] = b_pair<BF16>((pb & mask) | uk.magic, mult, off0, sc0);
+        if (FN == 2) b1w[pr] = b_pair<BF16>(((pb >> 8) & mask) | uk.magic, mult, off1, sc1);
       }
       half8v bf[2];
-      bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
-      if (FN == 2) bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+      bf[0] = __builtin_bit_cast(half8v, b0w);
+      if (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<BF16>(f.a[i], bf[j], acc[i][j]);
     }
   };
   using C0 = std::integral_constant<int, 0>;
@@ -373,24 +391,22 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     };
     auto dequant = [&](const u32x4& wlo, const u32x4& whi, half8v(&bf)[2]) {
       const uint32_t w[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
-      half2v h0[4], h1[4];
+      u32x4 b0w, b1w;
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
         const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
-        h0[pr] = __builtin_elementwise_fma(as_h2((pb & mask) | uk.magic), mult, off0) * sc0;
-        if constexpr (FN == 2)
-          h1[pr] = __builtin_elementwise_fma(as_h2(((pb >> 8) & mask) | uk.magic), mult, off1) * sc1;
+        b0w[pr] = b_pair<BF16>((pb & mask) | uk.magic, mult, off0, sc0);
+        if constexpr (FN == 2) b1w[pr] = b_pair<BF16>(((pb >> 8) & mask) | uk.magic, mult, off1, sc1);
       }
-      bf[0] = half8v{h0[0][0], h0[0][1], h0[1][0], h0[1][1], h0[2][0], h0[2][1], h0[3][0], h0[3][1]};
-      if constexpr (FN == 2)
-        bf[1] = half8v{h1[0][0], h1[0][1], h1[1][0], h1[1][1], h1[2][0], h1[2][1], h1[3][0], h1[3][1]};
+      bf[0] = __builtin_bit_cast(half8v, b0w);
+      if constexpr (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
     };
     auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<BF16>(a[i], bf[j], acc[i][j]);
     };
     // One MFMA, then a few VALU instructions, FM * FN times: the dequant issues while
     // the matrix core works.
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + (j == 0 ? c0 : c1);
-      bj[j] = (bias != nullptr && n < N) ? (float)bias[n] : 0.f;
+      bj[j] = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
     }
   #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -510,10 +526,10 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       for (int r = 0; r < 16; ++r) {
         const int row = wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (FN == 2)
-          *reinterpret_cast<half2v*>(&Ys[row * YLD + c0]) =
-              half2v{(_Float16)(acc[i][0][r] + bj[0]), (_Float16)(acc[i][FN - 1][r] + bj[FN - 1])};
+          *reinterpret_cast<uint32_t*>(&Ys[row * YLD + c0]) =
+              pack_act2<BF16>(acc[i][0][r] + bj[0], acc[i][FN - 1][r] + bj[FN - 1]);
         else
-          Ys[row * YLD + c0] = (_Float16)(acc[i][0][r] + bj[0]);
+          reinterpret_cast<uint16_t*>(Ys)[row * YLD + c0] = float_to_act<BF16>(acc[i][0][r] + bj[0]);
       }
   }
   __syncthreads();
@@ -528,11 +544,12 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   }
 }
 
-// y = fp16(sum over splits of partial[s] + bias), 8 columns per thread, splits
-// summed in order (deterministic).
+// y = round(sum over splits of partial[s] + bias) to fp16 or (BF16) bfloat16, 8
+// columns per thread, splits summed in order (deterministic).
+template <bool BF16>
 __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restrict__ partial,
-                                                          const _Float16* __restrict__ bias, int64_t MN,
-                                                          int N, int splits, _Float16* __restrict__ y) {
+                                                          const uint16_t* __restrict__ bias, int64_t MN,
+                                                          int N, int splits, uint16_t* __restrict__ y) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e >= MN) return;
   floatx4 a = *reinterpret_cast<const floatx4*>(partial + e);
@@ -543,47 +560,49 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restric
   }
   if (bias != nullptr) {
     const int n = (int)(e % N);
-    const half8v bv = *reinterpret_cast<const half8v*>(bias + n);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] += (float)bv[j];
-      b[j] += (float)bv[4 + j];
+      a[j] += act_to_float<BF16>(bias[n + j]);
+      b[j] += act_to_float<BF16>(bias[n + 4 + j]);
     }
   }
-  half8v o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    o[j] = (_Float16)a[j];
-    o[4 + j] = (_Float16)b[j];
-  }
-  *reinterpret_cast<half8v*>(y + e) = o;
+  const u32x4 o = {pack_act2<BF16>(a[0], a[1]), pack_act2<BF16>(a[2], a[3]), pack_act2<BF16>(b[0], b[1]),
+                   pack_act2<BF16>(b[2], b[3])};
+  *reinterpret_cast<u32x4*>(y + e) = o;
 }
 
-hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
-                       const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
-                       const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream) {
+template <bool BF16>
+static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
+                                const TilePlan& p, float* partial, uint16_t* y, hipStream_t stream) {
   const bool split = p.splits > 1;
   auto go = [&](auto kern, int bm, int bn, int threads) {
     const int m_tiles = (M + bm - 1) / bm;
     const int n_tiles = (N + bn - 1) / bn;
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(threads), 0,
-                       stream, reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint32_t*>(qweight),
-                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales),
-                       reinterpret_cast<const _Float16*>(bias), M, K, N, g, m_tiles, p.kps,
-                       split ? partial : nullptr, reinterpret_cast<_Float16*>(y));
+                       stream, x, reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
+                       reinterpret_cast<const _Float16*>(scales), bias, M, K, N, g, m_tiles, p.kps,
+                       split ? partial : nullptr, y);
   };
   switch (p.variant) {
-    case 0: go(tile_kernel<8, 1, 1, 2>, 256, 128, 512); break;
-    case 1: go(tile_kernel<2, 1, 2, 1>, 128, 64, 256); break;
-    default: go(tile_kernel<2, 1, 1, 1>, 64, 128, 256); break;
+    case 0: go(tile_kernel<8, 1, 1, 2, BF16>, 256, 128, 512); break;
+    case 1: go(tile_kernel<2, 1, 2, 1, BF16>, 128, 64, 256); break;
+    default: go(tile_kernel<2, 1, 1, 1, BF16>, 64, 128, 256); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t MN = (int64_t)M * N;
   const int64_t blocks = (MN / 8 + 255) / 256;
-  hipLaunchKernelGGL(tile_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partial,
-                     reinterpret_cast<const _Float16*>(bias), MN, N, p.splits, reinterpret_cast<_Float16*>(y));
+  hipLaunchKernelGGL(tile_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N,
+                     p.splits, y);
   return hipGetLastError();
+}
+
+hipError_t launch_tile(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                       const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
+                       const TilePlan& p, bool bf16, float* partial, uint16_t* y, hipStream_t stream) {
+  return bf16 ? launch_tile_t<true>(x, qweight, qzeros, scales, bias, M, K, N, g, p, partial, y, stream)
+              : launch_tile_t<false>(x, qweight, qzeros, scales, bias, M, K, N, g, p, partial, y, stream);
 }
 
 }  // namespace awq

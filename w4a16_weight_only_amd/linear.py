@@ -136,17 +136,21 @@ def awq_quantize_rtn(w: torch.Tensor, group_size: int = 128, sym: bool = False,
 def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
              bias: torch.Tensor | None = None, group_size: int = 128,
              out: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x . dequant(W) + bias in fp16 with fp32 accumulation.
+    """y = x . dequant(W) + bias with fp32 accumulation, in x's dtype: fp16, or
+    bfloat16 (then bias and y are bfloat16 too; scales stay fp16).
 
     x may have leading dimensions; they are flattened into rows (as the pages'
     kernels do) and restored on the output."""
-    _check_tensor("x", x, torch.float16)
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    act = x.dtype if x.dtype in (torch.float16, torch.bfloat16) else torch.float16
+    _check_tensor("x", x, act)
     dev = x.device
     _check_tensor("qweight", qweight, torch.int32, dev)
     _check_tensor("qzeros", qzeros, torch.int32, dev)
     _check_tensor("scales", scales, torch.float16, dev)
     if bias is not None:
-        _check_tensor("bias", bias, torch.float16, dev)
+        _check_tensor("bias", bias, act, dev)
     K, N = qweight.shape[0], qweight.shape[1] * 8
     if x.shape[-1] != K:
         raise ValueError(f"x has {x.shape[-1]} input features, qweight has {K}")
@@ -156,15 +160,17 @@ def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scale
     for d in lead:
         M *= d
     if out is None:
-        out = torch.empty(lead + (N,), dtype=torch.float16, device=dev)
+        out = torch.empty(lead + (N,), dtype=act, device=dev)
     else:
-        _check_tensor("out", out, torch.float16, dev)
+        _check_tensor("out", out, act, dev)
         if tuple(out.shape) != lead + (N,):
             raise ValueError(f"out must be {lead + (N,)}")
+    lib = _lib.load()
+    fn, name = (lib.awq_gemm_bf16, "awq_gemm_bf16") if act == torch.bfloat16 else (lib.awq_gemm, "awq_gemm")
     with torch.cuda.device(dev):
-        st = _lib.load().awq_gemm(_ptr(x), _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(bias),
-                                  M, K, N, group_size, _ptr(out), _stream(dev))
-    _lib.check(st, "awq_gemm")
+        st = fn(_ptr(x), _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(bias), M, K, N, group_size, _ptr(out),
+                _stream(dev))
+    _lib.check(st, name)
     return out
 
 

@@ -95,6 +95,35 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
                 group_size=w.group_size)
 
 
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float draws, rounded by torch's CPU cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_inputs_bf16(w: Workload, seed: int | None = None) -> dict:
+    """The same draws as make_inputs with bfloat16 activations: x and bias are the
+    float64 draws rounded to float32 and then to bfloat16 (bit patterns, uint16)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    M, K, N, G = w.M, w.K, w.N, w.groups
+    qweight = random_words(rng, (K, N // 8))
+    qzeros = random_words(rng, (G, N // 8))
+    scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K))
+    if w.outlier_count:
+        idx = rng.choice(K, size=w.outlier_count, replace=False)
+        x[:, idx] *= w.outlier_gain
+    bias = rng.normal(0.0, 0.01, size=N) if w.bias else None
+    return dict(x=to_bf16_bits(x), qweight=qweight, qzeros=qzeros, scales=scales,
+                bias=None if bias is None else to_bf16_bits(bias), group_size=w.group_size)
+
+
+def make_custom_bf16(M, K, N, group_size, bias=True, seed=0, outlier_count=0) -> dict:
+    return make_inputs_bf16(Workload(f"custom_m{M}_k{K}_n{N}_g{group_size}", M, K, N, group_size,
+                                     bias, outlier_count=outlier_count, seed=seed))
+
+
 def make_custom(M, K, N, group_size, bias=True, seed=0, outlier_count=0) -> dict:
     """Same distributions at an arbitrary shape (ragged and edge-case tests)."""
     return make_inputs(Workload(f"custom_m{M}_k{K}_n{N}_g{group_size}", M, K, N, group_size,
