@@ -79,19 +79,26 @@ def load_traffic(workload: str, digest: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_workload(name, steps, warmup, torch, awq, synth):
+def time_workload(name, steps, warmup, torch, awq, synth, bf16=False):
+    """awq_gemm on workload `name`; bf16=True takes bfloat16 x, bias and y (awq_gemm_bf16)."""
     w = synth.WORKLOADS[name]
-    d = synth.make_inputs(w)
+    d = synth.make_inputs_bf16(w) if bf16 else synth.make_inputs(w)
     dev = torch.device("cuda", 0)
     layer_bytes = d["qweight"].nbytes + d["qzeros"].nbytes + d["scales"].nbytes
     copies = max(1, -(-ROTATE_BYTES // layer_bytes))
-    x = torch.from_numpy(d["x"]).to(dev)
-    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+
+    def act(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(a.view(np.int16) if bf16 else a).to(dev)
+        return t.view(torch.bfloat16) if bf16 else t
+    x = act(d["x"])
+    bias = act(d["bias"])
     weights = []
     for i in range(copies):
         # Independent buffers with identical contents: the same layer, fresh addresses.
         weights.append(tuple(torch.from_numpy(d[k]).to(dev) for k in ("qweight", "qzeros", "scales")))
-    y = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    y = torch.empty((w.M, w.N), dtype=torch.bfloat16 if bf16 else torch.float16, device=dev)
     g = w.group_size
     stream = torch.cuda.Stream(dev)
     torch.cuda.synchronize()
@@ -383,6 +390,15 @@ def main():
                 entry["dequant_then_dense_us"] = dd  # awq_dequant_f16 + hipBLASLt fp16 GEMM
             sec.append(entry)
         out["secondary"] = sec
+        # bfloat16 activations (awq_gemm_bf16) on the same weights.
+        bf = []
+        for name in ("decode_m1_k4096_n4096_g128", "decode_m16_k4096_n11008_g128", "down_proj_m64_k11008_n4096_g64",
+                     "down_proj_m512_k11008_n4096_g64", "prefill_m2048_k4096_n4096_g128"):
+            n_steps = min(args.steps, 200)
+            rs = time_workload(name, n_steps, 10, torch, awq, synth, bf16=True)
+            v, u, rf, pl = summarize(rs, n_steps)
+            bf.append(dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3), roofline=rf))
+        out["bf16"] = bf
         # The RTN writer (fp16 weight -> GEMM pack), HBM-bound.
         out["writer"] = [time_quantize_rtn(K, N, g, sym, min(args.steps, 100), torch, awq, synth)
                          for (K, N, g, sym) in ((4096, 4096, 128, False), (4096, 4096, 128, True),
