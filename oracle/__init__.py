@@ -7,5 +7,5 @@ from .awq_ref import (  # noqa: F401
     AWQ_ORDER, AWQ_REVERSE, AwqFormatError, resolve_groups, validate_pack,
     pack_awq, unpack_awq, unpack_awq_gather, dequant_ref, dequant_ref_T,
     gemm_ref, gemm_ref_entries, fp16_rne, quantize_rtn,
-    bf16_to_f64, f32_to_bf16_rne, gemm_ref_bf16,
+    bf16_to_f64, f32_to_bf16_rne, gemm_ref_bf16, moe_align_ref, moe_gemm_ref,
 )

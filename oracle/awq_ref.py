@@ -278,6 +278,53 @@ def gemm_ref_bf16(x_bits, qweight, qzeros, scales, bias_bits, group_size) -> np.
     return gemm_ref(x, qweight, qzeros, scales, bias, group_size)
 
 
+# Routed experts.  vLLM's AWQ support sends a routed-expert (MoE) layer to a 4-bit
+# WNA16 MoE kernel over per-expert qweight / qzeros / scales ([VLLM] section 5.4).
+# Reading taken: each routed slot s (token t = s // topk, its choice s % topk)
+# multiplies that token's activations by its expert's dequantised weight; the
+# expert's activation function and the weighted sum over the topk choices come
+# after this product and are not part of it.
+
+def moe_align_ref(expert_ids, num_experts: int):
+    """Counting sort of routed slots by expert (stable: slot order within an expert).
+
+    Returns (offsets [E + 1], sorted_slots [S]): the slots of expert e are
+    sorted_slots[offsets[e] : offsets[e + 1]], in increasing slot order."""
+    ids = np.asarray(expert_ids).astype(np.int64).ravel()
+    if ids.size and (ids.min() < 0 or ids.max() >= num_experts):
+        raise AwqFormatError("expert id out of range")
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for e in ids:
+        counts[e] += 1
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    cursor = offsets[:-1].copy()
+    sorted_slots = np.empty(ids.size, dtype=np.int64)
+    for s, e in enumerate(ids):
+        sorted_slots[cursor[e]] = s
+        cursor[e] += 1
+    return offsets, sorted_slots
+
+
+def moe_gemm_ref(x, qweights, qzeros, scales, expert_ids, topk: int, group_size: int) -> np.ndarray:
+    """y[s] = x[s // topk] . dequant(W[expert_ids[s]]) in float64, shape [S, N].
+
+    qweights / qzeros / scales are stacked per expert ([E, K, N/8], [E, G, N/8],
+    [E, G, N]); each expert's product is gemm_ref on the rows routed to it."""
+    x = np.asarray(x)
+    ids = np.asarray(expert_ids).astype(np.int64).ravel()
+    E = np.asarray(qweights).shape[0]
+    N = np.asarray(scales).shape[2]
+    if ids.size != x.shape[0] * topk:
+        raise AwqFormatError("expert_ids must hold topk entries per token")
+    y = np.zeros((ids.size, N), dtype=np.float64)
+    for e in range(E):
+        rows = np.nonzero(ids == e)[0]
+        if rows.size:
+            y[rows] = gemm_ref(x[rows // topk], qweights[e], qzeros[e], scales[e], None, group_size)
+    return y
+
+
 def quantize_rtn(W, group_size: int, sym: bool = False):
     """Round-to-nearest writer: fp16 W [K, N] -> (qweight [K, N/8], qzeros [G, N/8],
     scales fp16 [G, N]) in the GEMM layout, so that dequant_ref gives back

@@ -328,6 +328,51 @@ def pin_gemm_bf16_widening(o):
     assert np.array_equal(o.gemm_ref_bf16(eye, qw, qz, scales, None, g), o.dequant_ref(qw, qz, scales, g))
 
 
+def pin_moe_align(o):
+    """A hand-worked routing: slots 0..5 to experts [2, 0, 2, 1, 0, 2] of 4 give counts
+    [2, 1, 3, 0], offsets [0, 2, 3, 6, 6] and slots (1, 4 | 3 | 0, 2, 5), each expert's
+    slots in increasing order; on random routings the result is a permutation whose
+    segments hold exactly the slots of their expert, in increasing order."""
+    off, srt = o.moe_align_ref([2, 0, 2, 1, 0, 2], 4)
+    assert off.tolist() == [0, 2, 3, 6, 6] and srt.tolist() == [1, 4, 3, 0, 2, 5]
+    rng = _rng(32)
+    for S, E in ((1, 1), (37, 5), (500, 64)):
+        ids = rng.integers(0, E, S)
+        off, srt = o.moe_align_ref(ids, E)
+        assert sorted(srt.tolist()) == list(range(S))
+        for e in range(E):
+            seg = srt[off[e]:off[e + 1]]
+            assert (ids[seg] == e).all() and (np.diff(seg) > 0).all() and seg.size == (ids == e).sum()
+
+
+def pin_moe_gemm(o):
+    """One expert and topk = 1 is gemm_ref; relabelling the experts (with their weights)
+    leaves y unchanged; and a tiny case matches an exact rational triple loop."""
+    from fractions import Fraction
+    rng = _rng(33)
+    T, K, N, g, E, topk = 3, 16, 8, 8, 3, 2
+    qw = np.stack([o.pack_awq(rng.integers(0, 16, (K, N))) for _ in range(E)])
+    qz = np.stack([o.pack_awq(rng.integers(0, 16, (K // g, N))) for _ in range(E)])
+    sc = rng.uniform(1e-3, 2e-2, (E, K // g, N)).astype(np.float16)
+    x = rng.standard_normal((T, K)).astype(np.float16)
+    ids = np.array([[0, 2], [1, 0], [2, 1]]).ravel()
+    y = o.moe_gemm_ref(x, qw, qz, sc, ids, topk, g)
+    assert np.array_equal(o.moe_gemm_ref(x, qw[:1], qz[:1], sc[:1], np.zeros(T, dtype=np.int64), 1, g),
+                          o.gemm_ref(x, qw[0], qz[0], sc[0], None, g))
+    perm = np.array([2, 0, 1])  # new label of old expert e is perm[e]
+    inv = np.argsort(perm)
+    assert np.array_equal(o.moe_gemm_ref(x, qw[inv], qz[inv], sc[inv], perm[ids], topk, g), y)
+    for s in range(T * topk):
+        e, t = ids[s], s // topk
+        codes = o.unpack_awq(qw[e]); zeros = o.unpack_awq(qz[e])
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[t, k])) * (int(codes[k, n]) - int(zeros[k // g, n])) * \
+                       Fraction(float(sc[e, k // g, n]))
+            assert abs(float(acc) - y[s, n]) <= 1e-12 * max(1.0, abs(float(acc))), (s, n)
+
+
 def pin_rtn_hand_example(o):
     """tests/golden/rtn_example.json: one group of 4 rows, 8 equal columns, worked by hand
     from the quantizer table (asymmetric and symmetric)."""
@@ -393,6 +438,6 @@ def pin_rtn_error_bound(o):
                 assert (sc.astype(np.float64) > 0).all()
 
 
-ALL_PINS = [pin_bf16_conversion, pin_gemm_bf16_widening, pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
+ALL_PINS = [pin_moe_align, pin_moe_gemm, pin_bf16_conversion, pin_gemm_bf16_widening, pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
             pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
             pin_special_cases, pin_entries_agree, pin_format_rules]

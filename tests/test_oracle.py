@@ -54,6 +54,10 @@ MUTANTS = [
      "    _, G", 0),
     ("pack shifts by the column index",
      "<< np.uint32(4 * i)", "<< np.uint32(4 * AWQ_ORDER[i])", 0),
+    ("MoE slot uses the slot index as the token",
+     "gemm_ref(x[rows // topk], qweights[e]", "gemm_ref(x[rows % x.shape[0]], qweights[e]", 0),
+    ("MoE align fills experts from the end",
+     "        sorted_slots[cursor[e]] = s\n        cursor[e] += 1", "        cursor[e] += 1\n        sorted_slots[cursor[e] - 1] = ids.size - 1 - s", 0),
     ("bf16 widened with a 15-bit shift",
      "(b.astype(np.uint32) << np.uint32(16))", "(b.astype(np.uint32) << np.uint32(15))", 0),
     ("bf16 rounding truncates",
