@@ -144,3 +144,54 @@ def make_weights(K: int, N: int, seed: int = 0, std: float = 0.02, outlier_cols:
         idx = rng.choice(N, size=outlier_cols, replace=False)
         w[:, idx] *= outlier_gain
     return w.astype(np.float16)
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    """Routed-expert layer: T tokens, each sent to topk distinct experts of E; every
+    expert holds one AWQ GEMM-layout weight [K, N] (group size g)."""
+    name: str
+    T: int
+    E: int
+    topk: int
+    K: int
+    N: int
+    group_size: int
+    seed: int = 0
+
+    @property
+    def slots(self) -> int:
+        return self.T * self.topk
+
+    @property
+    def groups(self) -> int:
+        return 1 if self.group_size == -1 else self.K // self.group_size
+
+
+# An 8-expert top-2 layer with 4096-wide tokens and 14336-wide expert projections
+# (the shape class of the pages' 7B-scale models, extended to routed experts).
+MOE_WORKLOADS = {w.name: w for w in [
+    MoeWorkload("moe_decode_t16_e8_top2_k4096_n14336_g128", 16, 8, 2, 4096, 14336, 128),
+    MoeWorkload("moe_prefill_t1024_e8_top2_k4096_n14336_g128", 1024, 8, 2, 4096, 14336, 128),
+]}
+
+
+def make_moe_inputs(w: MoeWorkload, seed: int | None = None) -> dict:
+    """Draw order (one Generator): per expert e = 0..E-1 its qweight words, qzeros
+    words and scales (as make_inputs); then x standard normal [T, K] -> fp16; then per
+    token rng.choice(E, topk, replace=False) as its experts (slot t * topk + j)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    G = w.groups
+    qw, qz, sc = [], [], []
+    for _ in range(w.E):
+        qw.append(random_words(rng, (w.K, w.N // 8)))
+        qz.append(random_words(rng, (G, w.N // 8)))
+        sc.append(rng.uniform(1e-3, 2e-2, size=(G, w.N)).astype(np.float16))
+    x = rng.standard_normal((w.T, w.K)).astype(np.float16)
+    ids = np.stack([rng.choice(w.E, size=w.topk, replace=False) for _ in range(w.T)]).astype(np.int32).ravel()
+    return dict(x=x, qweight=np.stack(qw), qzeros=np.stack(qz), scales=np.stack(sc), expert_ids=ids,
+                topk=w.topk, group_size=w.group_size)
+
+
+def make_moe_custom(T, E, topk, K, N, group_size, seed=0) -> dict:
+    return make_moe_inputs(MoeWorkload(f"moe_custom_t{T}_e{E}_top{topk}", T, E, topk, K, N, group_size, seed))
