@@ -163,6 +163,52 @@ int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qze
                   void* y_bf16, struct ihipStream_t* stream);
 
 /*
+ * Routed experts (MoE).  vLLM's AWQ support runs a routed-expert layer on a 4-bit
+ * WNA16 MoE kernel over per-expert qweight / qzeros / scales (vLLM article, section
+ * 5.4).  Here: T tokens, each routed to topk experts of E; routed slot s = t * topk
+ * + j (token t = s / topk) computes
+ *   y[s, :] = x[t, :] . dequant(W[expert_ids[s]])      (fp16, fp32 accumulation)
+ * The expert's activation function and the weighted sum over a token's topk slots
+ * come after this product and are not part of it.
+ *
+ * awq_moe_tiles: table entries for S = T * topk slots, E experts and tiles of
+ * block_rows rows: ceil(S / block_rows) + E (an upper bound of sum over experts of
+ * ceil(count / block_rows)); -1 for invalid arguments.  Host-only.
+ *
+ * awq_moe_align: counting sort of the S slots by expert (device).
+ *   expert_ids    device int32 [S]; ids outside [0, E) are not routed
+ *   offsets       device int32 [E + 1]: expert e owns sorted rows offsets[e] .. offsets[e+1]-1
+ *   sorted_slots  device int32 [S]: slot ids grouped by expert (order within an
+ *                 expert unspecified; entries past offsets[E] are not written)
+ *   tile_table    device int32 [awq_moe_tiles(S, E, block_rows)][4], 16-byte aligned:
+ *                 (expert, first sorted row, rows, 0) per tile of at most block_rows
+ *                 rows, then (-1, 0, 0, 0)
+ *   1 <= E <= 1024, S < 2^30.  Returns AWQ_OK or an error status.
+ *
+ * awq_moe_gemm: the grouped product, one call (alignment, then one launch of the
+ * MFMA tile kernel in which each workgroup gathers the x rows of one expert's tile
+ * and scatters its y rows).
+ *   x_f16        device fp16 [T, K]
+ *   qweight      device int32 [E, K, N/8];  qzeros int32 [E, G, N/8];  scales fp16 [E, G, N]
+ *   expert_ids   device int32 [T * topk]
+ *   y_f16        device fp16 [T * topk, N]; rows of slots with an id outside [0, E)
+ *                are left unwritten
+ * Limits: those of awq_gemm with M = T * topk, plus 1 <= E <= 1024, topk >= 1 and
+ * x below 4 GiB.  T == 0 enqueues nothing.  The alignment lives in the same
+ * library-owned per-(device, stream) workspace as awq_gemm's, with the same
+ * allocation rule.  The result is deterministic (each row depends only on its slot).
+ * Returns AWQ_OK or an error status.
+ */
+int64_t awq_moe_tiles(int64_t S, int64_t E, int64_t block_rows);
+int awq_moe_align(const int32_t* expert_ids, int64_t S, int64_t E, int64_t block_rows,
+                  int32_t* offsets, int32_t* sorted_slots, int32_t* tile_table,
+                  struct ihipStream_t* stream);
+int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
+                 const void* scales_f16, const int32_t* expert_ids,
+                 int64_t T, int64_t topk, int64_t E, int64_t K, int64_t N, int64_t group_size,
+                 void* y_f16, struct ihipStream_t* stream);
+
+/*
  * Round-to-nearest writer of the GEMM pack: quantise an fp16 weight in groups of
  * group_size input rows per output column.  Source: GPTQModel wiki "AWQ", section
  * "Group quantization and zero points" (both quantizers, the clamp of the zero, the

@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     AWQ_ERR_HIP, AwqError, LIB_PATH, load as load_library, status_string,
 )
 from .linear import (  # noqa: F401
-    AwqLinear, awq_dequant, awq_gemm, awq_quantize_rtn, group_size_from_config, plan, validate,
+    AwqLinear, awq_dequant, awq_gemm, awq_moe_align, awq_moe_gemm, awq_quantize_rtn, group_size_from_config, plan, validate,
 )

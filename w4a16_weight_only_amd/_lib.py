@@ -30,6 +30,9 @@ SIGNATURES = {
     "awq_dequant_f16": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "awq_quantize_rtn": (ctypes.c_int, [_vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]),
+    "awq_moe_tiles": (ctypes.c_int64, [_i64, _i64, _i64]),
+    "awq_moe_align": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "awq_moe_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
     "awq_gemm_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]),
     "awq_gemm_plan": (ctypes.c_int, [_i64, _i64, _i64, _i64,
                                      ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),

@@ -367,6 +367,61 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
 }
 }  // namespace
 
+int64_t awq_moe_tiles(int64_t S, int64_t E, int64_t block_rows) {
+  if (S < 0 || E < 1 || block_rows < 1) return -1;
+  return (S + block_rows - 1) / block_rows + E;
+}
+
+int awq_moe_align(const int32_t* expert_ids, int64_t S, int64_t E, int64_t block_rows, int32_t* offsets,
+                  int32_t* sorted_slots, int32_t* tile_table, struct ihipStream_t* stream) {
+  if (S < 0 || E < 1 || block_rows < 1) return AWQ_ERR_SHAPE;
+  if (E > 1024 || S >= (int64_t(1) << 30)) return AWQ_ERR_UNSUPPORTED;
+  if (!offsets || !tile_table || (S > 0 && (!expert_ids || !sorted_slots))) return AWQ_ERR_NULL;
+  if (!aligned16(tile_table)) return AWQ_ERR_ALIGN;
+  const int64_t tiles = awq_moe_tiles(S, E, block_rows);
+  hipError_t e = awq::launch_moe_align(expert_ids, (int)S, (int)E, (int)block_rows, (int)tiles, offsets, sorted_slots,
+                                       tile_table, stream);
+  return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+
+int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                 const int32_t* expert_ids, int64_t T, int64_t topk, int64_t E, int64_t K, int64_t N,
+                 int64_t group_size, void* y_f16, struct ihipStream_t* stream) {
+  if (T < 0 || topk < 1 || E < 1) return AWQ_ERR_SHAPE;
+  int st = limits_check(T * topk, K, N, group_size);
+  if (st != AWQ_OK) return st;
+  if (E > 1024 || T * topk >= (int64_t(1) << 30)) return AWQ_ERR_UNSUPPORTED;
+  if (T * K * 2 >= (int64_t(1) << 32)) return AWQ_ERR_UNSUPPORTED;  // gathered rows use 32-bit offsets
+  if (T == 0) return AWQ_OK;
+  if (!x_f16 || !qweight || !qzeros || !scales_f16 || !expert_ids || !y_f16) return AWQ_ERR_NULL;
+  if (!aligned16(x_f16) || !aligned16(qweight) || !aligned16(qzeros) || !aligned16(scales_f16) || !aligned16(y_f16))
+    return AWQ_ERR_ALIGN;
+  const int64_t S = T * topk;
+  const int g = eff_group(K, group_size);
+  const int64_t G = K / g;
+  int block_rows = 0;
+  const int variant = awq::moe_tile_variant(S / E, &block_rows);
+  const int64_t tiles = awq_moe_tiles(S, E, block_rows);
+  const int64_t bn = awq::kTileBN[variant];
+  if (tiles * ((N + bn - 1) / bn) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  // Scratch: tile table (16-byte entries), offsets, sorted slots; written by the
+  // alignment kernel before the product reads it, on the same stream.
+  void* scratch = nullptr;
+  st = get_scratch(tiles * 16 + (E + 1 + S + 4) * 4, stream, &scratch);
+  if (st != AWQ_OK) return st;
+  int32_t* table = static_cast<int32_t*>(scratch);
+  int32_t* offsets = table + 4 * tiles;
+  int32_t* sorted = offsets + E + 1;
+  hipError_t e = awq::launch_moe_align(expert_ids, (int)S, (int)E, block_rows, (int)tiles, offsets, sorted, table,
+                                       stream);
+  if (e != hipSuccess) return AWQ_ERR_HIP;
+  awq::MoeTiles moe{sorted, table, (int)topk, (int)tiles, K * (N / 8), G * (N / 8), G * N};
+  e = awq::launch_tile_grouped(static_cast<const uint16_t*>(x_f16), qweight, qzeros,
+                               static_cast<const uint16_t*>(scales_f16), (int)K, (int)N, g, variant, moe,
+                               static_cast<uint16_t*>(y_f16), stream);
+  return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+}
+
 int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
              const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
              struct ihipStream_t* stream) {

@@ -41,6 +41,30 @@ struct TilePlan {
   int kps;     // k-tiles of kTileBK per split
 };
 
+// Routed experts: the tile kernel's grouped mode.  Workgroup b takes table entry
+// b % tiles and column tile b / tiles; an entry is (expert, first sorted row, rows,
+// 0), with expert < 0 for an unused entry (the workgroup exits).  Row r of the entry
+// is routed slot sorted_slots[first + r], which reads x row slot / topk and writes
+// y row slot.  Expert e's weights start e * w_stride words into qweight (and
+// likewise for qzeros and scales).
+struct MoeTiles {
+  const int32_t* sorted_slots;
+  const int32_t* table;
+  int topk;
+  int tiles;
+  int64_t w_stride, z_stride, s_stride;
+};
+// Tile rows of the grouped variant picked for an average of `avg_rows` slots per
+// expert, and the variant itself.
+int moe_tile_variant(int64_t avg_rows, int* block_rows);
+// Counting sort of S slots by expert into offsets [E + 1], sorted_slots [S] and the
+// tile table [tiles][4] (tiles = ceil(S / block_rows) + E), one workgroup.
+hipError_t launch_moe_align(const int32_t* expert_ids, int S, int E, int block_rows, int tiles,
+                            int32_t* offsets, int32_t* sorted_slots, int32_t* table, hipStream_t stream);
+hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                               const uint16_t* scales, int K, int N, int g, int variant, const MoeTiles& moe,
+                               uint16_t* y, hipStream_t stream);
+
 // out: float32 [K, N] (f16 = false) or fp16 [K, N] (f16 = true).
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, void* out, bool f16, hipStream_t stream);

@@ -87,12 +87,15 @@ __device__ __forceinline__ uint32_t b_pair(uint32_t magic_pair, half2v mult, hal
   else return as_u32(qz * sc);
 }
 
-template <int FM, int FN, int WM, int KG, bool BF16>
+// GROUPED: routed-expert mode (MoeTiles): each workgroup takes one table entry's
+// rows of one expert, gathers their x rows and scatters its y rows; no bias, no K
+// splits.
+template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false>
 __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
     const uint16_t* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
-    float* __restrict__ partial, uint16_t* __restrict__ y) {
+    float* __restrict__ partial, uint16_t* __restrict__ y, MoeTiles moe) {
   constexpr int THREADS = 256 * KG;   // KG groups of 4 waves; group kg takes k16 steps of its share
   constexpr int WN = 4 / WM;          // waves along N
   constexpr int BM = WM * 32 * FM;    // workgroup rows
@@ -138,8 +141,22 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int kg = wave >> 2;           // k-group
   const int w4 = wave & 3;            // wave within the group
   const int wm = w4 / WN, wn = w4 % WN;
-  const int tile_m = blockIdx.x % m_tiles;
-  const int tile_n = blockIdx.x / m_tiles;
+  int tile_m = blockIdx.x % m_tiles;
+  int tile_n = blockIdx.x / m_tiles;
+  int first = 0;  // grouped: first sorted row of this workgroup's entry
+  if constexpr (GROUPED) {
+    const int ti = blockIdx.x % moe.tiles;
+    tile_n = blockIdx.x / moe.tiles;
+    tile_m = 0;
+    const int* ent = moe.table + 4 * ti;
+    const int e = ent[0];
+    if (e < 0) return;  // an unused entry: the whole workgroup leaves before any barrier
+    first = ent[1];
+    M = ent[2];         // rows of this entry (1 .. BM); rows are entry-local from here on
+    qweight += e * moe.w_stride;
+    qzeros += e * moe.z_stride;
+    scales += e * moe.s_stride;
+  }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
@@ -166,9 +183,18 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const int grp = wave * IPW + j;
     const int lch = (lane & 7) ^ (((8 * grp + lrow) >> 1) & 7);
     const int a_ch = K < kBK ? (lch & 3) : lch;
-    a_row0[j] = min(m0 + 8 * grp, M - 1);
-    const int t = min(lrow, M - 1 - a_row0[j]);
-    a_off[j] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
+    if constexpr (GROUPED) {
+      // Gathered: row r of the entry is token sorted_slots[first + r] / topk (x below
+      // 4 GiB, checked by the host).
+      const int r = min(8 * grp + lrow, M - 1);
+      const int tok = moe.sorted_slots[first + r] / moe.topk;
+      a_row0[j] = 0;
+      a_off[j] = ((uint32_t)tok * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
+    } else {
+      a_row0[j] = min(m0 + 8 * grp, M - 1);
+      const int t = min(lrow, M - 1 - a_row0[j]);
+      a_off[j] = ((uint32_t)t * (uint32_t)K + 8u * (uint32_t)a_ch) * 2u;
+    }
   }
   // Packed weights and group data also go straight to LDS: NB wave loads of 16 rows
   // (BW = 16) or 32 rows (BW = 8) for the weights, one for the group data, spread over
@@ -538,9 +564,10 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   for (int q = tid; q < BM * PR; q += THREADS) {
     const int row = q / PR, p = q % PR;
     const int grow = m0 + row, gcol = n0 + 8 * p;
-    if (grow < M && gcol < N)
-      *reinterpret_cast<u32x4*>(&y[(int64_t)grow * N + gcol]) =
-          *reinterpret_cast<const u32x4*>(&Ys[row * YLD + 8 * p]);
+    if (grow < M && gcol < N) {
+      const int64_t orow = GROUPED ? (int64_t)moe.sorted_slots[first + grow] : (int64_t)grow;  // scattered
+      *reinterpret_cast<u32x4*>(&y[orow * N + gcol]) = *reinterpret_cast<const u32x4*>(&Ys[row * YLD + 8 * p]);
+    }
   }
 }
 
@@ -582,7 +609,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(threads), 0,
                        stream, x, reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        reinterpret_cast<const _Float16*>(scales), bias, M, K, N, g, m_tiles, p.kps,
-                       split ? partial : nullptr, y);
+                       split ? partial : nullptr, y, MoeTiles{});
   };
   switch (p.variant) {
     case 0: go(tile_kernel<8, 1, 1, 2, BF16>, 256, 128, 512); break;
@@ -595,6 +622,30 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   const int64_t blocks = (MN / 8 + 255) / 256;
   hipLaunchKernelGGL(tile_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N,
                      p.splits, y);
+  return hipGetLastError();
+}
+
+int moe_tile_variant(int64_t avg_rows, int* block_rows) {
+  const int v = avg_rows >= 192 ? 0 : (avg_rows >= 96 ? 1 : 2);
+  *block_rows = kTileBM[v];
+  return v;
+}
+
+hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                               const uint16_t* scales, int K, int N, int g, int variant, const MoeTiles& moe,
+                               uint16_t* y, hipStream_t stream) {
+  auto go = [&](auto kern, int bn, int threads) {
+    const int n_tiles = (N + bn - 1) / bn;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)moe.tiles * n_tiles), 1u), dim3(threads), 0, stream, x,
+                       reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
+                       reinterpret_cast<const _Float16*>(scales), nullptr, 0, K, N, g, 1, (K + kBK - 1) / kBK,
+                       nullptr, y, moe);
+  };
+  switch (variant) {
+    case 0: go(tile_kernel<8, 1, 1, 2, false, true>, 128, 512); break;
+    case 1: go(tile_kernel<2, 1, 2, 1, false, true>, 64, 256); break;
+    default: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;
+  }
   return hipGetLastError();
 }
 

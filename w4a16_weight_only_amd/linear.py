@@ -174,6 +174,63 @@ def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scale
     return out
 
 
+def awq_moe_align(expert_ids: torch.Tensor, num_experts: int, block_rows: int) -> tuple:
+    """Counting sort of routed slots by expert: (offsets [E + 1], sorted_slots [S],
+    tile_table [tiles, 4]) as int32 device tensors."""
+    _check_tensor("expert_ids", expert_ids, torch.int32)
+    dev = expert_ids.device
+    S = expert_ids.numel()
+    lib = _lib.load()
+    tiles = lib.awq_moe_tiles(S, num_experts, block_rows)
+    if tiles < 0:
+        _lib.check(_lib.AWQ_ERR_SHAPE, "awq_moe_align")
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    sorted_slots = torch.full((max(S, 1),), -1, dtype=torch.int32, device=dev)[:S]
+    table = torch.empty((tiles, 4), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.awq_moe_align(_ptr(expert_ids), S, num_experts, block_rows, _ptr(offsets), _ptr(sorted_slots),
+                               _ptr(table), _stream(dev))
+    _lib.check(st, "awq_moe_align")
+    return offsets, sorted_slots, table
+
+
+def awq_moe_gemm(x: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
+                 expert_ids: torch.Tensor, group_size: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed-expert product: x [T, K] fp16, stacked expert weights qweight [E, K, N/8],
+    qzeros [E, G, N/8], scales [E, G, N], expert_ids int32 [T, topk] (or [T * topk]);
+    returns y [T * topk, N] (slot s = t * topk + j) with y[s] = x[t] . dequant(W[id])."""
+    _check_tensor("x", x, torch.float16)
+    dev = x.device
+    _check_tensor("qweight", qweight, torch.int32, dev)
+    _check_tensor("qzeros", qzeros, torch.int32, dev)
+    _check_tensor("scales", scales, torch.float16, dev)
+    _check_tensor("expert_ids", expert_ids, torch.int32, dev)
+    if x.dim() != 2 or qweight.dim() != 3 or qzeros.dim() != 3 or scales.dim() != 3:
+        raise ValueError("x must be [T, K]; qweight, qzeros, scales stacked per expert")
+    T, K = x.shape
+    E, N = qweight.shape[0], qweight.shape[2] * 8
+    if qweight.shape[1] != K or qzeros.shape[0] != E or scales.shape[0] != E:
+        raise ValueError("expert weight shapes disagree with x")
+    validate(K, N, group_size, qweight[0], qzeros[0], scales[0])
+    S = expert_ids.numel()
+    if T == 0 or S % T != 0:
+        if T == 0 and S == 0:
+            return torch.empty((0, N), dtype=torch.float16, device=dev) if out is None else out
+        raise ValueError("expert_ids must hold the same number of experts for every token")
+    topk = S // T
+    if out is None:
+        out = torch.empty((S, N), dtype=torch.float16, device=dev)
+    else:
+        _check_tensor("out", out, torch.float16, dev)
+        if tuple(out.shape) != (S, N):
+            raise ValueError(f"out must be [{S}, {N}]")
+    with torch.cuda.device(dev):
+        st = _lib.load().awq_moe_gemm(_ptr(x), _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(expert_ids), T, topk,
+                                      E, K, N, group_size, _ptr(out), _stream(dev))
+    _lib.check(st, "awq_moe_gemm")
+    return out
+
+
 class AwqLinear(torch.nn.Module):
     """Inference-only linear layer holding one AWQ GEMM-layout weight."""
 
