@@ -231,6 +231,58 @@ def time_quantize_rtn(K, N, g, sym, steps, torch, awq, synth):
                 algorithmic_bytes=nbytes, achieved_gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
 
 
+def time_moe(name, steps, torch, awq, synth):
+    """awq_moe_gemm on a routed-expert workload, same protocol (expert weights rotated
+    over >= 512 MB, one graph replay timed with HIP events).  Algorithmic bytes: the
+    packed weights, zeros and scales of every expert that receives a slot, x once and
+    y once; FLOPs 2 * slots * K * N."""
+    w = synth.MOE_WORKLOADS[name]
+    d = synth.make_moe_inputs(w)
+    dev = torch.device("cuda", 0)
+    active = np.unique(d["expert_ids"]).size
+    per_expert = (d["qweight"][0].nbytes + d["qzeros"][0].nbytes + d["scales"][0].nbytes)
+    nbytes = active * per_expert + d["x"].nbytes + w.slots * w.N * 2
+    flops = 2 * w.slots * w.K * w.N
+    copies = max(1, -(-ROTATE_BYTES // (w.E * per_expert)))
+    x = torch.from_numpy(d["x"]).to(dev)
+    ids = torch.from_numpy(d["expert_ids"].reshape(w.T, w.topk)).to(dev)
+    weights = [tuple(torch.from_numpy(d[k]).to(dev) for k in ("qweight", "qzeros", "scales")) for _ in range(copies)]
+    y = torch.empty((w.slots, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(dev)
+
+    def step(i):
+        qw, qz, sc = weights[i % copies]
+        awq.awq_moe_gemm(x, qw, qz, sc, ids, w.group_size, out=y)
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            step(i)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        stream.synchronize()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    s_per = ev0.elapsed_time(ev1) / 1e3 / steps
+    del weights, graph
+    torch.cuda.empty_cache()
+    gbs, tfs = nbytes / s_per / 1e9, flops / s_per / 1e12
+    mfma_bound = flops / nbytes > (FP16_MFMA_PEAK_TFS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    roof = (dict(bound="mfma", achieved=round(tfs, 2), peak=FP16_MFMA_PEAK_TFS, unit="TFLOP/s", frac=round(tfs / FP16_MFMA_PEAK_TFS, 4))
+            if mfma_bound else dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                    frac=round(gbs / HBM_PEAK_GBS, 4)))
+    return dict(workload=name, active_experts=int(active), call_us=round(s_per * 1e6, 3), algorithmic_bytes=nbytes,
+                flops=flops, roofline=roof, note="one call = alignment kernel + grouped tile kernel")
+
+
 def read_ceiling(nbytes, torch, steps=400):
     """A plain streaming read of the same byte count for comparison: the probe
     library's read kernel (16-byte nontemporal loads, 16 KiB contiguous per
@@ -399,6 +451,8 @@ def main():
             v, u, rf, pl = summarize(rs, n_steps)
             bf.append(dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3), roofline=rf))
         out["bf16"] = bf
+        # Routed experts (awq_moe_gemm).
+        out["moe"] = [time_moe(name, min(args.steps, 50), torch, awq, synth) for name in synth.MOE_WORKLOADS]
         # The RTN writer (fp16 weight -> GEMM pack), HBM-bound.
         out["writer"] = [time_quantize_rtn(K, N, g, sym, min(args.steps, 100), torch, awq, synth)
                          for (K, N, g, sym) in ((4096, 4096, 128, False), (4096, 4096, 128, True),

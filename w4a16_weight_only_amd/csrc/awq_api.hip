@@ -402,7 +402,7 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
   int block_rows = 0;
   const int variant = awq::moe_tile_variant(S / E, &block_rows);
   const int64_t tiles = awq_moe_tiles(S, E, block_rows);
-  const int64_t bn = awq::kTileBN[variant];
+  const int64_t bn = variant < awq::kTileVariants ? awq::kTileBN[variant] : 128;
   if (tiles * ((N + bn - 1) / bn) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
   // Scratch: tile table (16-byte entries), offsets, sorted slots; written by the
   // alignment kernel before the product reads it, on the same stream.

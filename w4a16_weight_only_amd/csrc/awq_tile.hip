@@ -625,9 +625,13 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   return hipGetLastError();
 }
 
+// Grouped variants by slots per expert: 256 x 128 from 192, 128 x 64 from 96,
+// 64 x 128 above 32, and 32 x 128 (variant 3, grouped mode only) for the few rows
+// per expert of decode-sized batches, where the weights dominate and a smaller x
+// tile lets four workgroups share a CU.
 int moe_tile_variant(int64_t avg_rows, int* block_rows) {
-  const int v = avg_rows >= 192 ? 0 : (avg_rows >= 96 ? 1 : 2);
-  *block_rows = kTileBM[v];
+  const int v = avg_rows >= 192 ? 0 : (avg_rows >= 96 ? 1 : (avg_rows > 32 ? 2 : 3));
+  *block_rows = v == 3 ? 32 : kTileBM[v];
   return v;
 }
 
@@ -644,7 +648,8 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
   switch (variant) {
     case 0: go(tile_kernel<8, 1, 1, 2, false, true>, 128, 512); break;
     case 1: go(tile_kernel<2, 1, 2, 1, false, true>, 64, 256); break;
-    default: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;
+    case 2: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;
+    default: go(tile_kernel<1, 1, 1, 1, false, true>, 128, 256); break;  // 32 x 128
   }
   return hipGetLastError();
 }
