@@ -147,6 +147,33 @@ def test_quantize_rtn_argument_errors_touch_no_device(lib):
     assert q(p, 4096, 4096, 128, 1, p, odd, p, None) == _lib.AWQ_ERR_ALIGN
 
 
+def test_moe_and_bf16_argument_errors_touch_no_device(lib):
+    """Routed-expert and bfloat16 entry points check their arguments before any HIP call."""
+    p = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.awq_moe_tiles(2048, 8, 256) == 8 + 8
+    assert lib.awq_moe_tiles(1, 8, 32) == 1 + 8
+    assert lib.awq_moe_tiles(10, 0, 32) == -1
+    a = lib.awq_moe_align
+    assert a(p, 10, 0, 32, p, p, p, None) == _lib.AWQ_ERR_SHAPE
+    assert a(p, 10, 1025, 32, p, p, p, None) == _lib.AWQ_ERR_UNSUPPORTED
+    assert a(None, 10, 8, 32, p, p, p, None) == _lib.AWQ_ERR_NULL
+    assert a(p, 10, 8, 32, p, p, odd, None) == _lib.AWQ_ERR_ALIGN
+    g = lib.awq_moe_gemm
+    assert g(p, p, p, p, p, 0, 2, 8, 4096, 4096, 128, p, None) == _lib.AWQ_OK  # no tokens: nothing to do
+    assert g(p, p, p, p, p, 4, 0, 8, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_SHAPE
+    assert g(p, p, p, p, p, 4, 2, 2000, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_UNSUPPORTED
+    assert g(p, p, p, p, p, 4, 2, 8, 4096, 4096, 100, p, None) == _lib.AWQ_ERR_GROUP
+    assert g(p, p, p, p, None, 4, 2, 8, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_NULL
+    assert g(odd, p, p, p, p, 4, 2, 8, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
+    assert g(p, p, p, p, p, 1 << 20, 2, 8, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_UNSUPPORTED  # x >= 4 GiB
+    b = lib.awq_gemm_bf16
+    assert b(p, p, p, p, None, 0, 4096, 4096, 128, p, None) == _lib.AWQ_OK
+    assert b(None, p, p, p, None, 1, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_NULL
+    assert b(p, p, p, p, odd, 1, 4096, 4096, 128, p, None) == _lib.AWQ_ERR_ALIGN
+    assert b(p, p, p, p, None, 1, 4096, 4096, 16, p, None) == _lib.AWQ_ERR_UNSUPPORTED
+
+
 def test_quantization_config():
     cfg = {"quant_method": "awq", "bits": 4, "group_size": 64, "zero_point": True, "version": "gemm"}
     assert awq.group_size_from_config(cfg) == 64
