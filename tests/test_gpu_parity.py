@@ -113,6 +113,23 @@ def test_gemm_ragged(M, K, N, g, bias):
     tol_check(gemm(d), yref, f"M{M}K{K}N{N}g{g}")
 
 
+LARGE = [  # (M, K, N, g): extreme grid shapes (the oracle stays cheap with small K or N)
+    (8192, 256, 1024, 128),      # 32 x 8 tiles of 256 x 128, every M tile full
+    (8190, 128, 256, -1),        # last M tile with 254 rows
+    (1, 64, 131072, 32),         # 512 skinny column tiles
+    (40, 96, 131072, 32),        # 2048 column tiles of the 64 x 128 variant
+    (300, 32768, 64, 128),       # long K on the tile family, split over K
+]
+
+
+@pytest.mark.parametrize("M,K,N,g", LARGE)
+def test_gemm_large_grids(M, K, N, g):
+    print(f"large M={M} K={K} N={N} g={g} plan={awq.plan(M, K, N, g)}", flush=True)
+    d = synth.make_custom(M, K, N, g, bias=True, seed=M + N)
+    yref = oracle.gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g)
+    tol_check(gemm(d), yref, f"large M{M}K{K}N{N}")
+
+
 @pytest.mark.parametrize("M,K,N,g", [(5, 352, 800, 32), (2, 11008, 32, -1)])
 def test_dequant_ragged_negative_scales(M, K, N, g):
     """Negative scales make (q - z) == 0 a negative zero: bits must still agree."""
