@@ -130,6 +130,29 @@ def test_gemm_large_grids(M, K, N, g):
     tol_check(gemm(d), yref, f"large M{M}K{K}N{N}")
 
 
+LAYERS = [  # (M, K, N, g): full-size layers whose grids span several rounds of resident workgroups
+    (1, 8192, 28672, 128),       # one or two rows: every wave's run held inside one group
+    (2, 4096, 114688, 128),
+    (1, 28672, 8192, 128),       # 56 K splits
+    (4, 8192, 28672, 128),       # four rows: runs over several groups (LDS tables)
+    (16, 4096, 114688, 128),     # 8-wave workgroups, fp32 partials
+]
+
+
+@pytest.mark.parametrize("M,K,N,g", LAYERS)
+def test_gemm_layer_sampled_entries(M, K, N, g):
+    """Every row at 520 output columns (spread over N, first and last included), each
+    entry from the oracle's one-column dot product."""
+    print(f"layer M={M} K={K} N={N} g={g} plan={awq.plan(M, K, N, g)}", flush=True)
+    d = synth.make_custom(M, K, N, g, bias=True, seed=M + K + N)
+    y = gemm(d)
+    cols = np.unique(np.concatenate([np.linspace(0, N - 1, 512).astype(np.int64), np.arange(N - 8, N)]))
+    rows = np.repeat(np.arange(M), len(cols))
+    yref = oracle.gemm_ref_entries(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g,
+                                   rows, np.tile(cols, M)).reshape(M, len(cols))
+    tol_check(y[:, cols], yref, f"layer M{M}K{K}N{N}")
+
+
 @pytest.mark.parametrize("M,K,N,g", [(5, 352, 800, 32), (2, 11008, 32, -1)])
 def test_dequant_ragged_negative_scales(M, K, N, g):
     """Negative scales make (q - z) == 0 a negative zero: bits must still agree."""

@@ -83,8 +83,10 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   s.waves = M <= 4 ? 4 : 8;
   s.mrows = M <= 4 ? 4 : 16;
   const int64_t W = s.waves;
-  // Whole grid resident in one round: 4-wave workgroups fit two per CU, 8-wave ones
-  // (large LDS reduction buffer) one per CU.
+  // Whole grid resident in one round, counting two 4-wave workgroups per CU (three
+  // fit when every wave stays inside one group; counting three gives more splits,
+  // which measured slower at four rows) and one 8-wave workgroup (large LDS
+  // reduction buffer).
   const int64_t cap = s.waves == 4 ? (int64_t)cus * AWQ_SKINNY_WG_PER_2CU / 2 : (int64_t)cus;
   int64_t L = (T * s.n_tiles + W * cap - 1) / (W * cap);
   const int64_t l_min = (T + W * awq::kSkinnyMaxSplits - 1) / (W * awq::kSkinnyMaxSplits);
@@ -94,6 +96,12 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   // at half the workgroups).
   if (L < 2) L = 2;
   if (L > T) L = T;
+  // One or two rows on a grid of more than two rounds: keep each wave's run inside
+  // one group (at most 4 k-steps).  Such waves need no per-group LDS tables and
+  // fewer registers, so three workgroups share a compute unit, and the extra splits
+  // cost one atomic per output element each; with more rows the atomics outweigh
+  // the gain (measured on 4096 x 114688, 8192 x 28672 and 28672 x 8192 layers).
+  if (M <= 2 && gsteps < T && L > gsteps && T * s.n_tiles > W * cap * 2) L = gsteps < 4 ? gsteps : 4;
   auto splits_of = [&](int64_t l) { return (T + W * l - 1) / (W * l); };
   if (gsteps >= T) {
     s.single_group = true;  // one group spans K

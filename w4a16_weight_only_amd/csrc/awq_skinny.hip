@@ -137,14 +137,17 @@ __device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[
 // the 16-byte reads of the 16 column lanes over the banks).
 constexpr int kTabStride = 20;
 
-template <int WAVES>
+// red: per wave, accumulator and lane; with at most 4 rows only lanes 0..15 (rows
+// 0..3) hold rows that are stored, so RL = 16 lanes are kept, a quarter of the LDS,
+// which lets a third 4-wave workgroup share a compute unit.
+template <int WAVES, int RL>
 struct SkinnyLds {
   union {
     struct {
       uint32_t zsplat[kSkinnyMaxGroups][16][kTabStride];
       float scale[kSkinnyMaxGroups][16][kTabStride];
     } meta;
-    floatx4 red[WAVES][16][64];  // [wave][accumulator][lane]
+    floatx4 red[WAVES][16][RL];  // [wave][accumulator][lane]
   } u;
 };
 
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
   constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
   constexpr bool ATOMIC = WAVES == 4 && !BF16;
-  __shared__ SkinnyLds<WAVES> sh;
+  __shared__ SkinnyLds<WAVES, (MROWS > 4 ? 64 : 16)> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
