@@ -90,19 +90,29 @@ def test_plan_families():
     assert p16["family"] == "skinny"
     p2048 = awq.plan(2048, 4096, 4096, 128)
     assert p2048["family"] == "tile" and p2048["workspace_bytes"] == 0 and p2048["splits"] == 1
-    assert p2048["grid"] == (8 * 32, 1)
+    assert p2048["grid"] == (8 * 32, 1)  # 8 x 32 tiles: the XCD runs need no padding
+
+
+def tile_blocks(M, N, tile_rows, tile_cols):
+    """Launched tile grid: the column tiles sharing a 128-byte weight line (256 //
+    tile_cols of them) form a run; row tiles x runs, padded to whole groups of 8 runs
+    (one per XCD), each of 256 // tile_cols blocks."""
+    ct = 256 // tile_cols
+    units = -(-M // tile_rows) * -(-(-(-N // tile_cols)) // ct)
+    return 8 * ct * -(-units // 8)
 
 
 @pytest.mark.parametrize("M,K,N,g,tile_rows,tile_cols", [
     (64, 11008, 4096, 64, 64, 128), (512, 11008, 4096, 64, 256, 128), (100, 2080, 160, -1, 128, 64)])
 def test_tile_split_k_plans(M, K, N, g, tile_rows, tile_cols):
-    """Below one tile per compute unit the tile family splits K: grid (tiles, splits),
-    every split keeps >= 8 k-tiles of 64 (or there is one split), the splits cover K
-    exactly, and the fp32 partial workspace holds splits x M x N."""
+    """The tile family splits K on few tiles: grid (tile blocks, splits), every split
+    keeps >= 8 k-tiles of 64 (or there is one split), the splits cover K exactly, and
+    the fp32 partial workspace holds splits x M x N."""
     p = awq.plan(M, K, N, g)
     tiles = -(-M // tile_rows) * -(-N // tile_cols)
     kt = -(-K // 64)
-    assert p["family"] == "tile" and p["grid"][0] == tiles and p["grid"][1] == p["splits"]
+    assert p["family"] == "tile" and p["grid"][0] == tile_blocks(M, N, tile_rows, tile_cols)
+    assert p["grid"][1] == p["splits"]
     assert p["splits"] > 1
     kps = -(-kt // p["splits"])
     assert kps >= 8 or p["splits"] == 1

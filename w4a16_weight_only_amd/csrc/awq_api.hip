@@ -145,26 +145,32 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     auto tiles = [&](int v) {
       return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
     };
-    // The large tile while it fills the device by itself; below that, the tile
-    // whose rows fit M best, and K split until the grid covers every compute unit
-    // (each split keeps at least 8 k-tiles).
+    // Row tile by M: 256 x 128 above 128 rows, 128 x 64 above 64, 64 x 128 below
+    // (the large tile on few rows wastes most of its MFMA rows and x loads).
+    // Above 128 rows the product is MFMA-bound: K is split only while the tiles
+    // leave compute units idle.  At or below 128 rows the weight stream dominates
+    // and K is split to about two workgroups per compute unit (rounded down;
+    // measured best over 1 to 4 per unit on 4096- to 28672-wide layers).  Every
+    // split keeps at least 8 k-tiles.
     const int64_t fill = (int64_t)cus * 3 / 4;
-    int v = 0;
-    if (tiles(0) < fill) v = M > 128 ? 0 : (M > 64 ? 1 : 2);
+    const int v = M > 128 ? 0 : (M > 64 ? 1 : 2);
     const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
     int64_t splits = 1;
-    if (tiles(v) < fill) {
-      splits = ((int64_t)cus + tiles(v) - 1) / tiles(v);
-      const int64_t max_splits = KT / 8 > 1 ? KT / 8 : 1;
-      if (splits > max_splits) splits = max_splits;
+    if (v == 0) {
+      if (tiles(v) < fill) splits = ((int64_t)cus + tiles(v) - 1) / tiles(v);
+    } else {
+      splits = 2 * (int64_t)cus / tiles(v);
+      if (splits < 1) splits = 1;
     }
+    const int64_t max_splits = KT / 8 > 1 ? KT / 8 : 1;
+    if (splits > max_splits) splits = max_splits;
     const int64_t kps = (KT + splits - 1) / splits;
     splits = (KT + kps - 1) / kps;
     p.tp.variant = v;
     p.block = awq::kTileThreads[v];
     p.tp.splits = (int)splits;
     p.tp.kps = (int)kps;
-    p.grid_x = (int)tiles(v);
+    p.grid_x = (int)awq::tile_blocks((M + awq::kTileBM[v] - 1) / awq::kTileBM[v], N, awq::kTileBN[v]);
     p.grid_y = (int)splits;
     if (splits > 1) p.partial_bytes = splits * M * N * 4;
   }

@@ -35,15 +35,20 @@ constexpr int kTileBM[kTileVariants] = {256, 128, 64};
 constexpr int kTileBN[kTileVariants] = {128, 64, 128};
 constexpr int kTileThreads[kTileVariants] = {512, 256, 256};
 constexpr int kTileBK = 64;
+// Blocks of a tile grid with row_units row tiles (or table entries): whole runs of
+// 8 * (256 / bn) blocks, so that the column tiles sharing 128-byte weight lines
+// fall on one XCD (the block order of tile_kernel); padding blocks exit at once.
+int64_t tile_blocks(int64_t row_units, int64_t N, int bn);
 struct TilePlan {
   int variant;
   int splits;  // K splits (1: direct fp16 output)
   int kps;     // k-tiles of kTileBK per split
 };
 
-// Routed experts: the tile kernel's grouped mode.  Workgroup b takes table entry
-// b % tiles and column tile b / tiles; an entry is (expert, first sorted row, rows,
-// 0), with expert < 0 for an unused entry (the workgroup exits).  Row r of the entry
+// Routed experts: the tile kernel's grouped mode.  Each workgroup takes one table
+// entry and one column tile (entries in place of row tiles in the block order of
+// tile_kernel); an entry is (expert, first sorted row, rows, 0), with expert < 0 for
+// an unused entry (the workgroup exits).  Row r of the entry
 // is routed slot sorted_slots[first + r], which reads x row slot / topk and writes
 // y row slot.  Expert e's weights start e * w_stride words into qweight (and
 // likewise for qzeros and scales).

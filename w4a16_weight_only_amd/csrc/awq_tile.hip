@@ -141,12 +141,23 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int kg = wave >> 2;           // k-group
   const int w4 = wave & 3;            // wave within the group
   const int wm = w4 / WN, wn = w4 % WN;
-  int tile_m = blockIdx.x % m_tiles;
-  int tile_n = blockIdx.x / m_tiles;
+  // Block order.  Workgroups go to the 8 XCDs in turn (block b to XCD b % 8), each
+  // XCD with its own L2; the CT = 256 / BN column tiles whose weights share the
+  // 128-byte lines of a row get blocks 8 apart, so that one XCD reads each line once
+  // for all of them, at about the same time.  Block b is unit u (row tile, or table
+  // entry, and a run of CT column tiles) and part p of the run; the grid is whole
+  // runs of 8 CT blocks, and blocks past the units or the columns leave at once.
+  constexpr int CT = 256 / BN;
+  const int bx = blockIdx.x;
+  const int u = (bx & 7) + 8 * (bx / (8 * CT));
+  const int row_units = GROUPED ? moe.tiles : m_tiles;
+  const int n_tiles = (N + BN - 1) / BN;
+  int tile_m = u % row_units;
+  const int tile_n = CT * (u / row_units) + (bx >> 3) % CT;
+  if (tile_n >= n_tiles) return;  // also every unit past the last (its tile_n is larger still)
   int first = 0;  // grouped: first sorted row of this workgroup's entry
   if constexpr (GROUPED) {
-    const int ti = blockIdx.x % moe.tiles;
-    tile_n = blockIdx.x / moe.tiles;
+    const int ti = tile_m;
     tile_m = 0;
     const int* ent = moe.table + 4 * ti;
     const int e = ent[0];
@@ -605,6 +616,15 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restric
   *reinterpret_cast<u32x4*>(y + e) = o;
 }
 
+// Blocks of the tile grid (see the block order in tile_kernel): row_units units per
+// run of 256 / bn column tiles, in whole runs of 8 (256 / bn) blocks.
+int64_t tile_blocks(int64_t row_units, int64_t N, int bn) {
+  const int64_t ct = 256 / bn;
+  const int64_t n_tiles = (N + bn - 1) / bn;
+  const int64_t units = row_units * ((n_tiles + ct - 1) / ct);
+  return 8 * ct * ((units + 7) / 8);
+}
+
 template <bool BF16>
 static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                                 const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
@@ -612,8 +632,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   const bool split = p.splits > 1;
   auto go = [&](auto kern, int bm, int bn, int threads) {
     const int m_tiles = (M + bm - 1) / bm;
-    const int n_tiles = (N + bn - 1) / bn;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)m_tiles * n_tiles), (unsigned)p.splits), dim3(threads), 0,
+    hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks(m_tiles, N, bn), (unsigned)p.splits), dim3(threads), 0,
                        stream, x, reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        reinterpret_cast<const _Float16*>(scales), bias, M, K, N, g, m_tiles, p.kps,
                        split ? partial : nullptr, y, MoeTiles{});
@@ -646,8 +665,7 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
                                const uint16_t* scales, int K, int N, int g, int variant, const MoeTiles& moe,
                                uint16_t* y, hipStream_t stream) {
   auto go = [&](auto kern, int bn, int threads) {
-    const int n_tiles = (N + bn - 1) / bn;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)moe.tiles * n_tiles), 1u), dim3(threads), 0, stream, x,
+    hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks(moe.tiles, N, bn), 1u), dim3(threads), 0, stream, x,
                        reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
                        reinterpret_cast<const _Float16*>(scales), nullptr, 0, K, N, g, 1, (K + kBK - 1) / kBK,
                        nullptr, y, moe);
