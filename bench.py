@@ -280,7 +280,9 @@ def time_moe(name, steps, torch, awq, synth):
             if mfma_bound else dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                                     frac=round(gbs / HBM_PEAK_GBS, 4)))
     return dict(workload=name, active_experts=int(active), call_us=round(s_per * 1e6, 3), algorithmic_bytes=nbytes,
-                flops=flops, roofline=roof, note="one call = alignment kernel + grouped tile kernel")
+                flops=flops, roofline=roof,
+                note=("one call = skinny kernel batched over experts (+ split reduce), no alignment pass"
+                      if w.T <= 16 else "one call = alignment kernel + grouped tile kernel"))
 
 
 def read_ceiling(nbytes, torch, steps=400):

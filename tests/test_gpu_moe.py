@@ -107,6 +107,75 @@ def test_moe_gemm(T, E, topk, K, N, g, routing):
     tol_check(y, yref, f"moe T{T}E{E}k{topk}")
 
 
+SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batched skinny family
+    (1, 8, 2, 4096, 512, 128),
+    (3, 16, 4, 1024, 96, 32),      # N below one 256-column tile
+    (4, 8, 2, 11008, 256, 64),     # 4-wave workgroups, fixed-point K splits
+    (2, 4, 1, 8192, 1024, -1),
+    (8, 64, 2, 2048, 768, -1),     # most experts receive no slot
+    (16, 8, 2, 4096, 1024, 128),   # 8-wave workgroups, fp32 partials
+    (13, 6, 3, 4096, 320, 64),
+]
+
+
+@pytest.mark.parametrize("T,E,topk,K,N,g", SKINNY_CASES)
+def test_moe_gemm_few_tokens(T, E, topk, K, N, g):
+    d = synth.make_moe_custom(T, E, topk, K, N, g, seed=T * 7 + E + K)
+    print(f"moe few tokens T={T} E={E} topk={topk} K={K} N={N} g={g}", flush=True)
+    y = run(d)
+    yref = oracle.moe_gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["expert_ids"], topk, g)
+    tol_check(y, yref, f"moe few T{T}E{E}k{topk}")
+
+
+@pytest.mark.parametrize("T", [3, 12])
+def test_moe_gemm_few_tokens_odd_routing(T):
+    """A token that names one expert twice gets that expert's row in both slots; slots
+    whose id lies outside [0, E) route nowhere and keep what out held."""
+    E, topk, K, N, g = 5, 3, 1024, 256, 64
+    d = synth.make_moe_custom(T, E, topk, K, N, g, seed=T + 99)
+    ids = d["expert_ids"].reshape(T, topk).copy()
+    ids[0, 1] = ids[0, 0]          # repeated expert
+    ids[1, 2] = -1                 # routes nowhere
+    ids[T - 1, 0] = E              # routes nowhere
+    d["expert_ids"] = ids.ravel()
+    t = {k: torch.from_numpy(np.ascontiguousarray(d[k])).cuda() for k in ("x", "qweight", "qzeros", "scales")}
+    out = torch.full((T * topk, N), 7.0, dtype=torch.float16, device="cuda")
+    awq.awq_moe_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], torch.from_numpy(ids).cuda(), g, out=out)
+    torch.cuda.synchronize()
+    y = out.cpu().numpy()
+    valid = (d["expert_ids"] >= 0) & (d["expert_ids"] < E)
+    yref = oracle.moe_gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], np.where(valid, d["expert_ids"], E),
+                               topk, g)
+    tol_check(y[valid], yref[valid], f"moe odd T{T}")
+    assert np.all(y[~valid] == 7.0)
+    assert np.array_equal(y[0], y[1])
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_moe_gemm_few_tokens_graph_replay(T):
+    """The K splits of the few-token path meet in zero-maintained accumulators (4
+    tokens) or in partials (16): replays must reproduce the eager bits."""
+    d = synth.make_moe_custom(T, 8, 2, 4096, 512, 128, seed=T + 5)
+    t = {k: torch.from_numpy(np.ascontiguousarray(d[k])).cuda() for k in ("x", "qweight", "qzeros", "scales")}
+    ids = torch.from_numpy(d["expert_ids"].reshape(-1, 2)).cuda()
+    y = torch.empty((2 * T, 512), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        awq.awq_moe_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], ids, 128, out=y)
+        eager = y.clone()
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        awq.awq_moe_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], ids, 128, out=y)
+    for _ in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            graph.replay()
+        s.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16))
+
+
 @pytest.mark.parametrize("name", list(synth.MOE_WORKLOADS))
 def test_moe_gemm_workload_sampled_columns(name):
     """Full-size layer; the reference covers 64 word columns (512 outputs) spread over N."""

@@ -121,6 +121,21 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
       L = l2;
     }
   }
+  // 8-wave plans whose waves span several groups: take one-group runs of at most 4
+  // k-steps instead when that lowers (rounds of resident workgroups) x (k-steps
+  // per wave + 2); the 2 stands for a workgroup's fixed cost (group data, the
+  // reduction, the partial stores).  The round count decides it: 5.25 rounds of
+  // 7-step waves lose to 7 full rounds of 4-step waves (4096 x 114688), while
+  // 1 or 2 full rounds beat 2 or 3.5 (11008 x 4096, 28672 x 8192); measured.
+  if (W == 8 && !s.single_group) {
+    int64_t l1 = gsteps < 4 ? gsteps : 4;
+    while (gsteps % l1 != 0) --l1;
+    auto cost = [&](int64_t l) { return (s.n_tiles * splits_of(l) + cap - 1) / cap * (l + 2); };
+    if (splits_of(l1) <= awq::kSkinnyMaxSplits && cost(l1) < cost(L)) {
+      L = l1;
+      s.single_group = true;
+    }
+  }
   if (splits_of(L) > awq::kSkinnyMaxSplits) return false;
   s.L = (int)L;
   s.splits = (int)splits_of(L);
@@ -413,6 +428,29 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
   const int64_t S = T * topk;
   const int g = eff_group(K, group_size);
   const int64_t G = K / g;
+  // Up to kSkinnyMaxM tokens: the skinny family batched over experts (every token a
+  // row, routed rows stored), no alignment pass.
+  awq::SkinnyPlan sk{};
+  const int64_t tiles_e = (N + awq::kSkinnyCols - 1) / awq::kSkinnyCols;
+  if (T <= awq::kSkinnyMaxM && E * tiles_e < (int64_t(1) << 31) &&
+      plan_skinny(T, K, E * tiles_e * awq::kSkinnyCols, g, device_cus(), sk)) {
+    Plan p;
+    if (sk.splits > 1) {
+      if (sk.waves == 4) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
+      else p.partial_bytes = (int64_t)sk.n_tiles * sk.splits * sk.mrows * awq::kSkinnyCols * 4;
+    }
+    uint64_t* accum = nullptr;
+    float* partial = nullptr;
+    if (sk.splits > 1) {
+      st = get_workspace(p, stream, &accum, &partial);
+      if (st != AWQ_OK) return st;
+    }
+    const awq::SkinnyExperts ex{expert_ids, (int)topk, (int)tiles_e, K * (N / 8), G * (N / 8), G * N};
+    hipError_t e = awq::launch_skinny_experts(static_cast<const uint16_t*>(x_f16), qweight, qzeros,
+                                              static_cast<const uint16_t*>(scales_f16), (int)T, (int)K, (int)N, g,
+                                              sk, ex, accum, partial, static_cast<uint16_t*>(y_f16), stream);
+    return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
+  }
   int block_rows = 0;
   const int variant = awq::moe_tile_variant(S / E, &block_rows);
   const int64_t tiles = awq_moe_tiles(S, E, block_rows);

@@ -155,12 +155,13 @@ struct SkinnyLds {
 
 // Workspace: per tile, 64-bit accumulator 4 * slot + i holds row 4 (slot / 256) + i
 // of the slot's column, slot = q * 256 + accumulator * 16 + c.  All zero between calls.
-template <int WAVES, int MROWS, bool SINGLE, bool BF16>
+// EXPERTS: routed experts (SkinnyExperts); M is the token count, there is no bias.
+template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
     const uint16_t* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
-    uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y) {
+    uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y, SkinnyExperts ex) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
   // k-steps in flight per wave, and how K splits meet: 4-wave workgroups (M <= 4)
@@ -178,8 +179,29 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const int q = lane >> 4;
   const int c = lane & 15;
   const int NW = N >> 3;
-  const int tile = blockIdx.x;
+  // Column tile; with EXPERTS, block x also names the expert.  Accumulators and
+  // partials belong to the block.
+  const int expert = EXPERTS ? (int)blockIdx.x / ex.tiles : 0;
+  const int tile = EXPERTS ? (int)blockIdx.x - expert * ex.tiles : (int)blockIdx.x;
   const int split = blockIdx.y;
+  if constexpr (EXPERTS) {
+    bool hit = false;
+    for (int s = tid; s < M * ex.topk; s += THREADS) hit |= ex.ids[s] == expert;
+    if (!__syncthreads_or(hit)) return;  // uniform: no slot of this expert
+    qweight += expert * ex.w_stride;
+    qzeros += expert * ex.z_stride;
+    scales += expert * ex.s_stride;
+  }
+  // Store of output row `row`, column n: row `row` of y, or every slot of token
+  // `row` routed to this block's expert.
+  auto put = [&](int row, int n, float v) {
+    if constexpr (EXPERTS) {
+      for (int j = 0; j < ex.topk; ++j)
+        if (ex.ids[row * ex.topk + j] == expert) y[((int64_t)row * ex.topk + j) * N + n] = float_to_act<BF16>(v);
+    } else {
+      y[(int64_t)row * N + n] = float_to_act<BF16>(v);
+    }
+  };
   const int wc = tile * kSkinnyWordCols + 2 * c;
   const bool col_ok = wc < NW;  // NW % 4 == 0, so wc + 1 < NW as well
 
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * (s >> 8) + i;
-          if (row < rows) y[(int64_t)row * N + n] = float_to_act<BF16>(sum[k][i] + b);
+          if (row < rows) put(row, n, sum[k][i] + b);
         }
       }
     }
@@ -395,7 +417,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   if (!ATOMIC) {
     // 3'. Plain fp32 partial stores [tile][split][entry]; skinny_reduce_kernel sums
     // them in split order after this kernel completes.
-    float* tile_part = partial + ((int64_t)tile * splits + split) * TILE_ENTRIES;
+    float* tile_part = partial + ((int64_t)blockIdx.x * splits + split) * TILE_ENTRIES;
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int s = tid + k * THREADS;
@@ -405,7 +427,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   }
 
   // 3. Fixed-point accumulation across splits; the last arrival finishes the element.
-  uint64_t* tile_acc = accum + (int64_t)tile * TILE_ENTRIES;
+  uint64_t* tile_acc = accum + (int64_t)blockIdx.x * TILE_ENTRIES;
   constexpr float kClamp = 8388608.0f;  // 2^23
   constexpr float kToFixed = 16777216.0f;  // 2^24
 #pragma unroll
@@ -434,7 +456,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
         __hip_atomic_store(tile_acc + 4 * s + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n < N) {
           const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
-          y[(int64_t)row * N + n] = float_to_act<BF16>((float)value * (1.0f / kToFixed) + b);
+          put(row, n, (float)value * (1.0f / kToFixed) + b);
         }
       }
     }
@@ -446,17 +468,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 // 4 rows of slot 256 q + t (16 contiguous bytes per split), and the rounded values
 // meet in LDS in output order so that y is written as whole 16-byte row pieces.
 // tile_entries: rows kept per tile (4 or 16) x 256.
-template <bool BF16>
+// EXPERTS: partials of block b = expert * tiles + column tile; row t goes to the
+// slots of token t routed to the expert (blocks of unrouted experts never wrote
+// their partials and store nothing).
+template <bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             const uint16_t* __restrict__ bias, int M, int N,
-                                                            int splits, int tile_entries, uint16_t* __restrict__ y) {
+                                                            int splits, int tile_entries, uint16_t* __restrict__ y,
+                                                            SkinnyExperts ex) {
   const int TILE_ENTRIES = tile_entries;
   __shared__ __attribute__((aligned(16))) uint16_t ys[4][kSkinnyCols + 8];
-  const int tile = blockIdx.x / 4, q = blockIdx.x % 4;
+  const int block = blockIdx.x / 4, q = blockIdx.x % 4;
+  const int expert = EXPERTS ? block / ex.tiles : 0;
+  const int tile = EXPERTS ? block - expert * ex.tiles : block;
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
   const int slot = q * 256 + t;
-  const float* p = partial + (int64_t)tile * splits * TILE_ENTRIES + 4 * slot;
+  const float* p = partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot;
   floatx4 a = *reinterpret_cast<const floatx4*>(p);
   for (int sp = 1; sp < splits; ++sp) a += *reinterpret_cast<const floatx4*>(p + (int64_t)sp * TILE_ENTRIES);
   const int sv = (t >> 4) & 15, sc = t & 15;
@@ -469,8 +497,16 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   if (t < 4 * (kSkinnyCols / 8)) {
     const int i = t / (kSkinnyCols / 8), pc = t % (kSkinnyCols / 8);
     const int row = 4 * q + i, n0 = tile * kSkinnyCols + 8 * pc;
-    if (row < M && n0 < N)
-      *reinterpret_cast<u32x4*>(y + (int64_t)row * N + n0) = *reinterpret_cast<const u32x4*>(&ys[i][8 * pc]);
+    if (row < M && n0 < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&ys[i][8 * pc]);
+      if constexpr (EXPERTS) {
+        for (int j = 0; j < ex.topk; ++j)
+          if (ex.ids[row * ex.topk + j] == expert)
+            *reinterpret_cast<u32x4*>(y + ((int64_t)row * ex.topk + j) * N + n0) = v;
+      } else {
+        *reinterpret_cast<u32x4*>(y + (int64_t)row * N + n0) = v;
+      }
+    }
   }
 }
 
@@ -483,7 +519,7 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, x, reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), bias,
-                       M, K, N, g, p.L, p.splits, accum, partial, y);
+                       M, K, N, g, p.L, p.splits, accum, partial, y, SkinnyExperts{});
   };
   if (p.waves == 4) {
     if (p.single_group) go(skinny_kernel<4, 4, true, BF16>, 256);
@@ -497,7 +533,34 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(skinny_reduce_kernel<BF16>, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N,
-                       p.splits, p.mrows * kSkinnyCols, y);
+                       p.splits, p.mrows * kSkinnyCols, y, SkinnyExperts{});
+  }
+  return hipGetLastError();
+}
+
+// Routed experts (fp16): p.n_tiles = experts x column tiles per expert.
+hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
+                                 const uint16_t* scales, int T, int K, int N, int g, const SkinnyPlan& p,
+                                 const SkinnyExperts& ex, uint64_t* accum, float* partial, uint16_t* y,
+                                 hipStream_t stream) {
+  const dim3 grid(p.n_tiles, p.splits);
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, x, reinterpret_cast<const uint32_t*>(qweight),
+                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
+                       T, K, N, g, p.L, p.splits, accum, partial, y, ex);
+  };
+  if (p.waves == 4) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, false, true>, 256);
+    else go(skinny_kernel<4, 4, false, false, true>, 256);
+  } else {
+    if (p.single_group) go(skinny_kernel<8, 16, true, false, true>, 512);
+    else go(skinny_kernel<8, 16, false, false, true>, 512);
+  }
+  if (p.splits > 1 && p.waves == 8) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((skinny_reduce_kernel<false, true>), dim3(p.n_tiles * 4), dim3(256), 0, stream, partial,
+                       nullptr, T, N, p.splits, p.mrows * kSkinnyCols, y, ex);
   }
   return hipGetLastError();
 }
