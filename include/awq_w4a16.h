@@ -185,18 +185,21 @@ int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qze
  *                 rows, then (-1, 0, 0, 0)
  *   1 <= E <= 1024, S < 2^30.  Returns AWQ_OK or an error status.
  *
- * awq_moe_gemm: the grouped product, one call (alignment, then one launch of the
- * MFMA tile kernel in which each workgroup gathers the x rows of one expert's tile
- * and scatters its y rows).
+ * awq_moe_gemm: the grouped product, one call.  Up to 16 tokens: one launch of the
+ * skinny kernel over (expert, column tile) blocks, every token a row, routed rows
+ * stored, experts without a slot skipped (plus the split reduce for 5..16 tokens);
+ * more tokens: alignment, then one launch of the MFMA tile kernel in which each
+ * workgroup gathers the x rows of one expert's tile and scatters its y rows.
  *   x_f16        device fp16 [T, K]
  *   qweight      device int32 [E, K, N/8];  qzeros int32 [E, G, N/8];  scales fp16 [E, G, N]
  *   expert_ids   device int32 [T * topk]
  *   y_f16        device fp16 [T * topk, N]; rows of slots with an id outside [0, E)
  *                are left unwritten
  * Limits: those of awq_gemm with M = T * topk, plus 1 <= E <= 1024, topk >= 1 and
- * x below 4 GiB.  T == 0 enqueues nothing.  The alignment lives in the same
- * library-owned per-(device, stream) workspace as awq_gemm's, with the same
- * allocation rule.  The result is deterministic (each row depends only on its slot).
+ * x below 4 GiB.  T == 0 enqueues nothing.  The alignment and the split-K
+ * accumulators or partials live in the same library-owned per-(device, stream)
+ * workspace as awq_gemm's, with the same allocation rule.  The result is
+ * deterministic (each row depends only on its slot; splits meet in a fixed order).
  * Returns AWQ_OK or an error status.
  */
 int64_t awq_moe_tiles(int64_t S, int64_t E, int64_t block_rows);
