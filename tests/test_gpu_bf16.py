@@ -94,6 +94,21 @@ def test_gemm_bf16_ragged(M, K, N, g, bias):
     tol_check(gemm_bits(d, g), yref, f"bf16 M{M}K{K}N{N}g{g}")
 
 
+@pytest.mark.parametrize("M,K,N,g", [(16, 8192, 28672, 128), (3, 4096, 114688, 128)])
+def test_bf16_layer_sampled_entries(M, K, N, g):
+    """Full-size layers (16-row plan on 4-wave workgroups; 3 rows): every row at 520
+    columns, each entry from the oracle's one-column dot product on the exact values
+    of the bfloat16 inputs."""
+    print(f"bf16 layer M={M} K={K} N={N} g={g} plan={awq.plan(M, K, N, g)}", flush=True)
+    d = synth.make_custom_bf16(M, K, N, g, bias=True, seed=M + K)
+    ybits = gemm_bits(d, g)
+    cols = np.unique(np.concatenate([np.linspace(0, N - 1, 512).astype(np.int64), np.arange(N - 8, N)]))
+    rows = np.repeat(np.arange(M), len(cols))
+    yref = oracle.gemm_ref_entries(oracle.bf16_to_f64(d["x"]), d["qweight"], d["qzeros"], d["scales"],
+                                   oracle.bf16_to_f64(d["bias"]), g, rows, np.tile(cols, M)).reshape(M, len(cols))
+    tol_check(ybits[:, cols], yref, f"bf16 layer M{M}K{K}N{N}")
+
+
 def eye_bits(rows, K, pick):
     x = np.zeros((rows, K), dtype=np.float32)
     x[np.arange(rows), pick] = 1.0

@@ -80,8 +80,13 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   const int64_t T = K / awq::kKStep;
   const int64_t gsteps = g / awq::kKStep;  // g already resolved (-1 -> K)
   s.n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
-  s.waves = M <= 4 ? 4 : 8;
+  // Up to 4 rows: 4 waves.  Up to 16: 8 waves, or 4 waves (two per CU, shorter
+  // workgroups overlapping each other's fixed phases) once the 8-wave grid would
+  // take more than four rounds (layers above ~32 MB of packed weights): measured
+  // 8-15% faster on 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on
+  // layers of up to 22 MB.
   s.mrows = M <= 4 ? 4 : 16;
+  s.waves = (M <= 4 || T * s.n_tiles > (int64_t)8 * cus * 4) ? 4 : 8;
   const int64_t W = s.waves;
   // Whole grid resident in one round, counting two 4-wave workgroups per CU (three
   // fit when every wave stays inside one group; counting three gives more splits,
@@ -121,13 +126,13 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
       L = l2;
     }
   }
-  // 8-wave plans whose waves span several groups: take one-group runs of at most 4
+  // 16-row plans whose waves span several groups: take one-group runs of at most 4
   // k-steps instead when that lowers (rounds of resident workgroups) x (k-steps
   // per wave + 2); the 2 stands for a workgroup's fixed cost (group data, the
   // reduction, the partial stores).  The round count decides it: 5.25 rounds of
   // 7-step waves lose to 7 full rounds of 4-step waves (4096 x 114688), while
   // 1 or 2 full rounds beat 2 or 3.5 (11008 x 4096, 28672 x 8192); measured.
-  if (W == 8 && !s.single_group) {
+  if (s.mrows == 16 && !s.single_group) {
     int64_t l1 = gsteps < 4 ? gsteps : 4;
     while (gsteps % l1 != 0) --l1;
     auto cost = [&](int64_t l) { return (s.n_tiles * splits_of(l) + cap - 1) / cap * (l + 2); };
@@ -149,10 +154,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     p.grid_x = p.sk.n_tiles;
     p.grid_y = p.sk.splits;
     p.block = 64 * p.sk.waves;
-    // 4-wave fp16 plans: 64-bit fixed-point accumulators per tile entry; 8-wave
+    // 4-row fp16 plans: 64-bit fixed-point accumulators per tile entry; 16-row
     // plans and every bfloat16 plan: fp32 partials per (tile, split, entry).
     if (p.sk.splits > 1) {
-      if (p.sk.waves == 4 && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+      if (p.sk.mrows == 4 && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
       else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * awq::kSkinnyCols * 4;
     }
   } else {
@@ -436,7 +441,7 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
       plan_skinny(T, K, E * tiles_e * awq::kSkinnyCols, g, device_cus(), sk)) {
     Plan p;
     if (sk.splits > 1) {
-      if (sk.waves == 4) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
+      if (sk.mrows == 4) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
       else p.partial_bytes = (int64_t)sk.n_tiles * sk.splits * sk.mrows * awq::kSkinnyCols * 4;
     }
     uint64_t* accum = nullptr;

@@ -164,13 +164,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y, SkinnyExperts ex) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
-  // k-steps in flight per wave, and how K splits meet: 4-wave workgroups (M <= 4)
-  // combine splits with fixed-point atomics; 8-wave ones (up to 16 rows, where the
-  // atomic count M * N * S gets large) store fp32 partials for skinny_reduce_kernel.
+  // k-steps in flight per wave, and how K splits meet: 4-row plans combine splits
+  // with fixed-point atomics; 16-row plans (4 or 8 waves; the atomic count M * N * S
+  // gets large) store fp32 partials for skinny_reduce_kernel.
   // bfloat16 always takes the partials: the fixed-point format relies on fp16's
   // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
   constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
-  constexpr bool ATOMIC = WAVES == 4 && !BF16;
+  constexpr bool ATOMIC = MROWS == 4 && !BF16;
   __shared__ SkinnyLds<WAVES, (MROWS > 4 ? 64 : 16)> sh;
 
   const int tid = threadIdx.x;
@@ -521,15 +521,18 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), bias,
                        M, K, N, g, p.L, p.splits, accum, partial, y, SkinnyExperts{});
   };
-  if (p.waves == 4) {
+  if (p.mrows == 4) {
     if (p.single_group) go(skinny_kernel<4, 4, true, BF16>, 256);
     else go(skinny_kernel<4, 4, false, BF16>, 256);
+  } else if (p.waves == 4) {
+    if (p.single_group) go(skinny_kernel<4, 16, true, BF16>, 256);
+    else go(skinny_kernel<4, 16, false, BF16>, 256);
   } else {
     if (p.single_group) go(skinny_kernel<8, 16, true, BF16>, 512);
     else go(skinny_kernel<8, 16, false, BF16>, 512);
   }
-  // Partials (8-wave plans, and every bfloat16 plan) are summed by the reduce kernel.
-  if (p.splits > 1 && (p.waves == 8 || BF16)) {
+  // Partials (16-row plans, and every bfloat16 plan) are summed by the reduce kernel.
+  if (p.splits > 1 && (p.mrows == 16 || BF16)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(skinny_reduce_kernel<BF16>, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N,
@@ -549,14 +552,17 @@ hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, cons
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
                        T, K, N, g, p.L, p.splits, accum, partial, y, ex);
   };
-  if (p.waves == 4) {
+  if (p.mrows == 4) {
     if (p.single_group) go(skinny_kernel<4, 4, true, false, true>, 256);
     else go(skinny_kernel<4, 4, false, false, true>, 256);
+  } else if (p.waves == 4) {
+    if (p.single_group) go(skinny_kernel<4, 16, true, false, true>, 256);
+    else go(skinny_kernel<4, 16, false, false, true>, 256);
   } else {
     if (p.single_group) go(skinny_kernel<8, 16, true, false, true>, 512);
     else go(skinny_kernel<8, 16, false, false, true>, 512);
   }
-  if (p.splits > 1 && p.waves == 8) {
+  if (p.splits > 1 && p.mrows == 16) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((skinny_reduce_kernel<false, true>), dim3(p.n_tiles * 4), dim3(256), 0, stream, partial,
