@@ -127,4 +127,21 @@ __device__ __forceinline__ uint32_t zero_code(uint32_t zw, int j) {
 
 __device__ __forceinline__ half2v splat(_Float16 v) { return half2v{v, v}; }
 
+// Sum over s < splits of the 4 floats at p + s * stride, added in split order (the
+// same order, so the same bits, for every call).  The loads go out 8 splits at a
+// time so that their round trips overlap; a batch past the last split re-reads the
+// last one (in bounds) and does not add it.
+__device__ __forceinline__ floatx4 sum_splits(const float* __restrict__ p, int64_t stride, int splits) {
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  for (int s = 1; s < splits; s += 8) {
+    floatx4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const floatx4*>(p + (int64_t)min(s + j, splits - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s + j < splits) a += v[j];
+  }
+  return a;
+}
+
 }  // namespace awq

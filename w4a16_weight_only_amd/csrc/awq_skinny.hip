@@ -484,9 +484,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
   const int slot = q * 256 + t;
-  const float* p = partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot;
-  floatx4 a = *reinterpret_cast<const floatx4*>(p);
-  for (int sp = 1; sp < splits; ++sp) a += *reinterpret_cast<const floatx4*>(p + (int64_t)sp * TILE_ENTRIES);
+  const floatx4 a = sum_splits(partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot, TILE_ENTRIES, splits);
   const int sv = (t >> 4) & 15, sc = t & 15;
   const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
   const int n = tile * kSkinnyCols + ct;

@@ -589,31 +589,22 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   }
 }
 
-// y = round(sum over splits of partial[s] + bias) to fp16 or (BF16) bfloat16, 8
+// y = round(sum over splits of partial[s] + bias) to fp16 or (BF16) bfloat16, 4
 // columns per thread, splits summed in order (deterministic).
 template <bool BF16>
 __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restrict__ partial,
                                                           const uint16_t* __restrict__ bias, int64_t MN,
                                                           int N, int splits, uint16_t* __restrict__ y) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= MN) return;
-  floatx4 a = *reinterpret_cast<const floatx4*>(partial + e);
-  floatx4 b = *reinterpret_cast<const floatx4*>(partial + e + 4);
-  for (int s = 1; s < splits; ++s) {
-    a += *reinterpret_cast<const floatx4*>(partial + s * MN + e);
-    b += *reinterpret_cast<const floatx4*>(partial + s * MN + e + 4);
-  }
+  floatx4 a = sum_splits(partial + e, MN, splits);
   if (bias != nullptr) {
     const int n = (int)(e % N);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a[j] += act_to_float<BF16>(bias[n + j]);
-      b[j] += act_to_float<BF16>(bias[n + 4 + j]);
-    }
+    for (int j = 0; j < 4; ++j) a[j] += act_to_float<BF16>(bias[n + j]);
   }
-  const u32x4 o = {pack_act2<BF16>(a[0], a[1]), pack_act2<BF16>(a[2], a[3]), pack_act2<BF16>(b[0], b[1]),
-                   pack_act2<BF16>(b[2], b[3])};
-  *reinterpret_cast<u32x4*>(y + e) = o;
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2_t*>(y + e) = u32x2_t{pack_act2<BF16>(a[0], a[1]), pack_act2<BF16>(a[2], a[3])};
 }
 
 // Blocks of the tile grid (see the block order in tile_kernel): row_units units per
@@ -645,7 +636,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t MN = (int64_t)M * N;
-  const int64_t blocks = (MN / 8 + 255) / 256;
+  const int64_t blocks = (MN / 4 + 255) / 256;
   hipLaunchKernelGGL(tile_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N,
                      p.splits, y);
   return hipGetLastError();
