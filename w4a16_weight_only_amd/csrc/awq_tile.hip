@@ -63,6 +63,15 @@ __device__ __forceinline__ void load_lds16(const void* src, const void* lds) {
                : "memory", "m0");
 }
 
+// The same load from a wave-uniform 64-bit base (scalar registers) plus a 32-bit
+// per-lane byte offset: the base advances with scalar adds, so the per-load address
+// math stays off the vector ALU.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 // ORDER[p]: column within a packed word held by nibble p.
 __device__ __forceinline__ int order_of(int p) { return (p & 4) ? 2 * (p & 3) + 1 : 2 * p; }
 
@@ -226,6 +235,16 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // which holds word group (l % NG) ^ swz(row).
   auto swz = [](int r) { return ((r >> 3) & 1) * (NG / 2); };
   const int b_rl = lane / NG;
+  // Per-lane byte offset of each extra weight load from the k-tile's first row.
+  uint32_t w_off[XPW];
+#pragma unroll
+  for (int xs = 0; xs < XPW; ++xs) {
+    const int e = min(wave + NWAVES * xs, NB - 1);
+    const int row = e * RPI + b_rl;                 // row within the k-tile
+    const int grp = (lane % NG) ^ swz(row);
+    const int r = K < kBK ? (row & 31) : row;       // K = 32: re-read the real half
+    w_off[xs] = ((uint32_t)r * (uint32_t)NW + (uint32_t)min(wc0 + 4 * grp, NW - 4)) * 4u;
+  }
   // Group data: lane l < 2 GP loads piece l % GP of half l / GP (others repeat piece 0).
   const int g_lane = lane < 2 * GP ? lane : 0;
   const int g_half = g_lane < GP ? 0 : 1;
@@ -235,19 +254,13 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   auto load_tile = [&](int buf, int k0) {
     const int kl = tile_row(k0);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const char* src = xb + ((int64_t)a_row0[j] * K + kl) * 2 + a_off[j];
-      load_lds16(src, &As[buf][(wave * IPW + j) * 8 * kBK]);
-    }
+    for (int j = 0; j < IPW; ++j)
+      load_lds16_s(xb + ((int64_t)a_row0[j] * K + kl) * 2, a_off[j], &As[buf][(wave * IPW + j) * 8 * kBK]);
 #pragma unroll
     for (int xs = 0; xs < XPW; ++xs) {
       const int e = wave + NWAVES * xs;  // wave-uniform: which extra load this is
       if (e < NB) {
-        const int row = e * RPI + b_rl;                 // row within the k-tile
-        const int grp = (lane % NG) ^ swz(row);
-        const int r = K < kBK ? (row & 31) : row;       // K = 32: re-read the real half
-        const char* src = wb + ((int64_t)(kl + r) * NW + min(wc0 + 4 * grp, NW - 4)) * 4;
-        load_lds16(src, &Bs[buf][e * RPI * BW]);
+        load_lds16_s(wb + (int64_t)kl * NW * 4, w_off[xs], &Bs[buf][e * RPI * BW]);
       } else if (e == NB) {
         // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
         // inside the k-tile can only fall between the halves.
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
         const int64_t zoff = ((int64_t)gi * NW + zcol) << 2, soff = ((int64_t)gi * N + scol) << 1;
         load_lds16(sb + (soff + z * (zoff + to_z - soff)), &Gs[buf][0]);
       } else {
-        load_lds16(xb + ((int64_t)a_row0[0] * K + kl) * 2 + a_off[0], &stg.sink[0]);
+        load_lds16_s(xb + ((int64_t)a_row0[0] * K + kl) * 2, a_off[0], &stg.sink[0]);
       }
     }
   };
