@@ -178,9 +178,10 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     scales += e * moe.s_stride;
   }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  // Grouped mode: 32-row block i of this wave holds a routed row only if it starts
-  // below the entry's row count (uniform per wave); the others skip their MFMAs.
-  auto row_block_live = [&](int i) { return wm * 32 * FM + 32 * i < M; };
+  // Grouped mode multiplies every 32-row block of the tile, also those past the
+  // entry's rows (their x rows are clamped copies and their sums are never stored):
+  // a per-block liveness test between the MFMAs cost a full 256-row tile about a
+  // fifth of its time, more than it saved on the partly filled tiles.
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
 
@@ -374,7 +375,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (GROUPED && !row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(f.a[i], bf[j], acc[i][j]);
@@ -459,7 +459,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (GROUPED && !row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(a[i], bf[j], acc[i][j]);
