@@ -153,9 +153,28 @@ struct SkinnyLds {
 
 }  // namespace
 
+// Routed experts: bit t of the result is set when token t (t < T <= 16) sends a
+// slot to `expert`.  Lanes 0..T-1 of the calling wave each test one token; every wave
+// of a workgroup gets the same mask.
+__device__ __forceinline__ uint32_t routed_tokens(const SkinnyExperts& ex, int T, int expert, int lane) {
+  bool r = false;
+  if (lane < T)
+    for (int j = 0; j < ex.topk; ++j) r |= ex.ids[lane * ex.topk + j] == expert;
+  return (uint32_t)__ballot(r);
+}
+
+// Index of the n-th set bit of mask (n < popcount(mask)).
+__device__ __forceinline__ int nth_set_bit(uint32_t mask, int n) {
+  for (int i = 0; i < n; ++i) mask &= mask - 1;
+  return __builtin_ctz(mask);
+}
+
 // Workspace: per tile, 64-bit accumulator 4 * slot + i holds row 4 (slot / 256) + i
 // of the slot's column, slot = q * 256 + accumulator * 16 + c.  All zero between calls.
-// EXPERTS: routed experts (SkinnyExperts); M is the token count, there is no bias.
+// EXPERTS: routed experts (SkinnyExperts); M is the token count on entry, there is
+// no bias.  The block's rows are then only the tokens routed to its expert, in token
+// order (row m = the m-th such token), and M becomes their count: the MFMA rows, the
+// split accumulators or partials and the reduction cover just those rows.
 template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
@@ -184,20 +203,22 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const int expert = EXPERTS ? (int)blockIdx.x / ex.tiles : 0;
   const int tile = EXPERTS ? (int)blockIdx.x - expert * ex.tiles : (int)blockIdx.x;
   const int split = blockIdx.y;
+  uint32_t tokens = 0;  // EXPERTS: the routed-token mask of this block's expert
   if constexpr (EXPERTS) {
-    bool hit = false;
-    for (int s = tid; s < M * ex.topk; s += THREADS) hit |= ex.ids[s] == expert;
-    if (!__syncthreads_or(hit)) return;  // uniform: no slot of this expert
+    tokens = routed_tokens(ex, M, expert, lane);
+    if (tokens == 0) return;  // uniform: no slot of this expert
+    M = __builtin_popcount(tokens);
     qweight += expert * ex.w_stride;
     qzeros += expert * ex.z_stride;
     scales += expert * ex.s_stride;
   }
-  // Store of output row `row`, column n: row `row` of y, or every slot of token
-  // `row` routed to this block's expert.
+  // Store of output row `row`, column n: row `row` of y, or every slot of the
+  // row's token routed to this block's expert.
   auto put = [&](int row, int n, float v) {
     if constexpr (EXPERTS) {
+      const int tok = nth_set_bit(tokens, row);
       for (int j = 0; j < ex.topk; ++j)
-        if (ex.ids[row * ex.topk + j] == expert) y[((int64_t)row * ex.topk + j) * N + n] = float_to_act<BF16>(v);
+        if (ex.ids[tok * ex.topk + j] == expert) y[((int64_t)tok * ex.topk + j) * N + n] = float_to_act<BF16>(v);
     } else {
       y[(int64_t)row * N + n] = float_to_act<BF16>(v);
     }
@@ -219,7 +240,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // valid clamped address instead of being masked: an MFMA output row depends only
   // on its own x row, and rows >= M and columns >= N are never stored.
   const int m = lane & 15;
-  const uint32_t x_off = ((uint32_t)(m < M ? m : 0) * (uint32_t)K + 8u * q) * 2u;
+  const int xrow = EXPERTS ? nth_set_bit(tokens, m < M ? m : 0) : (m < M ? m : 0);
+  const uint32_t x_off = ((uint32_t)xrow * (uint32_t)K + 8u * q) * 2u;
   const uint32_t w_off = ((uint32_t)(8 * q) * (uint32_t)NW + (uint32_t)(col_ok ? wc : 0)) * 4u;
   const uint32_t row_bytes = (uint32_t)NW * 4u;
   const char* xb = reinterpret_cast<const char*>(x);
@@ -468,9 +490,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 // 4 rows of slot 256 q + t (16 contiguous bytes per split), and the rounded values
 // meet in LDS in output order so that y is written as whole 16-byte row pieces.
 // tile_entries: rows kept per tile (4 or 16) x 256.
-// EXPERTS: partials of block b = expert * tiles + column tile; row t goes to the
-// slots of token t routed to the expert (blocks of unrouted experts never wrote
-// their partials and store nothing).
+// EXPERTS: partials of block b = expert * tiles + column tile, whose rows are the
+// tokens routed to the expert in token order (row m = the m-th such token); row m
+// goes to that token's slots of the expert.  Blocks of experts without a slot
+// wrote no partials and store nothing.
 template <bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             const uint16_t* __restrict__ bias, int M, int N,
@@ -481,6 +504,11 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   const int block = blockIdx.x / 4, q = blockIdx.x % 4;
   const int expert = EXPERTS ? block / ex.tiles : 0;
   const int tile = EXPERTS ? block - expert * ex.tiles : block;
+  uint32_t tokens = 0;
+  if constexpr (EXPERTS) {
+    tokens = routed_tokens(ex, M, expert, threadIdx.x & 63);
+    M = __builtin_popcount(tokens);  // rows of the block (0: its expert got no slot)
+  }
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
   const int slot = q * 256 + t;
@@ -498,9 +526,10 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     if (row < M && n0 < N) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&ys[i][8 * pc]);
       if constexpr (EXPERTS) {
+        const int tok = nth_set_bit(tokens, row);
         for (int j = 0; j < ex.topk; ++j)
-          if (ex.ids[row * ex.topk + j] == expert)
-            *reinterpret_cast<u32x4*>(y + ((int64_t)row * ex.topk + j) * N + n0) = v;
+          if (ex.ids[tok * ex.topk + j] == expert)
+            *reinterpret_cast<u32x4*>(y + ((int64_t)tok * ex.topk + j) * N + n0) = v;
       } else {
         *reinterpret_cast<u32x4*>(y + (int64_t)row * N + n0) = v;
       }
