@@ -237,10 +237,10 @@ def test_deterministic(name):
 
 def test_reduction_modes_share_a_stream():
     """Alternate plans that combine K splits differently (fixed-point atomics for
-    M <= 4, fp32 partials + reduce kernel for skinny M > 4 and for split tiles) on
+    M <= 2, fp32 partials + reduce kernel for skinny M > 2 and for split tiles) on
     one stream, twice over: each keeps its own workspace state valid for the others."""
-    shapes = [(1, 4096, 4096, 128), (16, 4096, 1024, 128), (3, 2048, 512, 64), (9, 4096, 2048, -1),
-              (64, 2048, 512, 64)]
+    shapes = [(1, 4096, 4096, 128), (16, 4096, 1024, 128), (2, 2048, 512, 64), (3, 2048, 512, 64),
+              (9, 4096, 2048, -1), (64, 2048, 512, 64)]
     for rep in range(2):
         for (M, K, N, g) in shapes:
             d = synth.make_custom(M, K, N, g, seed=rep + M)

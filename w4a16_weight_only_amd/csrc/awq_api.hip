@@ -80,13 +80,17 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   const int64_t T = K / awq::kKStep;
   const int64_t gsteps = g / awq::kKStep;  // g already resolved (-1 -> K)
   s.n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
-  // Up to 4 rows: 4 waves.  Up to 16: 8 waves, or 4 waves (two per CU, shorter
-  // workgroups overlapping each other's fixed phases) once the 8-wave grid would
-  // take more than four rounds (layers above ~32 MB of packed weights): measured
-  // 8-15% faster on 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on
+  // One or two rows: 4-row plans (4 waves, splits meet in fixed-point atomics).
+  // From three rows the 16-row plans (fp32 partials and the reduce kernel) are
+  // faster, since every split costs the atomic plans one returning atomic per row
+  // and column (M = 3, 4: 10-25% faster; M = 2 mixed, within 7% either way).
+  // 16-row plans take 8 waves, or 4 waves (two per CU, shorter workgroups
+  // overlapping each other's fixed phases) once the 8-wave grid would take more
+  // than four rounds (layers above ~32 MB of packed weights): measured 8-15%
+  // faster on 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on
   // layers of up to 22 MB.
-  s.mrows = M <= 4 ? 4 : 16;
-  s.waves = (M <= 4 || T * s.n_tiles > (int64_t)8 * cus * 4) ? 4 : 8;
+  s.mrows = M <= 2 ? 4 : 16;
+  s.waves = (M <= 2 || T * s.n_tiles > (int64_t)8 * cus * 4) ? 4 : 8;
   const int64_t W = s.waves;
   // Whole grid resident in one round, counting two 4-wave workgroups per CU (three
   // fit when every wave stays inside one group; counting three gives more splits,
@@ -98,9 +102,9 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   if (L < l_min) L = l_min;
   // At least two k-steps per wave, so that each wave's second step is in flight
   // while its first is multiplied (measured faster than one step per wave even
-  // at half the workgroups); four for 2-4 rows, whose splits each cost one atomic
-  // per row and column (M = 3, 4 on 4096 x 4096: 8-12% faster with half the splits).
-  const int64_t l_floor = (M >= 2 && M <= 4) ? 4 : 2;
+  // at half the workgroups); four for two rows, whose splits each cost one atomic
+  // per row and column (half the splits measured faster).
+  const int64_t l_floor = M == 2 ? 4 : 2;
   if (L < l_floor) L = l_floor;
   if (L > T) L = T;
   // One or two rows on a grid of more than two rounds: keep each wave's run inside
