@@ -8,7 +8,9 @@
 // Work split.  A workgroup (4 or 8 waves) owns a column tile of 32 packed word-columns
 // (256 output columns = 128 contiguous bytes of every qweight row) and a run of
 // WAVES*L 32-row k-steps; wave w takes L consecutive k-steps of that run.  The host
-// picks L and the number of K splits S so that the whole grid is resident at once.
+// picks L and the number of K splits S (about one resident round of workgroups on
+// small layers, shorter one-group runs on large ones) and the plan's rows: 4-row
+// plans (one or two rows of x) or 16-row plans (up to 16).
 // At a few microseconds per call the kernel is latency-bound, so every input is
 // requested up front: each wave issues the weight loads of its first two k-steps,
 // and the workgroup turns the zero words and scales of every group it touches into
@@ -28,8 +30,10 @@
 // Groups: the MFMA accumulates sum_k x (q - z) per group; at the end of a group the
 // sum is scaled by s in fp32 (exact dequant, no fp16 weight rounding).
 // Reduction: the waves' accumulators meet in LDS in register order (conflict-free
-// 16-byte accesses) and are summed in wave order.  With S > 1 splits, the splits of
-// an output element meet in one 64-bit accumulator in the workspace: each workgroup
+// 16-byte accesses) and are summed in wave order.  With S > 1 splits, 16-row plans
+// (and bfloat16) store fp32 partials that a second kernel sums in split order; in
+// 4-row fp16 plans the splits of an output element meet in one 64-bit accumulator
+// in the workspace: each workgroup
 // adds, with one relaxed atomic fetch-add, its partial as a fixed-point integer
 // (24 fractional bits) plus 2^56, i.e. one arrival in the top byte.  Integer
 // addition does not depend on order, so the sum is bit-reproducible; the add that

@@ -6,22 +6,19 @@
 // the matrix products).
 //
 // Workgroup: KG groups of 4 waves as WM (M) x 4/WM (N); wave tile (32 FM) x (32 FN)
-// of v_mfma_f32_32x32x16_f16 accumulators.  Instantiations: FM = 8, FN = 1, WM = 1,
-// KG = 2 (workgroup 256 x 128, 8 waves; each B column is dequantised by one wave of
-// a k-group) for large M; FM = 2, FN = 1 with 2 x 2 waves (128 x 64) or 1 x 4
-// (64 x 128) when fewer rows would leave compute units idle.
+// of v_mfma_f32_32x32x16_f16 accumulators.  Instantiations, chosen by M alone:
+// FM = 8, FN = 1, WM = 1, KG = 2 (256 x 128, 8 waves; each B column is dequantised
+// by one wave of a k-group) above 128 rows; FM = 2, FN = 1 with 2 x 2 waves
+// (128 x 64) from 65 rows, or 1 x 4 (64 x 128) below; and, in the routed-expert
+// grouped mode only, FM = 1 (32 x 128).
 //
-// Staging, per k-tile of 64 rows: two LDS buffers and two register sets in
-// ping-pong.  The global loads of k-tile t + 3 are issued right after k-tile t is
-// multiplied and written to LDS two k-tiles later, so each load has two k-tiles of
-// MFMA work to arrive (a loaded round trip is 1.5-2 us on this part):
-//   x: BM x 64 fp16, 16-byte coalesced pieces; rows padded so that 16-byte fragment
-//      reads are conflict-free;
-//   qweight: the workgroup's BN / 8 packed word columns x 64 rows, still packed
-//      (4 KB for BN = 128), transposed to word-column-major so that a lane's 8
-//      consecutive rows are two 16-byte reads;
-//   group data: the zero words and fp16 scales of the groups of the k-tile's two
-//      32-row halves (g is a multiple of 32, so no other boundary can occur).
+// Staging, per k-tile of 64 rows, in a ring of kStages LDS buffers: x (BM x 64
+// fp16), the workgroup's packed qweight (64 rows x BN / 8 words, row-major as
+// stored) and the zero words + fp16 scales of the k-tile's two 32-row halves (g is
+// a multiple of 32, so no other group boundary can occur) go from global memory
+// straight into LDS (global_load_lds_dwordx4, no register round trip), kStages - 1
+// k-tiles ahead of the multiply; layouts are XOR-swizzled so that both the direct
+// loads and the fragment reads are conflict-free.
 // B operand, dequantised in registers: in a 32x32x16 B operand lane l supplies 8
 // consecutive k of column n = l % 32.  A wave's 32 FN columns are its packed word
 // columns x nibble positions: lane l takes word column l % 8 (FN = 2) or l % 4
@@ -34,8 +31,9 @@
 // Output columns are un-permuted at the store: MFMA column i of N-tile f is packed
 // word column (base + i % 8 or i % 4) at nibble position ((i / 8) % 4 + 4 f) or
 // (i / 4) % 8, i.e. output column 8 wc + ORDER[nibble].
-// Grid order: M tiles fastest, so consecutive workgroups (spread round-robin over
-// the 8 XCDs) share column tiles and each XCD's L2 sees one slab of x.
+// Grid order: XCD-aware (see the block order in the kernel): the column tiles that
+// share 128-byte weight lines run on one XCD, and M tiles (or table entries) are
+// fastest within a run, so each XCD's L2 also keeps one slab of x.
 #include <type_traits>
 
 #include "awq_device.h"
