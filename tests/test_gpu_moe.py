@@ -116,6 +116,9 @@ SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batch
     (8, 64, 2, 2048, 768, -1),     # most experts receive no slot
     (16, 8, 2, 4096, 1024, 128),   # 8-wave workgroups, fp32 partials
     (13, 6, 3, 4096, 320, 64),
+    (24, 16, 2, 4096, 1024, 128),  # 17-64 tokens, <= 8 slots per expert, >= 2 MB per expert:
+    (64, 32, 2, 2048, 2048, 64),   # chunks of 16 routed tokens
+    (33, 8, 1, 4096, 1056, 32),
 ]
 
 
@@ -128,15 +131,26 @@ def test_moe_gemm_few_tokens(T, E, topk, K, N, g):
     tol_check(y, yref, f"moe few T{T}E{E}k{topk}")
 
 
-@pytest.mark.parametrize("T", [3, 12])
-def test_moe_gemm_few_tokens_odd_routing(T):
+def test_moe_gemm_few_tokens_one_expert_many_chunks():
+    """40 tokens, every one on expert 2 (top-1 of 8): that expert's 40 routed tokens
+    take three 16-row chunks (16, 16, 8 rows); the other experts stream nothing."""
+    T, E, K, N, g = 40, 8, 4096, 1024, 64
+    d = synth.make_moe_custom(T, E, 1, K, N, g, seed=71)
+    d["expert_ids"] = np.full(T, 2, dtype=np.int32)
+    y = run(d)
+    yref = oracle.moe_gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["expert_ids"], 1, g)
+    tol_check(y, yref, "moe one expert, three chunks")
+
+
+@pytest.mark.parametrize("T,E,topk,K,N", [(3, 5, 3, 1024, 256), (12, 5, 3, 1024, 256), (30, 16, 2, 2048, 2048)])
+def test_moe_gemm_few_tokens_odd_routing(T, E, topk, K, N):
     """A token that names one expert twice gets that expert's row in both slots; slots
     whose id lies outside [0, E) route nowhere and keep what out held."""
-    E, topk, K, N, g = 5, 3, 1024, 256, 64
+    g = 64
     d = synth.make_moe_custom(T, E, topk, K, N, g, seed=T + 99)
     ids = d["expert_ids"].reshape(T, topk).copy()
     ids[0, 1] = ids[0, 0]          # repeated expert
-    ids[1, 2] = -1                 # routes nowhere
+    ids[1, topk - 1] = -1          # routes nowhere
     ids[T - 1, 0] = E              # routes nowhere
     d["expert_ids"] = ids.ravel()
     t = {k: torch.from_numpy(np.ascontiguousarray(d[k])).cuda() for k in ("x", "qweight", "qzeros", "scales")}

@@ -94,17 +94,20 @@ hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym,
 // x, bias and y are fp16 or (bf16 = true) bfloat16 bit patterns; scales are fp16.
 // bfloat16 skinny plans with splits > 1 always use partial (fp32 partials and the
 // reduce kernel), never accum.
-// Routed experts on the skinny family, for at most kSkinnyMaxM tokens: block x is
-// expert * tiles + column tile, x holds every token (row t = token t), and row t of
-// expert e's product goes to each slot t * topk + j with ids[t * topk + j] == e
-// (rows of tokens not routed to e are computed in the padded MFMA rows and never
-// stored).  A workgroup whose expert receives no slot exits before any load.
-// Expert e's weights start e * w_stride words into qweight (likewise qzeros and
-// scales).  Accumulators and partials are per block (expert and column tile).
+// Routed experts on the skinny family, for at most kSkinnyExpertsMaxT tokens: block x
+// is (chunk * experts + expert) * tiles + column tile.  The rows of a block are the
+// tokens routed to its expert (those with some ids[t * topk + j] == e), in token
+// order, from the (16 chunk)-th on, at most 16; row m goes to each slot t * topk + j
+// of its token t with ids[t * topk + j] == e.  A block without rows exits before any
+// load.  Expert e's weights start e * w_stride words into qweight (likewise qzeros
+// and scales).  Accumulators and partials are per block.
+constexpr int kSkinnyExpertsMaxT = 64;
 struct SkinnyExperts {
   const int32_t* ids;  // [T * topk]
   int topk;
   int tiles;           // column tiles per expert
+  int chunks;          // 16-row chunks of routed tokens per expert: ceil(T / 16)
+  int experts;
   int64_t w_stride, z_stride, s_stride;
 };
 hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,

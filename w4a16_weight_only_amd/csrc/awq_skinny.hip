@@ -157,28 +157,42 @@ struct SkinnyLds {
 
 }  // namespace
 
-// Routed experts: bit t of the result is set when token t (t < T <= 16) sends a
+// Routed experts: bit t of the result is set when token t (t < T <= 64) sends a
 // slot to `expert`.  Lanes 0..T-1 of the calling wave each test one token; every wave
 // of a workgroup gets the same mask.
-__device__ __forceinline__ uint32_t routed_tokens(const SkinnyExperts& ex, int T, int expert, int lane) {
+__device__ __forceinline__ uint64_t routed_tokens(const SkinnyExperts& ex, int T, int expert, int lane) {
   bool r = false;
   if (lane < T)
     for (int j = 0; j < ex.topk; ++j) r |= ex.ids[lane * ex.topk + j] == expert;
-  return (uint32_t)__ballot(r);
+  return (uint64_t)__ballot(r);
 }
 
 // Index of the n-th set bit of mask (n < popcount(mask)).
-__device__ __forceinline__ int nth_set_bit(uint32_t mask, int n) {
+__device__ __forceinline__ int nth_set_bit(uint64_t mask, int n) {
   for (int i = 0; i < n; ++i) mask &= mask - 1;
-  return __builtin_ctz(mask);
+  return __builtin_ctzll(mask);
+}
+
+// Block x of the routed-expert grid: chunk-major (every expert's first 16 routed
+// tokens first; the later chunks, empty for most experts, come last and exit at
+// once), then expert, then column tile.
+struct ExpertBlock {
+  int expert, chunk, tile;
+};
+__device__ __forceinline__ ExpertBlock expert_block(const SkinnyExperts& ex, int b, int experts) {
+  const int per_chunk = experts * ex.tiles;
+  const int c = b / per_chunk;
+  const int r = b - c * per_chunk;
+  return ExpertBlock{r / ex.tiles, c, r % ex.tiles};
 }
 
 // Workspace: per tile, 64-bit accumulator 4 * slot + i holds row 4 (slot / 256) + i
 // of the slot's column, slot = q * 256 + accumulator * 16 + c.  All zero between calls.
 // EXPERTS: routed experts (SkinnyExperts); M is the token count on entry, there is
-// no bias.  The block's rows are then only the tokens routed to its expert, in token
-// order (row m = the m-th such token), and M becomes their count: the MFMA rows, the
-// split accumulators or partials and the reduction cover just those rows.
+// no bias.  The block's rows are then only its chunk of the tokens routed to its
+// expert, in token order (row m = routed token 16 chunk + m), and M becomes their
+// count: the MFMA rows, the split accumulators or partials and the reduction cover
+// just those rows.
 template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
@@ -204,14 +218,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const int NW = N >> 3;
   // Column tile; with EXPERTS, block x also names the expert.  Accumulators and
   // partials belong to the block.
-  const int expert = EXPERTS ? (int)blockIdx.x / ex.tiles : 0;
-  const int tile = EXPERTS ? (int)blockIdx.x - expert * ex.tiles : (int)blockIdx.x;
+  const ExpertBlock eb = EXPERTS ? expert_block(ex, blockIdx.x, ex.experts) : ExpertBlock{0, 0, (int)blockIdx.x};
+  const int expert = eb.expert;
+  const int tile = eb.tile;
   const int split = blockIdx.y;
-  uint32_t tokens = 0;  // EXPERTS: the routed-token mask of this block's expert
+  uint64_t tokens = 0;  // EXPERTS: the routed-token mask of this block's expert
+  const int row0 = kSkinnyMaxM * eb.chunk;  // EXPERTS: first routed token of the chunk
   if constexpr (EXPERTS) {
     tokens = routed_tokens(ex, M, expert, lane);
-    if (tokens == 0) return;  // uniform: no slot of this expert
-    M = __builtin_popcount(tokens);
+    M = min(__builtin_popcountll(tokens) - row0, kSkinnyMaxM);
+    if (M <= 0) return;  // uniform: no routed token in this chunk
     qweight += expert * ex.w_stride;
     qzeros += expert * ex.z_stride;
     scales += expert * ex.s_stride;
@@ -220,7 +236,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // row's token routed to this block's expert.
   auto put = [&](int row, int n, float v) {
     if constexpr (EXPERTS) {
-      const int tok = nth_set_bit(tokens, row);
+      const int tok = nth_set_bit(tokens, row0 + row);
       for (int j = 0; j < ex.topk; ++j)
         if (ex.ids[tok * ex.topk + j] == expert) y[((int64_t)tok * ex.topk + j) * N + n] = float_to_act<BF16>(v);
     } else {
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // valid clamped address instead of being masked: an MFMA output row depends only
   // on its own x row, and rows >= M and columns >= N are never stored.
   const int m = lane & 15;
-  const int xrow = EXPERTS ? nth_set_bit(tokens, m < M ? m : 0) : (m < M ? m : 0);
+  const int xrow = EXPERTS ? nth_set_bit(tokens, row0 + (m < M ? m : 0)) : (m < M ? m : 0);
   const uint32_t x_off = ((uint32_t)xrow * (uint32_t)K + 8u * q) * 2u;
   const uint32_t w_off = ((uint32_t)(8 * q) * (uint32_t)NW + (uint32_t)(col_ok ? wc : 0)) * 4u;
   const uint32_t row_bytes = (uint32_t)NW * 4u;
@@ -494,10 +510,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 // 4 rows of slot 256 q + t (16 contiguous bytes per split), and the rounded values
 // meet in LDS in output order so that y is written as whole 16-byte row pieces.
 // tile_entries: rows kept per tile (4 or 16) x 256.
-// EXPERTS: partials of block b = expert * tiles + column tile, whose rows are the
-// tokens routed to the expert in token order (row m = the m-th such token); row m
-// goes to that token's slots of the expert.  Blocks of experts without a slot
-// wrote no partials and store nothing.
+// EXPERTS: partials of block b = (expert, chunk, column tile), whose rows are the
+// chunk's tokens routed to the expert in token order (row m = routed token
+// 16 chunk + m); row m goes to that token's slots of the expert.  Blocks without
+// rows wrote no partials and store nothing.
 template <bool BF16, bool EXPERTS = false>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             const uint16_t* __restrict__ bias, int M, int N,
@@ -506,12 +522,14 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   const int TILE_ENTRIES = tile_entries;
   __shared__ __attribute__((aligned(16))) uint16_t ys[4][kSkinnyCols + 8];
   const int block = blockIdx.x / 4, q = blockIdx.x % 4;
-  const int expert = EXPERTS ? block / ex.tiles : 0;
-  const int tile = EXPERTS ? block - expert * ex.tiles : block;
-  uint32_t tokens = 0;
+  const ExpertBlock eb = EXPERTS ? expert_block(ex, block, ex.experts) : ExpertBlock{0, 0, block};
+  const int expert = eb.expert;
+  const int tile = eb.tile;
+  const int row0 = kSkinnyMaxM * eb.chunk;
+  uint64_t tokens = 0;
   if constexpr (EXPERTS) {
     tokens = routed_tokens(ex, M, expert, threadIdx.x & 63);
-    M = __builtin_popcount(tokens);  // rows of the block (0: its expert got no slot)
+    M = min(__builtin_popcountll(tokens) - row0, kSkinnyMaxM);  // rows of the block (<= 0: none)
   }
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
@@ -530,7 +548,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     if (row < M && n0 < N) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&ys[i][8 * pc]);
       if constexpr (EXPERTS) {
-        const int tok = nth_set_bit(tokens, row);
+        const int tok = nth_set_bit(tokens, row0 + row);
         for (int j = 0; j < ex.topk; ++j)
           if (ex.ids[tok * ex.topk + j] == expert)
             *reinterpret_cast<u32x4*>(y + ((int64_t)tok * ex.topk + j) * N + n0) = v;
@@ -572,7 +590,7 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
   return hipGetLastError();
 }
 
-// Routed experts (fp16): p.n_tiles = experts x column tiles per expert.
+// Routed experts (fp16): p.n_tiles = chunks x experts x column tiles per expert.
 hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                                  const uint16_t* scales, int T, int K, int N, int g, const SkinnyPlan& p,
                                  const SkinnyExperts& ex, uint64_t* accum, float* partial, uint16_t* y,
