@@ -185,11 +185,13 @@ int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qze
  *                 rows, then (-1, 0, 0, 0)
  *   1 <= E <= 1024, S < 2^30.  Returns AWQ_OK or an error status.
  *
- * awq_moe_gemm: the grouped product, one call.  Up to 16 tokens: one launch of the
- * skinny kernel over (expert, column tile) blocks, every token a row, routed rows
- * stored, experts without a slot skipped (plus the split reduce for 5..16 tokens);
- * more tokens: alignment, then one launch of the MFMA tile kernel in which each
- * workgroup gathers the x rows of one expert's tile and scatters its y rows.
+ * awq_moe_gemm: the grouped product, one call.  Few tokens (up to 16; up to 64 when
+ * the experts average at most 8 slots and hold at least 2 MB of packed weight each):
+ * one launch of the skinny kernel over (16-token chunk, expert, column tile) blocks,
+ * each block's rows being its chunk of the tokens routed to its expert, experts
+ * without a slot skipped (plus the split reduce for 16-row plans); otherwise:
+ * alignment, then one launch of the MFMA tile kernel in which each workgroup
+ * gathers the x rows of one expert's tile and scatters its y rows.
  *   x_f16        device fp16 [T, K]
  *   qweight      device int32 [E, K, N/8];  qzeros int32 [E, G, N/8];  scales fp16 [E, G, N]
  *   expert_ids   device int32 [T * topk]
