@@ -46,9 +46,10 @@ struct TilePlan {
 };
 
 // Routed experts: the tile kernel's grouped mode.  Each workgroup takes one table
-// entry and one column tile (entries in place of row tiles in the block order of
-// tile_kernel); an entry is (expert, first sorted row, rows, 0), with expert < 0 for
-// an unused entry (the workgroup exits).  Row r of the entry
+// entry and one column tile (in the block order of tile_kernel, with entries
+// slowest, so that the unused entries at the end of the table take the last blocks);
+// an entry is (expert, first sorted row, rows, 0), with expert < 0 for an unused
+// entry (the workgroup exits).  Row r of the entry
 // is routed slot sorted_slots[first + r], which reads x row slot / topk and writes
 // y row slot.  Expert e's weights start e * w_stride words into qweight (and
 // likewise for qzeros and scales).

@@ -157,11 +157,21 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   constexpr int CT = 256 / BN;
   const int bx = blockIdx.x;
   const int u = (bx & 7) + 8 * (bx / (8 * CT));
-  const int row_units = GROUPED ? moe.tiles : m_tiles;
   const int n_tiles = (N + BN - 1) / BN;
-  int tile_m = u % row_units;
-  const int tile_n = CT * (u / row_units) + (bx >> 3) % CT;
-  if (tile_n >= n_tiles) return;  // also every unit past the last (its tile_n is larger still)
+  int tile_m, tile_n;
+  if constexpr (GROUPED) {
+    // Entries slowest: the unused entries at the end of the table (expert < 0) then
+    // take the last blocks of the grid, which exit at once, instead of slots among
+    // the working ones.
+    const int runs = (n_tiles + CT - 1) / CT;
+    tile_m = u / runs;
+    tile_n = CT * (u - tile_m * runs) + (bx >> 3) % CT;
+    if (tile_m >= moe.tiles || tile_n >= n_tiles) return;
+  } else {
+    tile_m = u % m_tiles;
+    tile_n = CT * (u / m_tiles) + (bx >> 3) % CT;
+    if (tile_n >= n_tiles) return;  // also every unit past the last (its tile_n is larger still)
+  }
   int first = 0;  // grouped: first sorted row of this workgroup's entry
   if constexpr (GROUPED) {
     const int ti = tile_m;
