@@ -97,7 +97,12 @@ __device__ __forceinline__ uint32_t b_pair(uint32_t magic_pair, half2v mult, hal
 // GROUPED: routed-expert mode (MoeTiles): each workgroup takes one table entry's
 // rows of one expert, gathers their x rows and scatters its y rows; no bias, no K
 // splits.
-template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false>
+// SKIP (grouped mode, 256-row tiles): this launch takes the entries with fewer than
+// BM / 2 rows and skips the MFMAs of the 32-row blocks past them; without SKIP the
+// launch takes the others and multiplies every block (the smaller grouped tiles take
+// every entry in one launch without SKIP).  A liveness test between the MFMAs costs a
+// full tile about a fifth of its time, so it lives in its own instantiation and launch.
+template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false, bool SKIP = false>
 __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
@@ -181,15 +186,18 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     if (e < 0) return;  // an unused entry: the whole workgroup leaves before any barrier
     first = ent[1];
     M = ent[2];         // rows of this entry (1 .. BM); rows are entry-local from here on
+    if constexpr (FM >= 4)
+      if ((2 * M < BM) != SKIP) return;  // the other launch's entry
     qweight += e * moe.w_stride;
     qzeros += e * moe.z_stride;
     scales += e * moe.s_stride;
   }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  // Grouped mode multiplies every 32-row block of the tile, also those past the
-  // entry's rows (their x rows are clamped copies and their sums are never stored):
-  // a per-block liveness test between the MFMAs cost a full 256-row tile about a
-  // fifth of its time, more than it saved on the partly filled tiles.
+  // Grouped mode without SKIP multiplies every 32-row block of the tile, also those
+  // past the entry's rows (their x rows are clamped copies and their sums are never
+  // stored); with SKIP, 32-row block i of this wave is multiplied only if it starts
+  // below the entry's row count (uniform per wave).
+  auto row_block_live = [&](int i) { return wm * 32 * FM + 32 * i < M; };
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
 
@@ -383,6 +391,8 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (SKIP)
+          if (!row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(f.a[i], bf[j], acc[i][j]);
@@ -467,6 +477,8 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (SKIP)
+          if (!row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(a[i], bf[j], acc[i][j]);
@@ -681,8 +693,14 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
                        reinterpret_cast<const _Float16*>(scales), nullptr, 0, K, N, g, 1, (K + kBK - 1) / kBK,
                        nullptr, y, moe);
   };
+  // 256-row tiles: two launches over the same table, entries of at least 128 rows
+  // without the block test, then the smaller ones (an expert's last few rows) with
+  // it.  The other variants hold at most two 32-row blocks per wave: one launch.
   switch (variant) {
-    case 0: go(tile_kernel<8, 1, 1, 2, false, true>, 128, 512); break;
+    case 0:
+      go(tile_kernel<8, 1, 1, 2, false, true, false>, 128, 512);
+      go(tile_kernel<8, 1, 1, 2, false, true, true>, 128, 512);
+      break;
     case 1: go(tile_kernel<2, 1, 2, 1, false, true>, 64, 256); break;
     case 2: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;
     default: go(tile_kernel<1, 1, 1, 1, false, true>, 128, 256); break;  // 32 x 128
