@@ -83,6 +83,8 @@ RAGGED = [  # (M, K, N, g, bias): both families, K splits through partials, tail
     (300, 96, 256, 32, True),       # partial last k-tile
     (40, 32, 96, 32, True),         # K = 32
     (257, 512, 256, 128, False),
+    (24, 4096, 512, 128, True),     # 32 x 128 tiles split over K
+    (20, 32, 96, 32, True),         # 32 x 128 tiles, K = 32
 ]
 
 

@@ -102,6 +102,9 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (300, 4096, 256, 128, False),  # 256 x 128 tiles split over K
     (40, 32, 96, 32, True),      # tile family, K = 32: one k-tile, only half of it real
     (300, 96, 256, 32, True),    # tile family, last k-tile partial (loaded 32 rows early)
+    (20, 32, 96, 32, True),      # 32 x 128 tiles: K = 32
+    (30, 96, 256, 32, True),     # 32 x 128 tiles: last k-tile partial
+    (24, 4128, 96, 32, True),    # 32 x 128 tiles split over K, last split ends in a half k-tile
 ]
 
 
