@@ -103,7 +103,7 @@ def tile_blocks(M, N, tile_rows, tile_cols):
 
 
 @pytest.mark.parametrize("M,K,N,g,tile_rows,tile_cols", [
-    (64, 11008, 4096, 64, 64, 128), (512, 11008, 4096, 64, 256, 128), (100, 2080, 160, -1, 128, 64)])
+    (64, 11008, 4096, 64, 64, 128), (512, 11008, 4096, 64, 256, 128), (100, 2080, 160, -1, 64, 128)])
 def test_tile_split_k_plans(M, K, N, g, tile_rows, tile_cols):
     """The tile family splits K on few tiles: grid (tile blocks, splits), every split
     keeps >= 8 k-tiles of 64 (or there is one split), the splits cover K exactly, and

@@ -86,9 +86,9 @@ def run(d):
 
 MOE_CASES = [  # (T, E, topk, K, N, g, routing)
     (5, 4, 2, 256, 96, 64, "random"),
-    (64, 8, 2, 512, 256, 128, "random"),       # 16 rows per expert: 64-row tiles
+    (64, 8, 2, 512, 256, 128, "random"),       # 16 rows per expert: 32-row tiles
     (300, 4, 1, 1024, 544, 32, "random"),
-    (200, 2, 1, 96, 128, 32, "random"),        # 128-row tiles, partial last k-tile
+    (200, 2, 1, 96, 128, 32, "random"),        # 64-row tiles, partial last k-tile
     (600, 4, 2, 256, 256, -1, "random"),       # 256-row tiles
     (1, 16, 4, 4096, 64, 128, "random"),
     (300, 8, 1, 512, 128, 64, "one_expert"),   # every slot on expert 3; the others empty

@@ -98,7 +98,7 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (1, 131072, 64, -1, True),   # skinny at the 128-split cap, 64 k-steps per wave
     (3, 65536, 96, 32, True),    # too many groups per workgroup for skinny: tile family
     (40, 4128, 96, 32, True),    # tile split over K, last split ends in a half k-tile
-    (100, 2080, 160, -1, True),  # 128 x 64 tiles split over K
+    (100, 2080, 160, -1, True),  # two 64 x 128 row tiles split over K
     (300, 4096, 256, 128, False),  # 256 x 128 tiles split over K
     (40, 32, 96, 32, True),      # tile family, K = 32: one k-tile, only half of it real
     (300, 96, 256, 32, True),    # tile family, last k-tile partial (loaded 32 rows early)

@@ -171,16 +171,17 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     auto tiles = [&](int v) {
       return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
     };
-    // Row tile by M: 256 x 128 above 128 rows, 128 x 64 above 64, 64 x 128 above 32,
-    // 32 x 128 below (a tile taller than M wastes MFMA rows and x loads; 32 x 128
-    // against 64 x 128 at 17-32 rows measured 6-25% faster).
+    // Row tile by M: 256 x 128 above 128 rows, 64 x 128 above 32, 32 x 128 below (a
+    // tile taller than M wastes MFMA rows and x loads: 32 x 128 against 64 x 128 at
+    // 17-32 rows measured 6-25% faster; at 65-128 rows two 64 x 128 row tiles beat
+    // one 128 x 64 tile by 4-13%, and at 33-64 one 64 x 128 tile beats two 32 x 128).
     // Above 128 rows the product is MFMA-bound: K is split only while the tiles
     // leave compute units idle.  At or below 128 rows the weight stream dominates
     // and K is split to about two workgroups per compute unit (rounded down;
     // measured best over 1 to 4 per unit on 4096- to 28672-wide layers).  Every
     // split keeps at least 8 k-tiles.
     const int64_t fill = (int64_t)cus * 3 / 4;
-    const int v = M > 128 ? 0 : (M > 64 ? 1 : (M > 32 ? 2 : 3));
+    const int v = M > 128 ? 0 : (M > 32 ? 1 : 2);
     const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
     int64_t splits = 1;
     if (v == 0) {

@@ -27,14 +27,14 @@ struct SkinnyPlan {
 };
 
 // MFMA tile family.  Variants (rows x columns per workgroup, threads):
-// 0: 256 x 128 (512: two k-groups of 4 waves), 1: 128 x 64 (256), 2: 64 x 128 (256),
-// 3: 32 x 128 (256).  With splits > 1 each workgroup covers kps k-tiles of 64 and
+// 0: 256 x 128 (512: two k-groups of 4 waves), 1: 64 x 128 (256), 2: 32 x 128 (256).
+// With splits > 1 each workgroup covers kps k-tiles of 64 and
 // writes fp32 sums to partial, [splits][M][N]; a second kernel adds the splits and
 // the bias.
-constexpr int kTileVariants = 4;
-constexpr int kTileBM[kTileVariants] = {256, 128, 64, 32};
-constexpr int kTileBN[kTileVariants] = {128, 64, 128, 128};
-constexpr int kTileThreads[kTileVariants] = {512, 256, 256, 256};
+constexpr int kTileVariants = 3;
+constexpr int kTileBM[kTileVariants] = {256, 64, 32};
+constexpr int kTileBN[kTileVariants] = {128, 128, 128};
+constexpr int kTileThreads[kTileVariants] = {512, 256, 256};
 constexpr int kTileBK = 64;
 // Blocks of a tile grid with row_units row tiles (or table entries): whole runs of
 // 8 * (256 / bn) blocks, so that the column tiles sharing 128-byte weight lines

@@ -8,8 +8,8 @@
 // Workgroup: KG groups of 4 waves as WM (M) x 4/WM (N); wave tile (32 FM) x (32 FN)
 // of v_mfma_f32_32x32x16_f16 accumulators.  Instantiations, chosen by M alone:
 // FM = 8, FN = 1, WM = 1, KG = 2 (256 x 128, 8 waves; each B column is dequantised
-// by one wave of a k-group) above 128 rows; FM = 2, FN = 1 with 2 x 2 waves
-// (128 x 64) from 65 rows, or 1 x 4 (64 x 128) from 33; FM = 1 (32 x 128) below.
+// by one wave of a k-group) above 128 rows; FM = 2, FN = 1 with 1 x 4 waves
+// (64 x 128) from 33; FM = 1 (32 x 128) below.
 //
 // Staging, per k-tile of 64 rows, in a ring of kStages LDS buffers: x (BM x 64
 // fp16), the workgroup's packed qweight (64 rows x BN / 8 words, row-major as
@@ -661,8 +661,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   };
   switch (p.variant) {
     case 0: go(tile_kernel<8, 1, 1, 2, BF16>, 256, 128, 512); break;
-    case 1: go(tile_kernel<2, 1, 2, 1, BF16>, 128, 64, 256); break;
-    case 2: go(tile_kernel<2, 1, 1, 1, BF16>, 64, 128, 256); break;
+    case 1: go(tile_kernel<2, 1, 1, 1, BF16>, 64, 128, 256); break;
     default: go(tile_kernel<1, 1, 1, 1, BF16>, 32, 128, 256); break;
   }
   hipError_t e = hipGetLastError();
@@ -674,12 +673,13 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   return hipGetLastError();
 }
 
-// Grouped variants by slots per expert: 256 x 128 from 192, 128 x 64 from 96,
-// 64 x 128 above 32, and 32 x 128 for the few rows per expert of decode-sized
-// batches, where the weights dominate and a smaller x tile lets four workgroups
-// share a CU.
+// Grouped variants by slots per expert: 256 x 128 from 192, 64 x 128 above 32, and
+// 32 x 128 for the few rows per expert of decode-sized batches, where the weights
+// dominate and a smaller x tile lets four workgroups share a CU.  Below 192 rows two
+// or three 64 x 128 row tiles beat one 256 x 128 tile that leaves rows idle; from
+// 192 the larger tile wins (768 tokens over 8 experts, top-2: 300 against 390 us).
 int moe_tile_variant(int64_t avg_rows, int* block_rows) {
-  const int v = avg_rows >= 192 ? 0 : (avg_rows >= 96 ? 1 : (avg_rows > 32 ? 2 : 3));
+  const int v = avg_rows >= 192 ? 0 : (avg_rows > 32 ? 1 : 2);
   *block_rows = kTileBM[v];
   return v;
 }
@@ -701,8 +701,7 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
       go(tile_kernel<8, 1, 1, 2, false, true, false>, 128, 512);
       go(tile_kernel<8, 1, 1, 2, false, true, true>, 128, 512);
       break;
-    case 1: go(tile_kernel<2, 1, 2, 1, false, true>, 64, 256); break;
-    case 2: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;
+    case 1: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;  // 64 x 128
     default: go(tile_kernel<1, 1, 1, 1, false, true>, 128, 256); break;  // 32 x 128
   }
   return hipGetLastError();
