@@ -190,8 +190,10 @@ int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qze
  * one launch of the skinny kernel over (16-token chunk, expert, column tile) blocks,
  * each block's rows being its chunk of the tokens routed to its expert, experts
  * without a slot skipped (plus the split reduce for 16-row plans); otherwise:
- * alignment, then one launch of the MFMA tile kernel in which each workgroup
- * gathers the x rows of one expert's tile and scatters its y rows.
+ * alignment, then the MFMA tile kernel, in which each workgroup gathers the x rows
+ * of one expert's tile and scatters its y rows (one launch, or two when the table
+ * has 256-row tiles: full tiles first, then each expert's last few rows in 64-row
+ * parts).
  *   x_f16        device fp16 [T, K]
  *   qweight      device int32 [E, K, N/8];  qzeros int32 [E, G, N/8];  scales fp16 [E, G, N]
  *   expert_ids   device int32 [T * topk]

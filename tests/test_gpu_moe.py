@@ -107,6 +107,22 @@ def test_moe_gemm(T, E, topk, K, N, g, routing):
     tol_check(y, yref, f"moe T{T}E{E}k{topk}")
 
 
+def test_moe_gemm_last_rows_of_256_row_tiles():
+    """Slots per expert 384, 383, 356, 64, 1 (top-1): the table has 256-row tiles,
+    the full tiles and a last tile of exactly 128 rows take the 256 x 128 launch, last
+    tiles of 127 and 100 rows take the 64 x 128 launch as two 64-row parts, those of
+    64 and 1 rows as one part (the second leaves)."""
+    counts = [384, 383, 356, 64, 1]
+    E, K, N, g = len(counts), 512, 384, 64
+    T = sum(counts)
+    d = synth.make_moe_custom(T, E, 1, K, N, g, seed=97)
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)
+    d["expert_ids"] = np.random.default_rng(98).permutation(ids).astype(np.int32)
+    y = run(d)
+    yref = oracle.moe_gemm_ref(d["x"], d["qweight"], d["qzeros"], d["scales"], d["expert_ids"], 1, g)
+    tol_check(y, yref, "moe last rows of 256-row tiles")
+
+
 SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batched skinny family
     (1, 8, 2, 4096, 512, 128),
     (3, 16, 4, 1024, 96, 32),      # N below one 256-column tile

@@ -479,7 +479,8 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
   const int variant = awq::moe_tile_variant(S / E, &block_rows);
   const int64_t tiles = awq_moe_tiles(S, E, block_rows);
   const int64_t bn = awq::kTileBN[variant];
-  if (tiles * ((N + bn - 1) / bn) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
+  // Grid of the launches (256-row tables also take a launch of two 64-row parts per entry).
+  if (awq::tile_blocks(tiles * (variant == 0 ? 2 : 1), N, (int)bn) >= (int64_t(1) << 31)) return AWQ_ERR_UNSUPPORTED;
   // Scratch: tile table (16-byte entries), offsets, sorted slots; written by the
   // alignment kernel before the product reads it, on the same stream.
   void* scratch = nullptr;

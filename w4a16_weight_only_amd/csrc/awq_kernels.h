@@ -60,6 +60,11 @@ struct MoeTiles {
   int topk;
   int tiles;
   int64_t w_stride, z_stride, s_stride;
+  // Set per launch: the launch takes the entries of lo <= rows < hi, each as sub
+  // row tiles of the kernel's BM rows (sub * BM covers the table's block rows or
+  // the entries' rows).
+  int sub = 1;
+  int lo = 0, hi = 1 << 30;
 };
 // Tile rows of the grouped variant picked for an average of `avg_rows` slots per
 // expert, and the variant itself.

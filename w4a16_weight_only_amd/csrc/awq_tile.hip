@@ -93,15 +93,10 @@ __device__ __forceinline__ uint32_t b_pair(uint32_t magic_pair, half2v mult, hal
   else return as_u32(qz * sc);
 }
 
-// GROUPED: routed-expert mode (MoeTiles): each workgroup takes one table entry's
-// rows of one expert, gathers their x rows and scatters its y rows; no bias, no K
-// splits.
-// SKIP (grouped mode, 256-row tiles): this launch takes the entries with fewer than
-// BM / 2 rows and skips the MFMAs of the 32-row blocks past them; without SKIP the
-// launch takes the others and multiplies every block (the smaller grouped tiles take
-// every entry in one launch without SKIP).  A liveness test between the MFMAs costs a
-// full tile about a fifth of its time, so it lives in its own instantiation and launch.
-template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false, bool SKIP = false>
+// GROUPED: routed-expert mode (MoeTiles): each workgroup takes BM rows (one row
+// tile of moe.sub) of one table entry, i.e. of one expert, gathers their x rows and
+// scatters its y rows; no bias, no K splits.
+template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false>
 __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
@@ -170,7 +165,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const int runs = (n_tiles + CT - 1) / CT;
     tile_m = u / runs;
     tile_n = CT * (u - tile_m * runs) + (bx >> 3) % CT;
-    if (tile_m >= moe.tiles || tile_n >= n_tiles) return;
+    if (tile_m >= moe.tiles * moe.sub || tile_n >= n_tiles) return;
   } else {
     tile_m = u % m_tiles;
     tile_n = CT * (u / m_tiles) + (bx >> 3) % CT;
@@ -178,25 +173,24 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   }
   int first = 0;  // grouped: first sorted row of this workgroup's entry
   if constexpr (GROUPED) {
-    const int ti = tile_m;
+    const int ti = tile_m / moe.sub;
+    const int part = tile_m - ti * moe.sub;  // row tile within the entry
     tile_m = 0;
     const int* ent = moe.table + 4 * ti;
     const int e = ent[0];
     if (e < 0) return;  // an unused entry: the whole workgroup leaves before any barrier
-    first = ent[1];
-    M = ent[2];         // rows of this entry (1 .. BM); rows are entry-local from here on
-    if constexpr (FM >= 4)
-      if ((2 * M < BM) != SKIP) return;  // the other launch's entry
+    const int rows = ent[2];
+    if (rows < moe.lo || rows >= moe.hi) return;  // the other launch's entry
+    first = ent[1] + part * BM;
+    M = min(rows - part * BM, BM);  // rows of this tile; rows are tile-local from here on
+    if (M <= 0) return;
     qweight += e * moe.w_stride;
     qzeros += e * moe.z_stride;
     scales += e * moe.s_stride;
   }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  // Grouped mode without SKIP multiplies every 32-row block of the tile, also those
-  // past the entry's rows (their x rows are clamped copies and their sums are never
-  // stored); with SKIP, 32-row block i of this wave is multiplied only if it starts
-  // below the entry's row count (uniform per wave).
-  auto row_block_live = [&](int i) { return wm * 32 * FM + 32 * i < M; };
+  // Grouped mode multiplies every 32-row block of the tile, also those past the
+  // tile's rows (their x rows are clamped copies and their sums are never stored).
   const int NW = N >> 3;
   const int wc0 = n0 / 8;
 
@@ -390,8 +384,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       if (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (SKIP)
-          if (!row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(f.a[i], bf[j], acc[i][j]);
@@ -476,8 +468,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     auto mfma_step = [&](const half8v(&a)[FM], const half8v(&bf)[2]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (SKIP)
-          if (!row_block_live(i)) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<BF16>(a[i], bf[j], acc[i][j]);
@@ -687,19 +677,26 @@ int moe_tile_variant(int64_t avg_rows, int* block_rows) {
 hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                                const uint16_t* scales, int K, int N, int g, int variant, const MoeTiles& moe,
                                uint16_t* y, hipStream_t stream) {
-  auto go = [&](auto kern, int bn, int threads) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks(moe.tiles, N, bn), 1u), dim3(threads), 0, stream, x,
-                       reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
-                       reinterpret_cast<const _Float16*>(scales), nullptr, 0, K, N, g, 1, (K + kBK - 1) / kBK,
-                       nullptr, y, moe);
+  auto go = [&](auto kern, int bn, int threads, int sub = 1, int lo = 0, int hi = 1 << 30) {
+    MoeTiles m = moe;
+    m.sub = sub;
+    m.lo = lo;
+    m.hi = hi;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks((int64_t)moe.tiles * sub, N, bn), 1u), dim3(threads), 0,
+                       stream, x, reinterpret_cast<const uint32_t*>(qweight),
+                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
+                       0, K, N, g, 1, (K + kBK - 1) / kBK, nullptr, y, m);
   };
-  // 256-row tiles: two launches over the same table, entries of at least 128 rows
-  // without the block test, then the smaller ones (an expert's last few rows) with
-  // it.  The other variants hold at most two 32-row blocks per wave: one launch.
+  // 256-row tables: two launches over the same table, the 256 x 128 tile on the
+  // entries of at least 128 rows, then the 64 x 128 tile on the smaller ones (an
+  // expert's last few rows), each as two 64-row parts (a part past the rows exits).
+  // A 256-row tile costs about one dequant pass of the expert's weights whatever its
+  // rows, a 64-row part about two fifths of that.  The other variants take every entry in one
+  // launch.
   switch (variant) {
     case 0:
-      go(tile_kernel<8, 1, 1, 2, false, true, false>, 128, 512);
-      go(tile_kernel<8, 1, 1, 2, false, true, true>, 128, 512);
+      go(tile_kernel<8, 1, 1, 2, false, true>, 128, 512, 1, 128);
+      go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256, 2, 0, 128);
       break;
     case 1: go(tile_kernel<2, 1, 1, 1, false, true>, 128, 256); break;  // 64 x 128
     default: go(tile_kernel<1, 1, 1, 1, false, true>, 128, 256); break;  // 32 x 128
