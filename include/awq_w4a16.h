@@ -127,8 +127,10 @@ int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* s
  * M == 0 returns AWQ_OK and enqueues nothing (GPTQModel wiki, "Native GEMM": empty
  * input launches no kernel).  Two kernel families are chosen by M: a
  * bandwidth-bound skinny family for small M and an MFMA tile family above it
- * (awq_gemm_plan reports the choice).  The result is deterministic: the same
- * inputs give the same bits on every call.
+ * (awq_gemm_plan reports the choice).  In the tile family a partly filled last
+ * 256-row tile that would take one more round of the compute units runs as a
+ * second launch of its own (awq_gemm_plan_tail).  The result is deterministic: the
+ * same inputs give the same bits on every call.
  * Workspace: the skinny family splits K across workgroups and reduces the partial
  * sums in a fixed order through a library-owned device buffer, one per
  * (device, stream).  The first call on a (device, stream) that needs a larger
@@ -252,13 +254,25 @@ int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size
  * The launch plan awq_gemm would use for this shape (host-only, no device work).
  *   family   0 = skinny split-K family, 1 = MFMA tile family
  *   splits   number of K splits across workgroups (1 = none)
- *   grid_x, grid_y, block   launch geometry of the main kernel
+ *   grid_x, grid_y, block   launch geometry of the main kernel (tile family: of the
+ *                           first launch, over rows 0 .. M - rows of awq_gemm_plan_tail)
  *   workspace_bytes         device workspace the call needs (0 if none)
  * Any output pointer may be NULL.  Returns AWQ_OK or the awq_check_limits status.
  */
 int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size,
                   int* family, int* splits, int* grid_x, int* grid_y, int* block,
                   int64_t* workspace_bytes);
+
+/*
+ * The second tile launch of awq_gemm for this shape, over the last rows (host-only).
+ *   rows     rows of that launch, the last rows of x and y (0: one launch only)
+ *   splits, grid_x, grid_y, block   as in awq_gemm_plan, for that launch
+ * awq_gemm_plan's workspace_bytes covers both launches (they run in stream order
+ * and share it).  Any output pointer may be NULL.  Returns AWQ_OK or the
+ * awq_check_limits status.
+ */
+int awq_gemm_plan_tail(int64_t M, int64_t K, int64_t N, int64_t group_size,
+                       int64_t* rows, int* splits, int* grid_x, int* grid_y, int* block);
 
 #ifdef __cplusplus
 }

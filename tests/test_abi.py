@@ -123,6 +123,41 @@ def test_tile_split_k_plans(M, K, N, g, tile_rows, tile_cols):
         awq.plan(1, 4096, 4104, 128)
 
 
+@pytest.mark.parametrize("M,K,N,tail_rows", [(2100, 4096, 4096, 52), (1100, 4096, 4096, 76),
+                                              (2300, 4096, 4096, 252), (2049, 64, 4096, 1),
+                                              (300, 4096, 4096, 0), (600, 4096, 11008, 0),
+                                              (2100, 4096, 14336, 0), (2048, 4096, 4096, 0)])
+def test_tile_second_launch(M, K, N, tail_rows):
+    """A partly filled last 256-row tile goes to a second launch exactly when the
+    256 x 128 workgroups (one per compute unit of 256) of the whole would take one
+    more round than those of the full tiles; the first launch then covers the full
+    tiles, the second the rest, and the workspace covers the larger of the two."""
+    def launch(rows):
+        bm, bn = (256, 128) if rows > 128 else ((64, 128) if rows > 32 else (32, 128))
+        tiles = -(-rows // bm) * -(-N // bn)
+        kt = -(-K // 64)
+        if bm == 256:
+            s = -(-256 // tiles) if tiles < 192 else 1
+        else:
+            s = max(1, 512 // tiles)
+        s = min(s, max(1, kt // 8))
+        s = -(-kt // -(-kt // s))
+        return tiles * s, s, tile_blocks(rows, N, bm, bn)
+    p = awq.plan(M, K, N, 128 if K >= 128 else -1)
+    if tail_rows == 0:
+        assert p["tail"] is None
+        return
+    full = M - tail_rows
+    wg_all, _, _ = launch(M)
+    wg_main, s_main, gx_main = launch(full)
+    wg_tail, s_tail, gx_tail = launch(tail_rows)
+    assert -(-wg_main // 256) < -(-wg_all // 256)
+    assert p["grid"] == (gx_main, s_main) and p["splits"] == s_main
+    assert p["tail"]["rows"] == tail_rows and p["tail"]["grid"] == (gx_tail, s_tail)
+    need = max(s_main * full * N * 4 if s_main > 1 else 0, s_tail * tail_rows * N * 4 if s_tail > 1 else 0)
+    assert p["workspace_bytes"] >= need
+
+
 def test_gemm_argument_errors_touch_no_device(lib):
     """Checks run before any HIP call, so these are safe without a GPU."""
     p = ctypes.c_void_p(1 << 20)  # aligned dummy, never dereferenced

@@ -85,6 +85,7 @@ RAGGED = [  # (M, K, N, g, bias): both families, K splits through partials, tail
     (257, 512, 256, 128, False),
     (24, 4096, 512, 128, True),     # 32 x 128 tiles split over K
     (20, 32, 96, 32, True),         # 32 x 128 tiles, K = 32
+    (2100, 128, 4096, 64, True),    # last 52 rows in a second launch
 ]
 
 

@@ -122,6 +122,9 @@ LARGE = [  # (M, K, N, g): extreme grid shapes (the oracle stays cheap with smal
     (1, 64, 131072, 32),         # 512 skinny column tiles
     (40, 96, 131072, 32),        # 2048 column tiles of the 64 x 128 variant
     (300, 32768, 64, 128),       # long K on the tile family, split over K
+    (2049, 64, 4096, -1),        # one full round of 256-row tiles, then a 1-row second launch
+    (2100, 128, 4096, 64),       # second launch: 52 rows on 64 x 128 tiles
+    (2248, 1024, 4096, 128),     # second launch: 200 rows on 256 x 128 tiles split over K
 ]
 
 

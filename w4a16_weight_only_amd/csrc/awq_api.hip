@@ -37,10 +37,22 @@ int limits_check(int64_t M, int64_t K, int64_t N, int64_t group_size) {
   return AWQ_OK;
 }
 
+struct TileLaunch {
+  awq::TilePlan tp{};   // splits 0: no launch
+  int grid_x = 0, block = 0;
+  int64_t workgroups = 0;  // working workgroups (tiles x splits)
+  // Rounds of 256 x 128 workgroups, one per compute unit at a time.
+  int64_t rounds(int cus) const { return (workgroups + cus - 1) / cus; }
+};
+
 struct Plan {
   int family = 0;  // 0 skinny, 1 tile
   awq::SkinnyPlan sk{};
   awq::TilePlan tp{};
+  // Tile family: the launch over rows [0, rows1), and over rows [rows1, M) when
+  // rows1 < M (the last, partly filled 256-row tile in a launch of its own).
+  int64_t rows1 = 0;
+  TileLaunch tile{}, tail{};
   int grid_x = 0, grid_y = 0, block = 0;
   int64_t accum_bytes = 0;    // zero-maintained fixed-point accumulators (4-wave plans)
   int64_t partial_bytes = 0;  // scratch fp32 partials (8-wave skinny plans, split tile plans)
@@ -153,6 +165,44 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   return true;
 }
 
+// One launch of the tile family over M rows.
+TileLaunch plan_tile(int64_t M, int64_t K, int64_t N, int cus) {
+  auto tiles = [&](int v) {
+    return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
+  };
+  // Row tile by M: 256 x 128 above 128 rows, 64 x 128 above 32, 32 x 128 below (a
+  // tile taller than M wastes MFMA rows and x loads: 32 x 128 against 64 x 128 at
+  // 17-32 rows measured 6-25% faster; at 65-128 rows two 64 x 128 row tiles beat
+  // one 128 x 64 tile by 4-13%, and at 33-64 one 64 x 128 tile beats two 32 x 128).
+  // Above 128 rows the product is MFMA-bound: K is split only while the tiles
+  // leave compute units idle.  At or below 128 rows the weight stream dominates
+  // and K is split to about two workgroups per compute unit (rounded down;
+  // measured best over 1 to 4 per unit on 4096- to 28672-wide layers).  Every
+  // split keeps at least 8 k-tiles.
+  const int64_t fill = (int64_t)cus * 3 / 4;
+  const int v = M > 128 ? 0 : (M > 32 ? 1 : 2);
+  const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
+  int64_t splits = 1;
+  if (v == 0) {
+    if (tiles(v) < fill) splits = ((int64_t)cus + tiles(v) - 1) / tiles(v);
+  } else {
+    splits = 2 * (int64_t)cus / tiles(v);
+    if (splits < 1) splits = 1;
+  }
+  const int64_t max_splits = KT / 8 > 1 ? KT / 8 : 1;
+  if (splits > max_splits) splits = max_splits;
+  const int64_t kps = (KT + splits - 1) / splits;
+  splits = (KT + kps - 1) / kps;
+  TileLaunch t;
+  t.tp.variant = v;
+  t.tp.splits = (int)splits;
+  t.tp.kps = (int)kps;
+  t.block = awq::kTileThreads[v];
+  t.grid_x = (int)awq::tile_blocks((M + awq::kTileBM[v] - 1) / awq::kTileBM[v], N, awq::kTileBN[v]);
+  t.workgroups = tiles(v) * splits;
+  return t;
+}
+
 Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = false) {
   Plan p;
   if (M <= AWQ_SKINNY_MAX_M && plan_skinny(M, K, N, g, cus, p.sk)) {
@@ -168,39 +218,30 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     }
   } else {
     p.family = 1;
-    auto tiles = [&](int v) {
-      return ((M + awq::kTileBM[v] - 1) / awq::kTileBM[v]) * ((N + awq::kTileBN[v] - 1) / awq::kTileBN[v]);
-    };
-    // Row tile by M: 256 x 128 above 128 rows, 64 x 128 above 32, 32 x 128 below (a
-    // tile taller than M wastes MFMA rows and x loads: 32 x 128 against 64 x 128 at
-    // 17-32 rows measured 6-25% faster; at 65-128 rows two 64 x 128 row tiles beat
-    // one 128 x 64 tile by 4-13%, and at 33-64 one 64 x 128 tile beats two 32 x 128).
-    // Above 128 rows the product is MFMA-bound: K is split only while the tiles
-    // leave compute units idle.  At or below 128 rows the weight stream dominates
-    // and K is split to about two workgroups per compute unit (rounded down;
-    // measured best over 1 to 4 per unit on 4096- to 28672-wide layers).  Every
-    // split keeps at least 8 k-tiles.
-    const int64_t fill = (int64_t)cus * 3 / 4;
-    const int v = M > 128 ? 0 : (M > 32 ? 1 : 2);
-    const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
-    int64_t splits = 1;
-    if (v == 0) {
-      if (tiles(v) < fill) splits = ((int64_t)cus + tiles(v) - 1) / tiles(v);
-    } else {
-      splits = 2 * (int64_t)cus / tiles(v);
-      if (splits < 1) splits = 1;
+    // A partly filled last 256-row tile whose workgroups would take one more round of
+    // the compute units (one 256 x 128 workgroup per unit) goes to a second launch with
+    // its own row tile and K splits: M = 2100 on 4096 x 4096, 137 -> 104 us; M = 1100,
+    // 97 -> 77 us.  Where the round count stays, one launch is faster (M = 300 or
+    // 600: the second launch's fixed cost and its reduce).
+    const TileLaunch all = plan_tile(M, K, N, cus);
+    p.rows1 = M;
+    p.tile = all;
+    const int64_t r = M % awq::kTileBM[0];
+    if (all.tp.variant == 0 && M > awq::kTileBM[0] && r != 0) {
+      const TileLaunch main = plan_tile(M - r, K, N, cus);
+      if (main.rounds(cus) < all.rounds(cus)) {
+        p.rows1 = M - r;
+        p.tile = main;
+        p.tail = plan_tile(r, K, N, cus);
+      }
     }
-    const int64_t max_splits = KT / 8 > 1 ? KT / 8 : 1;
-    if (splits > max_splits) splits = max_splits;
-    const int64_t kps = (KT + splits - 1) / splits;
-    splits = (KT + kps - 1) / kps;
-    p.tp.variant = v;
-    p.block = awq::kTileThreads[v];
-    p.tp.splits = (int)splits;
-    p.tp.kps = (int)kps;
-    p.grid_x = (int)awq::tile_blocks((M + awq::kTileBM[v] - 1) / awq::kTileBM[v], N, awq::kTileBN[v]);
-    p.grid_y = (int)splits;
-    if (splits > 1) p.partial_bytes = splits * M * N * 4;
+    p.tp = p.tile.tp;
+    p.block = p.tile.block;
+    p.grid_x = p.tile.grid_x;
+    p.grid_y = p.tile.tp.splits;
+    const int64_t b1 = p.tile.tp.splits > 1 ? p.tile.tp.splits * p.rows1 * N * 4 : 0;
+    const int64_t b2 = p.tail.tp.splits > 1 ? p.tail.tp.splits * (M - p.rows1) * N * 4 : 0;
+    p.partial_bytes = b1 > b2 ? b1 : b2;  // the launches run in stream order
   }
   return p;
 }
@@ -323,6 +364,24 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* fami
   return AWQ_OK;
 }
 
+int awq_gemm_plan_tail(int64_t M, int64_t K, int64_t N, int64_t group_size, int64_t* rows, int* splits,
+                       int* grid_x, int* grid_y, int* block) {
+  const int st = limits_check(M, K, N, group_size);
+  if (st != AWQ_OK) return st;
+  int cus = 256;
+  int count = 0;
+  if (hipGetDeviceCount(&count) == hipSuccess && count > 0) cus = device_cus();
+  else (void)hipGetLastError();
+  const Plan p = make_plan(M, K, N, eff_group(K, group_size), cus);
+  const bool tail = p.family == 1 && p.rows1 < M;
+  if (rows) *rows = tail ? M - p.rows1 : 0;
+  if (splits) *splits = tail ? p.tail.tp.splits : 0;
+  if (grid_x) *grid_x = tail ? p.tail.grid_x : 0;
+  if (grid_y) *grid_y = tail ? p.tail.tp.splits : 0;
+  if (block) *block = tail ? p.tail.block : 0;
+  return AWQ_OK;
+}
+
 namespace {
 int dequant_common(const int32_t* qweight, const int32_t* qzeros, const void* scales_f16, int64_t K, int64_t N,
                    int64_t group_size, void* out, bool f16, hipStream_t stream) {
@@ -399,11 +458,15 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
   } else {
     uint64_t* accum = nullptr;
     float* partial = nullptr;
-    if (p.tp.splits > 1) {
+    if (p.tp.splits > 1 || p.tail.tp.splits > 1) {
       const int ws = get_workspace(p, stream, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
-    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.tp, bf16, partial, y, stream);
+    e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)p.rows1, (int)K, (int)N, g, p.tp, bf16, partial, y,
+                         stream);
+    if (e == hipSuccess && p.rows1 < M)
+      e = awq::launch_tile(x + p.rows1 * K, qweight, qzeros, sc, b, (int)(M - p.rows1), (int)K, (int)N, g,
+                           p.tail.tp, bf16, partial, y + p.rows1 * N, stream);
   }
   return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP;
 }

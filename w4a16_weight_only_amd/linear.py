@@ -63,15 +63,23 @@ def validate(K: int, N: int, group_size: int, qweight, qzeros, scales, bias=None
 
 
 def plan(M: int, K: int, N: int, group_size: int) -> dict:
-    """The launch plan awq_gemm uses for a shape (host-only)."""
+    """The launch plan awq_gemm uses for a shape (host-only); tail: the second tile
+    launch over the last rows, or None."""
     lib = _lib.load()
     vals = [ctypes.c_int() for _ in range(5)]
     ws = ctypes.c_int64()
     st = lib.awq_gemm_plan(M, K, N, group_size, *[ctypes.byref(v) for v in vals], ctypes.byref(ws))
     _lib.check(st, "awq_gemm_plan")
     fam, splits, gx, gy, block = (v.value for v in vals)
+    rows = ctypes.c_int64()
+    tv = [ctypes.c_int() for _ in range(4)]
+    st = lib.awq_gemm_plan_tail(M, K, N, group_size, ctypes.byref(rows), *[ctypes.byref(v) for v in tv])
+    _lib.check(st, "awq_gemm_plan_tail")
+    tail = None
+    if rows.value:
+        tail = dict(rows=rows.value, splits=tv[0].value, grid=(tv[1].value, tv[2].value), block=tv[3].value)
     return dict(family="skinny" if fam == 0 else "tile", splits=splits, grid=(gx, gy), block=block,
-                workspace_bytes=ws.value)
+                workspace_bytes=ws.value, tail=tail)
 
 
 def awq_dequant(qweight: torch.Tensor, qzeros: torch.Tensor, scales: torch.Tensor,
