@@ -191,7 +191,7 @@ int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qze
  * the experts average at most 8 slots and hold at least 2 MB of packed weight each):
  * one launch of the skinny kernel over (16-token chunk, expert, column tile) blocks,
  * each block's rows being its chunk of the tokens routed to its expert, experts
- * without a slot skipped (plus the split reduce for 16-row plans); otherwise:
+ * without a slot skipped (plus the split reduce for plans of three or more rows); otherwise:
  * alignment, then the MFMA tile kernel, in which each workgroup gathers the x rows
  * of one expert's tile and scatters its y rows (one launch, or two when the table
  * has 256-row tiles: full tiles first, then each expert's last few rows in 64-row

@@ -135,6 +135,8 @@ SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batch
     (24, 16, 2, 4096, 1024, 128),  # 17-64 tokens, <= 8 slots per expert, >= 2 MB per expert:
     (64, 32, 2, 2048, 2048, 64),   # chunks of 16 routed tokens
     (33, 8, 1, 4096, 1056, 32),
+    (4, 32, 2, 2048, 2048, 64),    # 3-4 tokens over many column tiles: 4-row plan, fp32 partials
+    (3, 16, 1, 4096, 4096, 128),
 ]
 
 

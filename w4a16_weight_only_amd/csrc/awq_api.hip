@@ -93,16 +93,22 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   const int64_t gsteps = g / awq::kKStep;  // g already resolved (-1 -> K)
   s.n_tiles = (int)((N + awq::kSkinnyCols - 1) / awq::kSkinnyCols);
   // One or two rows: 4-row plans (4 waves, splits meet in fixed-point atomics).
-  // From three rows the 16-row plans (fp32 partials and the reduce kernel) are
-  // faster, since every split costs the atomic plans one returning atomic per row
-  // and column (M = 3, 4: 10-25% faster; M = 2 mixed, within 7% either way).
-  // 16-row plans take 8 waves, or 4 waves (two per CU, shorter workgroups
-  // overlapping each other's fixed phases) once the 8-wave grid would take more
-  // than four rounds (layers above ~32 MB of packed weights): measured 8-15%
-  // faster on 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on
-  // layers of up to 22 MB.
-  s.mrows = M <= 2 ? 4 : 16;
-  s.waves = (M <= 2 || T * s.n_tiles > (int64_t)8 * cus * 4) ? 4 : 8;
+  // From three rows the atomics cost more than fp32 partials and the reduce kernel
+  // (every split costs one returning atomic per row and column; M = 3, 4: 10-25%
+  // faster with partials; M = 2 mixed, within 7% either way).  Three or four rows
+  // on a layer whose 8-wave grid would take more than four rounds (above ~32 MB of
+  // packed weights) take 4-row plans with partials: their smaller LDS reduction
+  // buffer lets more workgroups share a compute unit (4096 x 114688: 69.5 -> 62.8
+  // us; 8192 x 28672: 37.3 -> 33.3 us; routed experts at 3-4 tokens 6-10%); on
+  // smaller layers they measured 0-3% slower than the 16-row plans.  16-row plans
+  // take 8 waves, or 4 waves (two per CU, shorter workgroups overlapping each
+  // other's fixed phases) on those large layers: measured 8-15% faster on
+  // 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on layers of up
+  // to 22 MB.
+  const bool large = T * s.n_tiles > (int64_t)8 * cus * 4;
+  s.mrows = (M <= 2 || (M <= 4 && large)) ? 4 : 16;
+  s.atomic = M <= 2;
+  s.waves = (s.mrows == 4 || large) ? 4 : 8;
   const int64_t W = s.waves;
   // Whole grid resident in one round, counting two 4-wave workgroups per CU (three
   // fit when every wave stays inside one group; counting three gives more splits,
@@ -119,12 +125,13 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   const int64_t l_floor = M == 2 ? 4 : 2;
   if (L < l_floor) L = l_floor;
   if (L > T) L = T;
-  // One or two rows on a grid of more than two rounds: keep each wave's run inside
-  // one group (at most 4 k-steps).  Such waves need no per-group LDS tables and
-  // fewer registers, so three workgroups share a compute unit, and the extra splits
-  // cost one atomic per output element each; with more rows the atomics outweigh
-  // the gain (measured on 4096 x 114688, 8192 x 28672 and 28672 x 8192 layers).
-  if (M <= 2 && gsteps < T && L > gsteps && T * s.n_tiles > W * cap * 2) L = gsteps < 4 ? gsteps : 4;
+  // 4-row plans on a grid of more than two rounds: keep each wave's run inside one
+  // group (at most 4 k-steps).  Such waves need no per-group LDS tables and fewer
+  // registers, so three workgroups share a compute unit, and the extra splits cost
+  // one atomic (or partial) per output element each; on 16-row plans the extra
+  // splits outweigh the gain (measured on 4096 x 114688, 8192 x 28672 and
+  // 28672 x 8192 layers).
+  if (s.mrows == 4 && gsteps < T && L > gsteps && T * s.n_tiles > W * cap * 2) L = gsteps < 4 ? gsteps : 4;
   auto splits_of = [&](int64_t l) { return (T + W * l - 1) / (W * l); };
   if (gsteps >= T) {
     s.single_group = true;  // one group spans K
@@ -213,7 +220,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     // 4-row fp16 plans: 64-bit fixed-point accumulators per tile entry; 16-row
     // plans and every bfloat16 plan: fp32 partials per (tile, split, entry).
     if (p.sk.splits > 1) {
-      if (p.sk.mrows == 4 && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+      if (p.sk.atomic && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
       else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * awq::kSkinnyCols * 4;
     }
   } else {
@@ -522,7 +529,7 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
                   device_cus(), sk)) {
     Plan p;
     if (sk.splits > 1) {
-      if (sk.mrows == 4) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
+      if (sk.atomic) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
       else p.partial_bytes = (int64_t)sk.n_tiles * sk.splits * sk.mrows * awq::kSkinnyCols * 4;
     }
     uint64_t* accum = nullptr;

@@ -24,6 +24,7 @@ struct SkinnyPlan {
   int waves;         // 4 or 8 waves per workgroup (8 only for 16-row plans)
   int mrows;         // rows kept per tile: 4 or 16
   bool single_group; // every wave's k-steps lie in one quantization group
+  bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
 };
 
 // MFMA tile family.  Variants (rows x columns per workgroup, threads):
@@ -95,9 +96,9 @@ RtnPlan rtn_plan(int64_t K, int64_t N, int g);
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
                                int32_t* qzeros, uint16_t* scales, void* scratch, hipStream_t stream);
 
-// With p.splits > 1: 4-row plans use accum, [n_tiles][4 * 256] 64-bit
-// accumulators that are zero before the call and left zero by it; 16-row plans use
-// partial, [n_tiles][splits][16 * 256] fp32 scratch, and a second reduce kernel.
+// With p.splits > 1: atomic plans use accum, [n_tiles][4 * 256] 64-bit
+// accumulators that are zero before the call and left zero by it; the others use
+// partial, [n_tiles][splits][mrows * 256] fp32 scratch, and a second reduce kernel.
 // x, bias and y are fp16 or (bf16 = true) bfloat16 bit patterns; scales are fp16.
 // bfloat16 skinny plans with splits > 1 always use partial (fp32 partials and the
 // reduce kernel), never accum.

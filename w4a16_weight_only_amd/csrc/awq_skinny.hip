@@ -10,7 +10,8 @@
 // WAVES*L 32-row k-steps; wave w takes L consecutive k-steps of that run.  The host
 // picks L and the number of K splits S (about one resident round of workgroups on
 // small layers, shorter one-group runs on large ones) and the plan's rows: 4-row
-// plans (one or two rows of x) or 16-row plans (up to 16).
+// plans (one or two rows of x; three or four on large layers) or 16-row plans (up
+// to 16).
 // At a few microseconds per call the kernel is latency-bound, so every input is
 // requested up front: each wave issues the weight loads of its first two k-steps,
 // and the workgroup turns the zero words and scales of every group it touches into
@@ -30,10 +31,10 @@
 // Groups: the MFMA accumulates sum_k x (q - z) per group; at the end of a group the
 // sum is scaled by s in fp32 (exact dequant, no fp16 weight rounding).
 // Reduction: the waves' accumulators meet in LDS in register order (conflict-free
-// 16-byte accesses) and are summed in wave order.  With S > 1 splits, 16-row plans
-// (and bfloat16) store fp32 partials that a second kernel sums in split order; in
-// 4-row fp16 plans the splits of an output element meet in one 64-bit accumulator
-// in the workspace: each workgroup
+// 16-byte accesses) and are summed in wave order.  With S > 1 splits, the plans of
+// three or more rows (and bfloat16) store fp32 partials that a second kernel sums in
+// split order; in fp16 plans of one or two rows (ATOMIC) the splits of an output
+// element meet in one 64-bit accumulator in the workspace: each workgroup
 // adds, with one relaxed atomic fetch-add, its partial as a fixed-point integer
 // (24 fractional bits) plus 2^56, i.e. one arrival in the top byte.  Integer
 // addition does not depend on order, so the sum is bit-reproducible; the add that
@@ -193,7 +194,7 @@ __device__ __forceinline__ ExpertBlock expert_block(const SkinnyExperts& ex, int
 // expert, in token order (row m = routed token 16 chunk + m), and M becomes their
 // count: the MFMA rows, the split accumulators or partials and the reduction cover
 // just those rows.
-template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false>
+template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false, bool ATOMIC = MROWS == 4 && !BF16>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
@@ -201,13 +202,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y, SkinnyExperts ex) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
-  // k-steps in flight per wave, and how K splits meet: 4-row plans combine splits
-  // with fixed-point atomics; 16-row plans (4 or 8 waves; the atomic count M * N * S
-  // gets large) store fp32 partials for skinny_reduce_kernel.
+  // k-steps in flight per wave, and how K splits meet: ATOMIC (4-row fp16 plans of
+  // one or two rows) combines splits with fixed-point atomics; the other plans (the
+  // atomic count M * N * S gets large) store fp32 partials for skinny_reduce_kernel.
   // bfloat16 always takes the partials: the fixed-point format relies on fp16's
   // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
   constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
-  constexpr bool ATOMIC = MROWS == 4 && !BF16;
+  static_assert(!ATOMIC || (MROWS == 4 && !BF16), "fixed-point atomics: 4-row fp16 plans only");
   __shared__ SkinnyLds<WAVES, (MROWS > 4 ? 64 : 16)> sh;
 
   const int tid = threadIdx.x;
@@ -570,9 +571,12 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), bias,
                        M, K, N, g, p.L, p.splits, accum, partial, y, SkinnyExperts{});
   };
-  if (p.mrows == 4) {
-    if (p.single_group) go(skinny_kernel<4, 4, true, BF16>, 256);
-    else go(skinny_kernel<4, 4, false, BF16>, 256);
+  if (p.mrows == 4 && p.atomic && !BF16) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, false, false, true>, 256);
+    else go(skinny_kernel<4, 4, false, false, false, true>, 256);
+  } else if (p.mrows == 4) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, BF16, false, false>, 256);
+    else go(skinny_kernel<4, 4, false, BF16, false, false>, 256);
   } else if (p.waves == 4) {
     if (p.single_group) go(skinny_kernel<4, 16, true, BF16>, 256);
     else go(skinny_kernel<4, 16, false, BF16>, 256);
@@ -580,8 +584,8 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
     if (p.single_group) go(skinny_kernel<8, 16, true, BF16>, 512);
     else go(skinny_kernel<8, 16, false, BF16>, 512);
   }
-  // Partials (16-row plans, and every bfloat16 plan) are summed by the reduce kernel.
-  if (p.splits > 1 && (p.mrows == 16 || BF16)) {
+  // Partials (every plan but the atomic ones) are summed by the reduce kernel.
+  if (p.splits > 1 && !(p.mrows == 4 && p.atomic && !BF16)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(skinny_reduce_kernel<BF16>, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N,
@@ -601,9 +605,12 @@ hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, cons
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
                        T, K, N, g, p.L, p.splits, accum, partial, y, ex);
   };
-  if (p.mrows == 4) {
-    if (p.single_group) go(skinny_kernel<4, 4, true, false, true>, 256);
-    else go(skinny_kernel<4, 4, false, false, true>, 256);
+  if (p.mrows == 4 && p.atomic) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, false, true, true>, 256);
+    else go(skinny_kernel<4, 4, false, false, true, true>, 256);
+  } else if (p.mrows == 4) {
+    if (p.single_group) go(skinny_kernel<4, 4, true, false, true, false>, 256);
+    else go(skinny_kernel<4, 4, false, false, true, false>, 256);
   } else if (p.waves == 4) {
     if (p.single_group) go(skinny_kernel<4, 16, true, false, true>, 256);
     else go(skinny_kernel<4, 16, false, false, true>, 256);
@@ -611,7 +618,7 @@ hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, cons
     if (p.single_group) go(skinny_kernel<8, 16, true, false, true>, 512);
     else go(skinny_kernel<8, 16, false, false, true>, 512);
   }
-  if (p.splits > 1 && p.mrows == 16) {
+  if (p.splits > 1 && !(p.mrows == 4 && p.atomic)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((skinny_reduce_kernel<false, true>), dim3(p.n_tiles * 4), dim3(256), 0, stream, partial,
