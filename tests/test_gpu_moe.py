@@ -137,6 +137,8 @@ SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batch
     (33, 8, 1, 4096, 1056, 32),
     (4, 32, 2, 2048, 2048, 64),    # 3-4 tokens over many column tiles: 4-row plan, fp32 partials
     (3, 16, 1, 4096, 4096, 128),
+    (8, 32, 2, 2048, 2048, 64),    # 5-8 tokens over many column tiles: 8-row plan
+    (6, 16, 2, 4096, 4096, 128),
 ]
 
 

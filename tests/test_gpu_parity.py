@@ -142,6 +142,8 @@ LAYERS = [  # (M, K, N, g): full-size layers whose grids span several rounds of 
     (1, 28672, 8192, 128),       # 56 K splits
     (4, 8192, 28672, 128),       # four rows on a large layer: 4-row plan, fp32 partials
     (3, 4096, 114688, 128),      # three rows, the same
+    (8, 4096, 114688, 128),      # eight rows on a large layer: 8-row plan, one-group runs
+    (6, 28672, 8192, 128),       # 8-row plan, runs over several groups (LDS tables)
     (16, 4096, 114688, 128),     # 16 rows on 4-wave workgroups, fp32 partials
     (16, 28672, 8192, 128),      # the same, wave runs over several groups (LDS tables)
     (12, 4096, 11008, 128),      # 16-row plan on 8-wave workgroups

@@ -100,13 +100,16 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   // packed weights) take 4-row plans with partials: their smaller LDS reduction
   // buffer lets more workgroups share a compute unit (4096 x 114688: 69.5 -> 62.8
   // us; 8192 x 28672: 37.3 -> 33.3 us; routed experts at 3-4 tokens 6-10%); on
-  // smaller layers they measured 0-3% slower than the 16-row plans.  16-row plans
+  // smaller layers they measured 0-3% slower than the 16-row plans.  Five to eight
+  // rows on those layers take 8-row plans for the same reason (32 KB of LDS
+  // reduction buffer instead of 64 KB; 4096 x 114688 M = 8: 73.8 -> 68.2 us;
+  // 8192 x 28672 M = 6: 38.6 -> 35.6 us).  16-row plans
   // take 8 waves, or 4 waves (two per CU, shorter workgroups overlapping each
   // other's fixed phases) on those large layers: measured 8-15% faster on
   // 8192 x 28672, 28672 x 8192 and 4096 x 114688, 10-25% slower on layers of up
   // to 22 MB.
   const bool large = T * s.n_tiles > (int64_t)8 * cus * 4;
-  s.mrows = (M <= 2 || (M <= 4 && large)) ? 4 : 16;
+  s.mrows = (M <= 2 || (M <= 4 && large)) ? 4 : ((M <= 8 && large) ? 8 : 16);
   s.atomic = M <= 2;
   s.waves = (s.mrows == 4 || large) ? 4 : 8;
   const int64_t W = s.waves;
@@ -151,13 +154,13 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
       L = l2;
     }
   }
-  // 16-row plans whose waves span several groups: take one-group runs of at most 4
+  // 8- and 16-row plans whose waves span several groups: take one-group runs of at most 4
   // k-steps instead when that lowers (rounds of resident workgroups) x (k-steps
   // per wave + 2); the 2 stands for a workgroup's fixed cost (group data, the
   // reduction, the partial stores).  The round count decides it: 5.25 rounds of
   // 7-step waves lose to 7 full rounds of 4-step waves (4096 x 114688), while
   // 1 or 2 full rounds beat 2 or 3.5 (11008 x 4096, 28672 x 8192); measured.
-  if (s.mrows == 16 && !s.single_group) {
+  if (s.mrows >= 8 && !s.single_group) {
     int64_t l1 = gsteps < 4 ? gsteps : 4;
     while (gsteps % l1 != 0) --l1;
     auto cost = [&](int64_t l) { return (s.n_tiles * splits_of(l) + cap - 1) / cap * (l + 2); };

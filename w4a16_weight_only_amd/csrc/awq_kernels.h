@@ -22,7 +22,7 @@ struct SkinnyPlan {
   int splits;        // K splits across workgroups (grid y)
   int L;             // k-steps per wave
   int waves;         // 4 or 8 waves per workgroup (8 only for 16-row plans)
-  int mrows;         // rows kept per tile: 4 or 16
+  int mrows;         // rows kept per tile: 4, 8 or 16 (8 only on 4 waves)
   bool single_group; // every wave's k-steps lie in one quantization group
   bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
 };

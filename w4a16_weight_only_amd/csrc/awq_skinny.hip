@@ -10,8 +10,8 @@
 // WAVES*L 32-row k-steps; wave w takes L consecutive k-steps of that run.  The host
 // picks L and the number of K splits S (about one resident round of workgroups on
 // small layers, shorter one-group runs on large ones) and the plan's rows: 4-row
-// plans (one or two rows of x; three or four on large layers) or 16-row plans (up
-// to 16).
+// plans (one or two rows of x; three or four on large layers), 8-row plans (five to
+// eight on large layers) or 16-row plans (up to 16).
 // At a few microseconds per call the kernel is latency-bound, so every input is
 // requested up front: each wave issues the weight loads of its first two k-steps,
 // and the workgroup turns the zero words and scales of every group it touches into
@@ -142,9 +142,9 @@ __device__ __forceinline__ void kstep_mfma(const Step& st, const uint32_t (&zs)[
 // the 16-byte reads of the 16 column lanes over the banks).
 constexpr int kTabStride = 20;
 
-// red: per wave, accumulator and lane; with at most 4 rows only lanes 0..15 (rows
-// 0..3) hold rows that are stored, so RL = 16 lanes are kept, a quarter of the LDS,
-// which lets a third 4-wave workgroup share a compute unit.
+// red: per wave, accumulator and lane; with at most 4 (8) rows only lanes 0..15
+// (0..31) hold rows that are stored, so RL = 16 (32) lanes are kept, which lets a
+// third 4-wave workgroup share a compute unit.
 template <int WAVES, int RL>
 struct SkinnyLds {
   union {
@@ -209,7 +209,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
   constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
   static_assert(!ATOMIC || (MROWS == 4 && !BF16), "fixed-point atomics: 4-row fp16 plans only");
-  __shared__ SkinnyLds<WAVES, (MROWS > 4 ? 64 : 16)> sh;
+  static_assert(MROWS == 4 || MROWS == 8 || MROWS == 16, "4, 8 or 16 rows");
+  __shared__ SkinnyLds<WAVES, 4 * MROWS> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -412,9 +413,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
   }
 
-  // 2. Waves -> LDS in register order, then sums over waves per slot.  With at most
-  // 4 rows only the q = 0 lanes (rows 0..3) hold rows that are ever stored.
-  if (MROWS > 4 || q == 0) {
+  // 2. Waves -> LDS in register order, then sums over waves per slot.  Only the
+  // lanes q < MROWS / 4 (rows 0 .. MROWS - 1) hold rows that are ever stored.
+  if (q < MROWS / 4) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) sh.u.red[wave][v][lane] = SINGLE ? part[v] : acc[v];
   }
@@ -577,6 +578,9 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
   } else if (p.mrows == 4) {
     if (p.single_group) go(skinny_kernel<4, 4, true, BF16, false, false>, 256);
     else go(skinny_kernel<4, 4, false, BF16, false, false>, 256);
+  } else if (p.mrows == 8) {
+    if (p.single_group) go(skinny_kernel<4, 8, true, BF16>, 256);
+    else go(skinny_kernel<4, 8, false, BF16>, 256);
   } else if (p.waves == 4) {
     if (p.single_group) go(skinny_kernel<4, 16, true, BF16>, 256);
     else go(skinny_kernel<4, 16, false, BF16>, 256);
@@ -611,6 +615,9 @@ hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, cons
   } else if (p.mrows == 4) {
     if (p.single_group) go(skinny_kernel<4, 4, true, false, true, false>, 256);
     else go(skinny_kernel<4, 4, false, false, true, false>, 256);
+  } else if (p.mrows == 8) {
+    if (p.single_group) go(skinny_kernel<4, 8, true, false, true>, 256);
+    else go(skinny_kernel<4, 8, false, false, true>, 256);
   } else if (p.waves == 4) {
     if (p.single_group) go(skinny_kernel<4, 16, true, false, true>, 256);
     else go(skinny_kernel<4, 16, false, false, true>, 256);
