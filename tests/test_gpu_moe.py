@@ -139,6 +139,7 @@ SKINNY_CASES = [  # (T, E, topk, K, N, g): up to 16 tokens take the expert-batch
     (3, 16, 1, 4096, 4096, 128),
     (8, 32, 2, 2048, 2048, 64),    # 5-8 tokens over many column tiles: 8-row plan
     (6, 16, 2, 4096, 4096, 128),
+    (12, 16, 4, 2048, 4096, 64),
 ]
 
 
