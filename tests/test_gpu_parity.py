@@ -104,6 +104,7 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (300, 96, 256, 32, True),    # tile family, last k-tile partial (loaded 32 rows early)
     (20, 32, 96, 32, True),      # 32 x 128 tiles: K = 32
     (30, 96, 256, 32, True),     # 32 x 128 tiles: last k-tile partial
+    (160, 1024, 512, 128, True),  # 129-192 rows on a short K: three 64 x 128 row tiles, split over K
     (24, 4128, 96, 32, True),    # 32 x 128 tiles split over K, last split ends in a half k-tile
 ]
 

@@ -190,7 +190,13 @@ TileLaunch plan_tile(int64_t M, int64_t K, int64_t N, int cus) {
   // measured best over 1 to 4 per unit on 4096- to 28672-wide layers).  Every
   // split keeps at least 8 k-tiles.
   const int64_t fill = (int64_t)cus * 3 / 4;
-  const int v = M > 128 ? 0 : (M > 32 ? 1 : 2);
+  int v = M > 128 ? 0 : (M > 32 ? 1 : 2);
+  // 129-192 rows with K <= 4096, where the 256-row tiles would be split over K: up to
+  // three 64 x 128 row tiles instead (M = 130 on 4096 x 4096: 28.7 -> 21.8 us; M = 176
+  // on 4096 x 11008: 61.1 -> 57.6 us).  With longer K (each weight dequantised by up
+  // to three workgroups: M = 144 on 8192 x 8192 52.5 -> 69.6 us) or an unsplit grid
+  // (M = 192 on 4096 x 28672: 83.8 -> 115.6 us) the 256-row tiles stay.
+  if (v == 0 && M <= 192 && K <= 4096 && tiles(0) < fill) v = 1;
   const int64_t KT = (K + awq::kTileBK - 1) / awq::kTileBK;
   int64_t splits = 1;
   if (v == 0) {
