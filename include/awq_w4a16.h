@@ -125,23 +125,42 @@ int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* s
  *   bias_f16    device fp16 [N], or NULL for no bias
  *   y_f16       device fp16 [M, N], written in full
  * M == 0 returns AWQ_OK and enqueues nothing (GPTQModel wiki, "Native GEMM": empty
- * input launches no kernel).  Two kernel families are chosen by M: a
- * bandwidth-bound skinny family for small M and an MFMA tile family above it
- * (awq_gemm_plan reports the choice).  In the tile family a partly filled last
- * 256-row tile that would take one more round of the compute units runs as a
- * second launch of its own (awq_gemm_plan_tail).  The result is deterministic: the
- * same inputs give the same bits on every call.
- * Workspace: the skinny family splits K across workgroups and reduces the partial
- * sums in a fixed order through a library-owned device buffer, one per
- * (device, stream).  The first call on a (device, stream) that needs a larger
- * buffer allocates it (and synchronises that stream); later calls allocate
- * nothing, so run one eager call before capturing a stream into a graph.
+ * input launches no kernel).  Kernel families are chosen by M: bandwidth-bound
+ * streaming kernels for small M (the decode family for 1 <= M <= 16, the older skinny
+ * family where the decode family's limits do not fit) and an MFMA tile family above
+ * (awq_gemm_plan reports the choice).  In the tile family a partly filled last 256-row
+ * tile that would take one more round of the compute units runs as a second launch
+ * of its own (awq_gemm_plan_tail).  The result is deterministic: the same inputs give
+ * the same bits on every call.  NaN and infinities in x, scales or bias propagate as
+ * float32 accumulation would propagate them.
+ * Workspace: the small-M families split K across workgroups and combine the partial
+ * sums through a library-owned device buffer, one per (device, stream): integer
+ * fixed-point words (order-independent, hence reproducible) or fp32 partials summed
+ * in a fixed order.  The first call on a (device, stream) that needs a larger buffer
+ * allocates it; later calls allocate nothing, so run one eager call of the largest
+ * shape before capturing a stream into a graph.  A call that would have to grow the
+ * buffer while its stream is being captured fails with AWQ_ERR_UNSUPPORTED.  A
+ * replaced buffer is kept (a graph captured earlier may still replay into it) until
+ * awq_release_workspace().  Calls that share a (device, stream) workspace must not run
+ * concurrently, e.g. two graphs captured on the same stream replayed at once on two
+ * other streams.
  * Returns AWQ_OK or an error status.
  */
 int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
              const void* scales_f16, const void* bias_f16,
              int64_t M, int64_t K, int64_t N, int64_t group_size,
              void* y_f16, struct ihipStream_t* stream);
+
+/*
+ * Frees every workspace buffer the library holds, on every device: the current
+ * per-(device, stream) buffers and those replaced by larger ones.  It synchronises each
+ * device first.  The caller guarantees that no graph captured from a library call will
+ * be replayed afterwards (its workspace address would dangle); later calls allocate
+ * afresh.  Not safe to call concurrently with other library calls.
+ * Returns AWQ_OK, or AWQ_ERR_HIP if the runtime reported an error (the buffers that
+ * could be freed are freed either way).
+ */
+int awq_release_workspace(void);
 
 /*
  * awq_gemm with bfloat16 activations: x, bias and y are bfloat16 (raw 16-bit

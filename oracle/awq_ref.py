@@ -118,20 +118,22 @@ def pack_awq(codes: np.ndarray) -> np.ndarray:
 
 
 def unpack_awq(words: np.ndarray) -> np.ndarray:
-    """Unpack int32 words [R, C] into codes [R, 8C], following [AWQ-SPEC]'s reader.
+    """Unpack int32 words [R, C] into codes [R, 8C].
 
-    For each word column c and nibble i: column c*8 + ORDER[i] receives
-    (word >> 4i) & 0xF.  The shift is done on the unsigned view so that a
-    negative word yields the same nibbles as its bit pattern says.
+    [AWQ-SPEC] Reader / [GPTQM] "Saved formats and packing": a word holds eight 4-bit
+    codes, nibble i in bits 4i..4i+3, and nibble i is the code of column ORDER[i] of
+    the word's eight columns.  So split every word into its nibble vector (taken
+    from the unsigned bit pattern, so negative words read as their bits say) and
+    place that vector's entries at positions ORDER along the column axis.
     """
-    u = np.asarray(words).view(np.uint32) if np.asarray(words).dtype == np.int32 \
-        else np.asarray(words, dtype=np.int64).astype(np.uint32)
+    w = np.asarray(words)
+    u = w.view(np.uint32) if w.dtype == np.int32 else w.astype(np.int64).astype(np.uint32)
     R, C = u.shape
-    out = np.empty((R, 8 * C), dtype=np.int32)
-    for col in range(C):
-        for i in range(8):
-            out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int32)
-    return out
+    shifts = np.uint32(4) * np.arange(8, dtype=np.uint32)
+    nibbles = (u[:, :, None] >> shifts[None, None, :]) & np.uint32(0xF)  # [R, C, nibble]
+    cols = np.empty((R, C, 8), dtype=np.int32)
+    cols[:, :, list(AWQ_ORDER)] = nibbles  # column ORDER[i] of each word <- nibble i
+    return cols.reshape(R, 8 * C)
 
 
 def unpack_awq_gather(words: np.ndarray) -> np.ndarray:
@@ -168,24 +170,22 @@ def dequant_ref(qweight, qzeros, scales, group_size) -> np.ndarray:
     s = np.asarray(scales)
     if z.shape != (G, N) or s.shape != (G, N):
         raise AwqFormatError("qzeros/scales shapes do not match K, N, group_size")
-    out = np.empty((K, N), dtype=np.float32)
-    for k in range(K):
-        gi = k // g
-        out[k, :] = (q[k].astype(np.float32) - z[gi].astype(np.float32)) * s[gi].astype(np.float32)
-    return out
+    grp = np.arange(K) // g  # the group row of every input row
+    return (q.astype(np.float32) - z[grp].astype(np.float32)) * s[grp].astype(np.float32)
 
 
 def dequant_ref_T(qweight, qzeros, scales, group_size) -> np.ndarray:
-    """The reader of [AWQ-SPEC] verbatim in orientation: returns [N, K] (out_features first)."""
+    """The same weight in [AWQ-SPEC]'s orientation [N, K] (out_features first), built one
+    quantization group at a time: the g rows of group i share zero row i and scale row i."""
     q = unpack_awq(qweight)
     K, N = q.shape
-    g, _ = resolve_groups(K, group_size)
+    g, G = resolve_groups(K, group_size)
     z = unpack_awq(qzeros)
     s = np.asarray(scales)
     out = np.empty((N, K), dtype=np.float32)
-    for k in range(K):
-        gi = k // g
-        out[:, k] = (q[k].astype(np.float32) - z[gi].astype(np.float32)) * s[gi].astype(np.float32)
+    for i in range(G):
+        block = (q[i * g:(i + 1) * g].astype(np.float32) - z[i].astype(np.float32)) * s[i].astype(np.float32)
+        out[:, i * g:(i + 1) * g] = block.T
     return out
 
 
@@ -205,6 +205,35 @@ def gemm_ref(x, qweight, qzeros, scales, bias, group_size) -> np.ndarray:
     y = x.astype(np.float64) @ W
     if bias is not None:
         y = y + np.asarray(bias).astype(np.float64)[None, :]
+    return y
+
+
+def gemm_ref_ieee(x, qweight, qzeros, scales, bias, group_size) -> np.ndarray:
+    """gemm_ref for inputs that may hold NaN or infinities (in x, scales or bias).
+
+    The value is still the exact sum of the products x[m, k] * W[k, n] plus bias; for
+    non-finite terms IEEE-754 fixes it: a product with a NaN factor, or an infinity
+    times zero, is NaN; an infinite term makes the sum that infinity, and infinities
+    of both signs (or a NaN term) make it NaN.  A float64 matmul library does not
+    promise these rules, so here only the products of two finite factors go through
+    the matmul; every product with a non-finite factor is formed elementwise and added
+    afterwards (IEEE addition then applies the rules above).
+    """
+    x = np.asarray(x).astype(np.float64)
+    W = dequant_ref(qweight, qzeros, scales, group_size).astype(np.float64)
+    if x.ndim != 2 or x.shape[1] != W.shape[0]:
+        raise AwqFormatError(f"x shape {x.shape} does not match K={W.shape[0]}")
+    fin_x = np.isfinite(x)
+    fin_w = np.isfinite(W)
+    y = np.where(fin_x, x, 0.0) @ np.where(fin_w, W, 0.0)
+    with np.errstate(invalid="ignore"):
+        for m, k in zip(*np.nonzero(~fin_x)):  # non-finite x: its whole weight row
+            y[m, :] = y[m, :] + x[m, k] * W[k, :]
+        for k, n in zip(*np.nonzero(~fin_w)):  # non-finite weight, finite x rows only
+            rows = fin_x[:, k]
+            y[rows, n] = y[rows, n] + x[rows, k] * W[k, n]
+        if bias is not None:
+            y = y + np.asarray(bias).astype(np.float64)[None, :]
     return y
 
 

@@ -178,6 +178,66 @@ def pin_brute_force_gemm(o):
                 assert Fraction(float(W[k, n])) == e, (t, k, n)
 
 
+def _ieee_brute_force(x, codes, zeros, scales, bias, g):
+    """y by Python float (IEEE binary64) arithmetic, one product and one add at a time:
+    the reference semantics of non-finite values, independent of any array library."""
+    M, K = x.shape
+    N = codes.shape[1]
+    y = np.empty((M, N), dtype=np.float64)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                w = float(int(codes[k, n]) - int(zeros[k // g, n])) * float(scales[k // g, n])
+                acc = acc + float(x[m, k]) * w
+            if bias is not None:
+                acc = acc + float(bias[n])
+            y[m, n] = acc
+    return y
+
+
+def pin_gemm_ieee(o):
+    """gemm_ref_ieee against an elementwise IEEE-754 triple loop on tiny layers that hold
+    NaN, +inf and -inf in x (some of them against zero weights, inf * 0 = NaN), an
+    infinite scale and a NaN bias entry; on finite inputs it equals gemm_ref."""
+    M, K, N, g = 4, 16, 16, 8
+    rng = _rng(31)
+    codes = rng.integers(0, 16, size=(K, N)).astype(np.int32)
+    zeros = rng.integers(0, 16, size=(K // g, N)).astype(np.int32)
+    codes[3, :4] = zeros[0, :4]  # zero weights in row 3, columns 0..3
+    scales = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    bias = rng.normal(0, 0.5, size=N).astype(np.float16)
+    qw, qz = o.pack_awq(codes), o.pack_awq(zeros)
+    fin = o.gemm_ref_ieee(x, qw, qz, scales, bias, g)
+    assert np.allclose(fin, o.gemm_ref(x, qw, qz, scales, bias, g), rtol=1e-12, atol=1e-12)
+    x[0, 3] = np.inf          # row 0: +inf against row 3 (zero weights in columns 0..3)
+    x[1, 5] = np.nan          # row 1: NaN everywhere
+    x[2, 2] = np.inf          # row 2: +inf and -inf
+    x[2, 12] = -np.inf
+    # column 9 of rows 8..15: +inf weights (scale inf, q - z = 7); row 3 multiplies
+    # them by positive x and by +inf at k = 10, so y[3, 9] = +inf exactly
+    zeros[1, 9] = 3
+    codes[8:16, 9] = 10
+    x[3, 8:16] = np.abs(x[3, 8:16]) + np.float16(0.5)
+    x[3, 10] = np.inf
+    qw, qz = o.pack_awq(codes), o.pack_awq(zeros)
+    scales[1, 9] = np.inf
+    bias[14] = np.nan         # column 14: NaN bias
+    y = o.gemm_ref_ieee(x, qw, qz, scales, bias, g)
+    with np.errstate(invalid="ignore", over="ignore"):
+        e = _ieee_brute_force(x, codes, zeros, scales, bias, g)
+    assert np.array_equal(np.isnan(y), np.isnan(e))
+    assert np.array_equal(np.isinf(y), np.isinf(e))
+    assert np.array_equal(np.sign(y[np.isinf(y)]), np.sign(e[np.isinf(e)]))
+    f = np.isfinite(e)
+    assert np.allclose(y[f], e[f], rtol=1e-12, atol=1e-12)
+    # the constructed cases really occur
+    assert np.isnan(y[1]).all() and np.isnan(y[:, 14]).all()
+    assert np.isnan(y[0, :4]).all() and np.isinf(y[0, 4:8]).any()
+    assert np.isnan(y[2]).any() and np.isinf(y).sum() > 4 and y[3, 9] == np.inf
+
+
 def pin_dequant_orientation(o):
     """The page's reader returns [out_features, in_features]; ours is its transpose."""
     rng = _rng(5)
@@ -440,4 +500,4 @@ def pin_rtn_error_bound(o):
 
 ALL_PINS = [pin_moe_align, pin_moe_gemm, pin_bf16_conversion, pin_gemm_bf16_widening, pin_rtn_hand_example, pin_rtn_roundtrip, pin_rtn_error_bound, pin_fp16_rounding, pin_hand_words, pin_permutation_inverse, pin_roundtrip_codes, pin_roundtrip_words,
             pin_two_unpacks_agree, pin_no_plus_one, pin_brute_force_gemm, pin_dequant_orientation,
-            pin_special_cases, pin_entries_agree, pin_format_rules]
+            pin_special_cases, pin_entries_agree, pin_format_rules, pin_gemm_ieee]

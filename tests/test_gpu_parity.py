@@ -337,3 +337,30 @@ def test_dequant_f16_negative_scales():
     W = awq.awq_dequant(t["qweight"], t["qzeros"], t["scales"], 32, dtype=torch.float16).cpu().numpy()
     ref = oracle.fp16_rne(oracle.dequant_ref(d["qweight"], d["qzeros"], d["scales"], 32))
     assert np.array_equal(bits(W), bits(ref))
+
+
+def test_graph_replay_survives_workspace_growth():
+    """A graph captured at a small shape keeps replaying correctly after a larger eager
+    call on the same stream has replaced the stream's workspace: the replaced buffer is
+    retired, not freed, and stays zero between calls."""
+    s = torch.cuda.Stream()
+    small = synth.make_custom(1, 1024, 512, 128, seed=31)
+    big = synth.make_custom(16, 4096, 8192, 128, seed=32)
+    ts, tb = dev(small), dev(big)
+    with torch.cuda.stream(s):
+        eager = awq.awq_gemm(ts["x"], ts["qweight"], ts["qzeros"], ts["scales"], ts["bias"], 128).clone()
+        y = torch.empty_like(eager)
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        awq.awq_gemm(ts["x"], ts["qweight"], ts["qzeros"], ts["scales"], ts["bias"], 128, out=y)
+    assert awq.plan(16, 4096, 8192, 128)["workspace_bytes"] > 4 * awq.plan(1, 1024, 512, 128)["workspace_bytes"]
+    yb_ref = oracle.gemm_ref(big["x"], big["qweight"], big["qzeros"], big["scales"], big["bias"], 128)
+    for rep in range(3):
+        y.zero_()
+        with torch.cuda.stream(s):
+            graph.replay()
+            yb = awq.awq_gemm(tb["x"], tb["qweight"], tb["qzeros"], tb["scales"], tb["bias"], 128)
+        s.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        tol_check(yb.cpu().numpy(), yb_ref, f"grown workspace rep {rep}")

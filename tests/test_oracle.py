@@ -33,16 +33,27 @@ MUTANTS = [
     ("reverse table used as the order",
      "AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)", "AWQ_ORDER = (0, 4, 1, 5, 2, 6, 3, 7)", 0),
     ("zero plus one (AWQ-005 violated)",
-     "- z[gi].astype(np.float32))", "- z[gi].astype(np.float32) - 1)", 0),
+     "- z[grp].astype(np.float32))", "- z[grp].astype(np.float32) - 1)", 0),
     ("group row k % G instead of k // g",
-     "gi = k // g\n        out[k, :]", "gi = k % (K // g)\n        out[k, :]", 0),
+     "grp = np.arange(K) // g", "grp = np.arange(K) % (K // g)", 0),
     ("scale taken from group 0",
-     "* s[gi].astype(np.float32)", "* s[0].astype(np.float32)", 0),
+     "* s[grp].astype(np.float32)", "* s[0].astype(np.float32)", 0),
     ("bias dropped",
      "y = y + np.asarray(bias).astype(np.float64)[None, :]", "y = y", 0),
     ("nibble mask dropped",
-     "out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)) & np.uint32(0xF))",
-     "out[:, col * 8 + AWQ_ORDER[i]] = ((u[:, col] >> np.uint32(4 * i)))", 0),
+     "nibbles = (u[:, :, None] >> shifts[None, None, :]) & np.uint32(0xF)",
+     "nibbles = (u[:, :, None] >> shifts[None, None, :])", 0),
+    ("nibbles placed in sequential columns",
+     "cols[:, :, list(AWQ_ORDER)] = nibbles", "cols[:, :, :] = nibbles", 0),
+    ("group-wise [N, K] reader uses the wrong zero row",
+     "- z[i].astype(np.float32)) * s[i]", "- z[0].astype(np.float32)) * s[i]", 0),
+    ("IEEE reference drops non-finite activations",
+     "            y[m, :] = y[m, :] + x[m, k] * W[k, :]", "            pass", 0),
+    ("IEEE reference drops non-finite weights",
+     "            y[rows, n] = y[rows, n] + x[rows, k] * W[k, n]", "            pass", 0),
+    ("IEEE reference multiplies non-finite weights by zeroed activations",
+     "            rows = fin_x[:, k]\n            y[rows, n] = y[rows, n] + x[rows, k] * W[k, n]",
+     "            y[:, n] = y[:, n] + np.where(fin_x[:, k], x[:, k], 0.0) * W[k, n]", 0),
     ("gather uses the order table instead of its inverse",
      "(4 * AWQ_REVERSE[j % 8])", "(4 * AWQ_ORDER[j % 8])", 0),
     ("entries use the wrong group row",

@@ -26,6 +26,7 @@ SIGNATURES = {
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_validate_pack": (ctypes.c_int, [_i64] * 10),
     "awq_check_limits": (ctypes.c_int, [_i64] * 4),
+    "awq_release_workspace": (ctypes.c_int, []),
     "awq_dequant": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "awq_dequant_f16": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "awq_quantize_rtn": (ctypes.c_int, [_vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp]),

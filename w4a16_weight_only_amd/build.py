@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libawq_w4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 PROBE_PATH = os.path.join(HERE, "libawq_probe.so")
-SOURCES = ["awq_api.hip", "awq_dequant.hip", "awq_moe.hip", "awq_quant.hip", "awq_skinny.hip", "awq_tile.hip"]
+SOURCES = ["awq_api.hip", "awq_decode.hip", "awq_dequant.hip", "awq_moe.hip", "awq_quant.hip", "awq_skinny.hip", "awq_tile.hip"]
 ARCH = "gfx950"
 
 

@@ -1,8 +1,9 @@
 // C ABI of the AWQ W4A16 library: argument checks, launch planning, workspace.
 // The declarations and their contracts are in include/awq_w4a16.h.
-#include <mutex>
 #include <map>
+#include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/awq_w4a16.h"
 #include "awq_kernels.h"
@@ -46,15 +47,16 @@ struct TileLaunch {
 };
 
 struct Plan {
-  int family = 0;  // 0 skinny, 1 tile
+  int family = 0;  // 0 skinny, 1 tile, 2 decode
   awq::SkinnyPlan sk{};
+  awq::DecodePlan dp{};
   awq::TilePlan tp{};
   // Tile family: the launch over rows [0, rows1), and over rows [rows1, M) when
   // rows1 < M (the last, partly filled 256-row tile in a launch of its own).
   int64_t rows1 = 0;
   TileLaunch tile{}, tail{};
   int grid_x = 0, grid_y = 0, block = 0;
-  int64_t accum_bytes = 0;    // zero-maintained fixed-point accumulators (4-wave plans)
+  int64_t accum_bytes = 0;    // zero-maintained fixed-point words + side words
   int64_t partial_bytes = 0;  // scratch fp32 partials (8-wave skinny plans, split tile plans)
   int64_t workspace_bytes() const { return accum_bytes + partial_bytes; }
 };
@@ -75,13 +77,7 @@ int device_cus() {
   return cus;
 }
 
-#ifndef AWQ_SKINNY_MAX_M
-#define AWQ_SKINNY_MAX_M awq::kSkinnyMaxM  // largest M planned on the skinny family
-#endif
-
-#ifndef AWQ_SKINNY_WG_PER_2CU
-#define AWQ_SKINNY_WG_PER_2CU 4  // 4-wave workgroups per two compute units
-#endif
+constexpr int kSkinnyWgPer2Cu = 4;  // 4-wave skinny workgroups counted per two compute units
 
 // Skinny plan for M <= kSkinnyMaxM, or false when no launch shape fits the
 // kernel's limits (at most kSkinnyMaxSplits splits, at most kSkinnyMaxGroups
@@ -117,7 +113,7 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   // fit when every wave stays inside one group; counting three gives more splits,
   // which measured slower at four rows) and one 8-wave workgroup (large LDS
   // reduction buffer).
-  const int64_t cap = s.waves == 4 ? (int64_t)cus * AWQ_SKINNY_WG_PER_2CU / 2 : (int64_t)cus;
+  const int64_t cap = s.waves == 4 ? (int64_t)cus * kSkinnyWgPer2Cu / 2 : (int64_t)cus;
   int64_t L = (T * s.n_tiles + W * cap - 1) / (W * cap);
   const int64_t l_min = (T + W * awq::kSkinnyMaxSplits - 1) / (W * awq::kSkinnyMaxSplits);
   if (L < l_min) L = l_min;
@@ -175,6 +171,46 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, awq::Skinn
   return true;
 }
 
+// Decode plan (fp16, 1 <= M <= 16), or false when the layer is outside its limits: a
+// wave's k-steps must lie in one quantization group, the splits fit the fixed-point
+// format, and qweight stays below 4 GiB (32-bit buffer offsets).  One workgroup per
+// (512-column tile, K split) of waves * ks k-steps.
+bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, awq::DecodePlan& d) {
+  // One or two rows: the returning fixed-point adds (M x N x splits of them) stay cheap.
+  // From three rows they cost more than the older skinny family's fp32 partials (M = 16
+  // on 4096 x 11008: 27.6 us at best against 13.9; M = 8 on 11008 x 4096: 17.2 against
+  // 12.9), which keeps those.
+  if (M < 1 || M > 2) return false;
+  if (K * (N / 2) >= (int64_t(1) << 32) - 4096) return false;
+  const int64_t T = K / awq::kKStep;
+  d.n_tiles = (int)((N / 8 + awq::kDecodeWords - 1) / awq::kDecodeWords);
+  d.mp = (int)M;
+  auto splits_of = [&](int ks, int waves) { return (T + (int64_t)ks * waves - 1) / ((int64_t)ks * waves); };
+  auto ok = [&](int ks, int waves) {
+    return (g == K || g % (awq::kKStep * ks) == 0) && splits_of(ks, waves) <= awq::kFxMaxSplits;
+  };
+  // Up to 128 k-steps (K <= 4096): one k-step per wave, 4 waves (4096 x 4096: 6.2 us
+  // against 6.6-8.2 for the other shapes).  Longer K: two k-steps per wave on 8-wave
+  // workgroups (11008 x 4096: 8.9 us against 9.7-12.8).
+  const int pref_ks = T <= 128 ? 1 : 2, pref_w = T <= 128 ? 4 : 8;
+  const int cand[4][2] = {{pref_ks, pref_w}, {1, 4}, {1, 8}, {2, 8}};
+  d.ks = 0;
+  for (const auto& c : cand)
+    if (ok(c[0], c[1])) {
+      d.ks = c[0];
+      d.waves = c[1];
+      break;
+    }
+  if (d.ks == 0) return false;
+  d.splits = (int)splits_of(d.ks, d.waves);
+  d.late = g == K || g % ((int64_t)awq::kKStep * d.ks * d.waves) == 0;
+  return true;
+}
+
+// Zero-maintained fixed-point workspace of a decode plan: 64-bit words, then float
+// side words, one of each per (tile, column, padded row).
+int64_t decode_entries(const awq::DecodePlan& d) { return (int64_t)d.n_tiles * awq::kDecodeCols * d.mp; }
+
 // One launch of the tile family over M rows.
 TileLaunch plan_tile(int64_t M, int64_t K, int64_t N, int cus) {
   auto tiles = [&](int v) {
@@ -221,7 +257,15 @@ TileLaunch plan_tile(int64_t M, int64_t K, int64_t N, int cus) {
 
 Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = false) {
   Plan p;
-  if (M <= AWQ_SKINNY_MAX_M && plan_skinny(M, K, N, g, cus, p.sk)) {
+  if (!bf16 && plan_decode(M, K, N, g, p.dp)) {
+    p.family = 2;
+    p.grid_x = p.dp.n_tiles;
+    p.grid_y = p.dp.splits;
+    p.block = 64 * p.dp.waves;
+    if (p.dp.splits > 1) p.accum_bytes = decode_entries(p.dp) * 12;
+    return p;
+  }
+  if (M <= awq::kSkinnyMaxM && plan_skinny(M, K, N, g, cus, p.sk)) {
     p.family = 0;
     p.grid_x = p.sk.n_tiles;
     p.grid_y = p.sk.splits;
@@ -229,7 +273,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
     // 4-row fp16 plans: 64-bit fixed-point accumulators per tile entry; 16-row
     // plans and every bfloat16 plan: fp32 partials per (tile, split, entry).
     if (p.sk.splits > 1) {
-      if (p.sk.atomic && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 8;
+      if (p.sk.atomic && !bf16) p.accum_bytes = (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols * 12;
       else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * awq::kSkinnyCols * 4;
     }
   } else {
@@ -263,10 +307,15 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16 = 
 }
 
 // Library-owned split-K workspace, one per (device, stream), in two buffers:
-//   accum    64-bit fixed-point accumulators; zeroed once at allocation and left zero
-//            by every call that uses them, so they must never hold anything else;
+//   accum    fixed-point words and their float side words; zeroed once at allocation
+//            and left zero by every call that uses them, so they never hold anything
+//            else between calls;
 //   partial  fp32 scratch, fully written before it is read in each call.
-// Growing a buffer frees the old one after the stream drains.
+// A buffer that must grow is replaced, and the old one is retired, never freed while
+// the library is loaded (a graph captured earlier may still hold its address and replay
+// into it); awq_release_workspace() frees retired and current buffers on request.  A
+// stream that is being captured cannot grow its workspace: that call fails with
+// AWQ_ERR_UNSUPPORTED before enqueueing anything.
 struct Buffer {
   void* ptr = nullptr;
   int64_t bytes = 0;
@@ -277,23 +326,22 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;  // (device, buffer) replaced by a larger one
 
-int ensure(Buffer& b, int64_t need, bool zero, hipStream_t stream) {
+int ensure(int dev, Buffer& b, int64_t need, bool zero, hipStream_t stream) {
   if (need <= 0 || (b.ptr && need <= b.bytes)) return AWQ_OK;
-  if (b.ptr) {
-    // Work already queued on this stream may still use the old buffer.
-    if (hipStreamSynchronize(stream) != hipSuccess) return AWQ_ERR_HIP;
-    if (hipFree(b.ptr) != hipSuccess) return AWQ_ERR_HIP;
-    b.ptr = nullptr;
-    b.bytes = 0;
-  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return AWQ_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) return AWQ_ERR_UNSUPPORTED;
   const int64_t bytes = need + need / 4;  // headroom against frequent regrowth
   void* ptr = nullptr;
   if (hipMalloc(&ptr, (size_t)bytes) != hipSuccess) return AWQ_ERR_HIP;
-  if (zero && hipMemset(ptr, 0, (size_t)bytes) != hipSuccess) {
+  // Zeroed in stream order, before any kernel of this stream can use the buffer.
+  if (zero && hipMemsetAsync(ptr, 0, (size_t)bytes, stream) != hipSuccess) {
     (void)hipFree(ptr);
     return AWQ_ERR_HIP;
   }
+  if (b.ptr) g_retired.emplace_back(dev, b.ptr);
   b.ptr = ptr;
   b.bytes = bytes;
   return AWQ_OK;
@@ -304,9 +352,9 @@ int get_workspace(const Plan& p, hipStream_t stream, uint64_t** accum, float** p
   if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& ws = g_ws[{dev, stream}];
-  int st = ensure(ws.accum, p.accum_bytes, true, stream);
+  int st = ensure(dev, ws.accum, p.accum_bytes, true, stream);
   if (st != AWQ_OK) return st;
-  st = ensure(ws.partial, p.partial_bytes, false, stream);
+  st = ensure(dev, ws.partial, p.partial_bytes, false, stream);
   if (st != AWQ_OK) return st;
   *accum = reinterpret_cast<uint64_t*>(ws.accum.ptr);
   *partial = reinterpret_cast<float*>(ws.partial.ptr);
@@ -320,7 +368,7 @@ int get_scratch(int64_t bytes, hipStream_t stream, void** out) {
   if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& ws = g_ws[{dev, stream}];
-  const int st = ensure(ws.partial, bytes, false, stream);
+  const int st = ensure(dev, ws.partial, bytes, false, stream);
   if (st != AWQ_OK) return st;
   *out = ws.partial.ptr;
   return AWQ_OK;
@@ -357,6 +405,26 @@ int awq_validate_pack(int64_t K, int64_t N, int64_t group_size, int64_t qweight_
   return AWQ_OK;
 }
 
+int awq_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return AWQ_ERR_HIP;
+  int st = AWQ_OK;
+  auto release = [&](int dev, void* ptr) {
+    if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(ptr) != hipSuccess)
+      st = AWQ_ERR_HIP;
+  };
+  for (auto& r : g_retired) release(r.first, r.second);
+  g_retired.clear();
+  for (auto& w : g_ws) {
+    if (w.second.accum.ptr) release(w.first.first, w.second.accum.ptr);
+    if (w.second.partial.ptr) release(w.first.first, w.second.partial.ptr);
+  }
+  g_ws.clear();
+  if (hipSetDevice(cur) != hipSuccess) st = AWQ_ERR_HIP;
+  return st;
+}
+
 int awq_check_limits(int64_t M, int64_t K, int64_t N, int64_t group_size) {
   return limits_check(M, K, N, group_size);
 }
@@ -372,7 +440,7 @@ int awq_gemm_plan(int64_t M, int64_t K, int64_t N, int64_t group_size, int* fami
   else (void)hipGetLastError();
   const Plan p = make_plan(M, K, N, eff_group(K, group_size), cus);
   if (family) *family = p.family;
-  if (splits) *splits = p.family == 0 ? p.sk.splits : p.tp.splits;
+  if (splits) *splits = p.family == 2 ? p.dp.splits : (p.family == 0 ? p.sk.splits : p.tp.splits);
   if (grid_x) *grid_x = p.grid_x;
   if (grid_y) *grid_y = p.grid_y;
   if (block) *block = p.block;
@@ -462,13 +530,25 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
   const auto* b = static_cast<const uint16_t*>(bias_f16);
   auto* y = static_cast<uint16_t*>(y_f16);
   hipError_t e;
-  if (p.family == 0) {
+  if (p.family == 2) {
+    uint64_t* accum = nullptr;
+    float* partial = nullptr;
+    if (p.dp.splits > 1) {
+      const int ws = get_workspace(p, stream, &accum, &partial);
+      if (ws != AWQ_OK) return ws;
+    }
+    float* side = accum ? reinterpret_cast<float*>(accum + decode_entries(p.dp)) : nullptr;
+    e = awq::launch_decode(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.dp, accum, side, y, stream);
+  } else if (p.family == 0) {
     uint64_t* accum = nullptr;
     float* partial = nullptr;
     if (p.sk.splits > 1) {
       const int ws = get_workspace(p, stream, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
+    // Fixed-point plans: the float side words follow the accumulator words.
+    if (p.sk.splits > 1 && p.sk.atomic && !bf16)
+      partial = reinterpret_cast<float*>(accum + (int64_t)p.sk.n_tiles * p.sk.mrows * awq::kSkinnyCols);
     e = awq::launch_skinny(x, qweight, qzeros, sc, b, (int)M, (int)K, (int)N, g, p.sk, bf16, accum, partial, y,
                            stream);
   } else {
@@ -538,7 +618,7 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
                   device_cus(), sk)) {
     Plan p;
     if (sk.splits > 1) {
-      if (sk.atomic) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 8;
+      if (sk.atomic) p.accum_bytes = (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols * 12;
       else p.partial_bytes = (int64_t)sk.n_tiles * sk.splits * sk.mrows * awq::kSkinnyCols * 4;
     }
     uint64_t* accum = nullptr;
@@ -546,6 +626,7 @@ int awq_moe_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzero
     if (sk.splits > 1) {
       st = get_workspace(p, stream, &accum, &partial);
       if (st != AWQ_OK) return st;
+      if (sk.atomic) partial = reinterpret_cast<float*>(accum + (int64_t)sk.n_tiles * sk.mrows * awq::kSkinnyCols);
     }
     const awq::SkinnyExperts ex{expert_ids, (int)topk, (int)tiles_e, (int)chunks, (int)E, K * (N / 8), G * (N / 8),
                                 G * N};

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "awq_kernels.h"
+
 namespace awq {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -126,6 +128,71 @@ __device__ __forceinline__ uint32_t zero_code(uint32_t zw, int j) {
 }
 
 __device__ __forceinline__ half2v splat(_Float16 v) { return half2v{v, v}; }
+
+// ---- Split-K sums in 64-bit fixed point, one word per output element.
+// Each of the `splits` workgroups that share an output element adds its fp32 partial p
+// with one returning atomic; the word is zero between calls (the workgroup that
+// completes it writes the output and clears it).  Layout of the word:
+//   bits 63..57  arrivals: workgroups that have added their partial (<= 127)
+//   bits 56..50  exceptional arrivals: partials that are NaN, +-inf or |p| >= 2^18
+//   bits 49..0   signed sum of rint(p * 2^24) over the other partials
+// Integer addition does not depend on order, so the sum is reproducible bit for bit;
+// every fp16 value is a multiple of 2^-24, so a sum of exact products stays exact.
+// An exceptional partial cannot be held in fixed point: it is added in fp32 to a float
+// side word of the same element (zero between calls) before its arrival is counted,
+// and the workgroup that completes the element adds that side word back.  The side
+// add is released before the arrival (agent-scope fence) and the completing workgroup
+// acquires before it reads, so it sees every side add: NaN, infinities and huge
+// partials reach the output as an fp32 sum would produce them.  Normal partials are
+// below 2^18 in magnitude, 2^42 in fixed point, so kFxMaxSplits = 127 of them stay
+// below 2^49.
+constexpr float kFxScale = 16777216.0f;  // 2^24
+constexpr float kFxLimit = 262144.0f;    // 2^18
+
+// False for NaN, +-inf and partials of magnitude >= 2^18.
+__device__ __forceinline__ bool fx_normal(float p) { return __builtin_fabsf(p) < kFxLimit; }
+
+// The word a workgroup adds for its partial p.
+__device__ __forceinline__ uint64_t fx_word(float p) {
+  const uint64_t arrival = 1ull << 57;
+  if (fx_normal(p)) return arrival + (uint64_t)(int64_t)__builtin_rintf(p * kFxScale);
+  return arrival + (1ull << 50);
+}
+
+struct FxSum {
+  int64_t value;  // sum of the normal partials, in units of 2^-24
+  uint32_t marks;  // exceptional partials (their fp32 sum is in the side word)
+  uint32_t arrivals;
+};
+// Splits the word returned by an add (old value + the word added).
+__device__ __forceinline__ FxSum fx_decode(uint64_t w) {
+  const int64_t value = (int64_t)(w << 14) >> 14;  // low 50 bits, sign-extended
+  const uint64_t rest = (w - (uint64_t)value) >> 50;  // arrivals * 128 + marks, exact
+  return FxSum{value, (uint32_t)(rest & 127u), (uint32_t)(rest >> 7)};
+}
+
+// Side add of an exceptional partial (before its word is added).  After all side adds
+// of the calling wave, fx_release() must precede the word adds.
+__device__ __forceinline__ void fx_side_add(float* side, float p) {
+  __hip_atomic_fetch_add(side, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fx_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ uint64_t fx_add(uint64_t* word, uint64_t add) {
+  return __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+}
+// The completed element's fp32 sum (for the workgroup whose add brought the arrivals to
+// `splits`); clears the side word.  The caller clears the 64-bit word.
+__device__ __forceinline__ float fx_total(const FxSum& s, float* side) {
+  float v = (float)s.value * (1.0f / kFxScale);
+  if (s.marks != 0) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    v += __hip_atomic_exchange(side, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return v;
+}
+__device__ __forceinline__ void fx_clear(uint64_t* word) {
+  __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Sum over s < splits of the 4 floats at p + s * stride, added in split order (the
 // same order, so the same bits, for every call).  The loads go out 8 splits at a

@@ -14,7 +14,8 @@ constexpr int kSkinnyCols = 8 * kSkinnyWordCols;
 constexpr int kKStep = 32;
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxGroups = 16;  // quantization groups one workgroup may touch
-constexpr int kSkinnyMaxSplits = 128;  // fixed-point accumulators hold up to 128 arrivals
+constexpr int kFxMaxSplits = 127;     // arrivals a fixed-point split-K word can count
+constexpr int kSkinnyMaxSplits = kFxMaxSplits;
 
 // Launch plan of the skinny family (chosen on the host, see awq_api.hip).
 struct SkinnyPlan {
@@ -26,6 +27,26 @@ struct SkinnyPlan {
   bool single_group; // every wave's k-steps lie in one quantization group
   bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
 };
+
+// Decode family (fp16 activations, 1 <= M <= 16): a workgroup of `waves` waves owns a
+// column tile of 64 packed word-columns (512 output columns, 256 contiguous bytes of a
+// row) and waves * ks k-steps of 32 rows, all of one wave's ks k-steps in one
+// quantization group.  The K splits meet in fixed-point accumulators: n_tiles * 512 * mp
+// 64-bit words, then as many float side words, zero before the call and left zero by it.
+constexpr int kDecodeWords = 64;
+constexpr int kDecodeCols = 8 * kDecodeWords;
+constexpr int kDecodeMaxM = 16;
+struct DecodePlan {
+  int n_tiles;  // column tiles of kDecodeCols
+  int splits;   // K splits (grid y), at most kFxMaxSplits
+  int ks;       // k-steps per wave: 1 or 2
+  int waves;    // waves per workgroup: 4 or 8
+  int mp;       // rows padded to 1, 2, 4, 8 or 16
+  bool late;    // the workgroup's rows lie in one group: scale after the wave reduction
+};
+hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                         const uint16_t* bias, int M, int K, int N, int g, const DecodePlan& p, uint64_t* accum,
+                         float* side, uint16_t* y, hipStream_t stream);
 
 // MFMA tile family.  Variants (rows x columns per workgroup, threads):
 // 0: 256 x 128 (512: two k-groups of 4 waves), 1: 64 x 128 (256), 2: 32 x 128 (256).

@@ -470,10 +470,31 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     return;
   }
 
-  // 3. Fixed-point accumulation across splits; the last arrival finishes the element.
+  // 3. Fixed-point accumulation across splits (awq_device.h); the add that completes an
+  // element finishes it.  For these plans `partial` holds the float side words, one per
+  // accumulator word.  Adds outside the layer (rows >= M, columns >= N) add 0 to their own
+  // slot, which never completes.
   uint64_t* tile_acc = accum + (int64_t)blockIdx.x * TILE_ENTRIES;
-  constexpr float kClamp = 8388608.0f;  // 2^23
-  constexpr float kToFixed = 16777216.0f;  // 2^24
+  float* tile_side = partial + (int64_t)blockIdx.x * TILE_ENTRIES;
+  bool exc = false;
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int s = tid + k * THREADS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      exc |= s < nslots && slot_n(s) < N && 4 * (s >> 8) + i < rows && !fx_normal(sum[k][i]);
+  }
+  if (__builtin_amdgcn_ballot_w64(exc) != 0) {  // rare: NaN, +-inf or huge partials
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int s = tid + k * THREADS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s < nslots && slot_n(s) < N && 4 * (s >> 8) + i < rows && !fx_normal(sum[k][i]))
+          fx_side_add(tile_side + 4 * s + i, sum[k][i]);
+    }
+    fx_release();
+  }
 #pragma unroll
   for (int k = 0; k < SLOTS; ++k) {
     const int s = tid + k * THREADS;
@@ -482,26 +503,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     uint64_t ret[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ret[i] = 0;
-      if (4 * (s >> 8) + i < rows) {
-        const float v = fminf(fmaxf(sum[k][i], -kClamp), kClamp);
-        const int64_t fx = (int64_t)rintf(v * kToFixed);
-        const uint64_t add = (1ull << 56) + (uint64_t)fx;
-        ret[i] = __hip_atomic_fetch_add(tile_acc + 4 * s + i, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
-      }
+      const bool live = n < N && 4 * (s >> 8) + i < rows;
+      ret[i] = fx_add(tile_acc + 4 * s + i, live ? fx_word(sum[k][i]) : 0ull);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * (s >> 8) + i;
-      if (row >= rows) continue;
-      const int64_t value = (int64_t)(ret[i] << 8) >> 8;  // low 56 bits, signed
-      const uint64_t count = (ret[i] - (uint64_t)value) >> 56;
-      if (count == (uint64_t)splits) {
-        __hip_atomic_store(tile_acc + 4 * s + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (n < N) {
-          const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
-          put(row, n, (float)value * (1.0f / kToFixed) + b);
-        }
+      const FxSum fs = fx_decode(ret[i]);
+      if (n < N && row < rows && fs.arrivals == (uint32_t)splits) {
+        const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
+        const float v = fx_total(fs, tile_side + 4 * s + i) + b;
+        fx_clear(tile_acc + 4 * s + i);
+        put(row, n, v);
       }
     }
   }

@@ -44,10 +44,7 @@ namespace awq {
 namespace {
 
 constexpr int kBK = 64;            // k-tile of the x staging
-#ifndef TILE_STAGES
-#define TILE_STAGES 4
-#endif
-constexpr int kStages = TILE_STAGES;  // LDS buffers of the k loop
+constexpr int kStages = 4;  // LDS buffers of the k loop
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l's data lands at lds + 16 l; lds must be the same for the whole wave.  Issued
@@ -307,9 +304,8 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const _Float16 zbase = hi_nib ? (_Float16)64.f : (_Float16)1024.f;
 
   half2v off0, off1, sc0, sc1;
-  // Group data of half h of k-tile buf.  keep = false zeroes the scales: the half then
-  // contributes x . 0 = 0 (for finite x), which is how the unused half of a partial
-  // last k-tile is skipped without a branch around the multiply.
+  // Group data of half h of k-tile buf.  keep = false zeroes the scales (the unused half
+  // of a partial last k-tile, whose MFMAs are skipped anyway).
   auto apply_group = [&](int buf, int h, bool keep) {
     const uint32_t* gz = reinterpret_cast<const uint32_t*>(&Gs[buf][h * GP]);
     const _Float16* gs = reinterpret_cast<const _Float16*>(&Gs[buf][h * GP + ZP]);
@@ -397,9 +393,12 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // last k-tile holds its 32 rows in the upper half (K >= 64) or the lower one
   // (K = 32); the other half is multiplied with zero scales.
   const int part_half = K >= kBK ? 1 : 0;
+  // The other half of a partial last k-tile is not multiplied at all (a uniform branch):
+  // zero weights would still turn an infinite x there into NaN.
   auto run = [&](int buf, bool part) {
 #pragma unroll
-    for (int kh = (KG == 1 ? 0 : kg); kh < 2; kh += KG) compute(C0{}, C2{}, buf, kh, !part || kh == part_half);
+    for (int kh = (KG == 1 ? 0 : kg); kh < 2; kh += KG)
+      if (!part || kh == part_half) compute(C0{}, C2{}, buf, kh, true);
   };
 
   // kStages LDS buffers.  While k-tile t is multiplied from buffer t % kStages,
@@ -489,11 +488,14 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     read_w(w1lo, w1hi, 0, 1);
     apply_group(0, kh, keep_of(0));
     dequant(w0lo, w0hi, b0);
-    for (int kt = 0; kt < KT; ++kt) {
+    // mul = false only on the last k-tile, for the k-group whose half of a partial last
+    // k-tile holds no new rows: its MFMAs are skipped (zero weights would still turn an
+    // infinite x there into NaN); it still takes part in the barrier.
+    auto body = [&](int kt, bool mul) {
       const int buf = kt % kStages, nbuf = (kt + 1) % kStages;
       load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
       read_a(a1, buf, 1);
-      mfma_step(a0, b0);
+      if (mul) mfma_step(a0, b0);
       dequant(w1lo, w1hi, b1);
       interleave();
       barrier_keep_last();
@@ -501,10 +503,12 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       read_w(w0lo, w0hi, nbuf, 0);
       read_w(w1lo, w1hi, nbuf, 1);
       apply_group(nbuf, kh, keep_of(kt + 1));
-      mfma_step(a1, b1);
+      if (mul) mfma_step(a1, b1);
       dequant(w0lo, w0hi, b0);
       interleave();
-    }
+    };
+    for (int kt = 0; kt < KT - 1; ++kt) body(kt, true);
+    body(KT - 1, keep_of(KT - 1));
   } else {
     for (int kt = 0; kt < KT; ++kt) {
       load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));

@@ -78,7 +78,7 @@ def plan(M: int, K: int, N: int, group_size: int) -> dict:
     tail = None
     if rows.value:
         tail = dict(rows=rows.value, splits=tv[0].value, grid=(tv[1].value, tv[2].value), block=tv[3].value)
-    return dict(family="skinny" if fam == 0 else "tile", splits=splits, grid=(gx, gy), block=block,
+    return dict(family={0: "skinny", 1: "tile", 2: "decode"}[fam], splits=splits, grid=(gx, gy), block=block,
                 workspace_bytes=ws.value, tail=tail)
 
 
