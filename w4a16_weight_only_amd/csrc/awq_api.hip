@@ -180,7 +180,7 @@ bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, awq::DecodePlan& d)
   // From three rows they cost more than the older skinny family's fp32 partials (M = 16
   // on 4096 x 11008: 27.6 us at best against 13.9; M = 8 on 11008 x 4096: 17.2 against
   // 12.9), which keeps those.
-  if (M < 1 || M > 2) return false;
+  if (M < 1 || M > awq::kDecodeMaxM) return false;
   if (K * (N / 2) >= (int64_t(1) << 32) - 4096) return false;
   const int64_t T = K / awq::kKStep;
   d.n_tiles = (int)((N / 8 + awq::kDecodeWords - 1) / awq::kDecodeWords);

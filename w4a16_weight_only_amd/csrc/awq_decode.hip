@@ -1,4 +1,4 @@
-// Decode family of awq_gemm (fp16 activations, 1 <= M <= 16): bandwidth-bound streaming
+// Decode family of awq_gemm (fp16 activations, 1 <= M <= 2): bandwidth-bound streaming
 // of the packed weight.
 //
 // What it computes: y[m, n] = sum_k x[m, k] * (q[k, n] - z[k/g, n]) * s[k/g, n] + bias[n]
@@ -321,13 +321,8 @@ hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_
       else p.late ? go(decode_kernel<MP, 1, 4, true>, 256) : go(decode_kernel<MP, 1, 4, false>, 256);
     }
   };
-  switch (p.mp) {
-    case 1: by_shape(std::integral_constant<int, 1>{}); break;
-    case 2: by_shape(std::integral_constant<int, 2>{}); break;
-    case 4: by_shape(std::integral_constant<int, 4>{}); break;
-    case 8: by_shape(std::integral_constant<int, 8>{}); break;
-    default: by_shape(std::integral_constant<int, 16>{}); break;
-  }
+  if (p.mp == 1) by_shape(std::integral_constant<int, 1>{});
+  else by_shape(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 

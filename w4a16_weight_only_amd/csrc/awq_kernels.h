@@ -28,20 +28,20 @@ struct SkinnyPlan {
   bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
 };
 
-// Decode family (fp16 activations, 1 <= M <= 16): a workgroup of `waves` waves owns a
+// Decode family (fp16 activations, 1 <= M <= 2): a workgroup of `waves` waves owns a
 // column tile of 64 packed word-columns (512 output columns, 256 contiguous bytes of a
 // row) and waves * ks k-steps of 32 rows, all of one wave's ks k-steps in one
 // quantization group.  The K splits meet in fixed-point accumulators: n_tiles * 512 * mp
 // 64-bit words, then as many float side words, zero before the call and left zero by it.
 constexpr int kDecodeWords = 64;
 constexpr int kDecodeCols = 8 * kDecodeWords;
-constexpr int kDecodeMaxM = 16;
+constexpr int kDecodeMaxM = 2;
 struct DecodePlan {
   int n_tiles;  // column tiles of kDecodeCols
   int splits;   // K splits (grid y), at most kFxMaxSplits
   int ks;       // k-steps per wave: 1 or 2
   int waves;    // waves per workgroup: 4 or 8
-  int mp;       // rows padded to 1, 2, 4, 8 or 16
+  int mp;       // rows: 1 or 2
   bool late;    // the workgroup's rows lie in one group: scale after the wave reduction
 };
 hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
