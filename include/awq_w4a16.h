@@ -152,6 +152,25 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
              void* y_f16, struct ihipStream_t* stream);
 
 /*
+ * awq_gemm for callers that cannot allocate device memory (code under HIP graph
+ * capture on a fresh stream, serving loops that must not call hipMalloc, harnesses that
+ * forbid it).  Same arguments, plans, kernels and results as awq_gemm; the split-K
+ * buffers come from one statically sized device array of the library (64 MiB per GPU,
+ * held from the first call on that GPU until the process ends: 2 MiB of zero-maintained
+ * fixed-point words, 62 MiB of fp32 partials), never from hipMalloc.  The first call on
+ * a device clears the word region with a small kernel on `stream`.  A shape whose plan
+ * needs more than either region returns AWQ_ERR_UNSUPPORTED before enqueueing anything
+ * (awq_gemm_plan's workspace_bytes shows the need).  Every call on one GPU shares that
+ * array: calls that overlap in time on one GPU (two streams, or concurrently replayed
+ * graphs) race and must not be issued; consecutive calls in any stream order are fine.
+ * Returns AWQ_OK or an error status.
+ */
+int awq_gemm_noalloc(const void* x_f16, const int32_t* qweight, const int32_t* qzeros,
+                     const void* scales_f16, const void* bias_f16,
+                     int64_t M, int64_t K, int64_t N, int64_t group_size,
+                     void* y_f16, struct ihipStream_t* stream);
+
+/*
  * Frees every workspace buffer the library holds, on every device: the current
  * per-(device, stream) buffers and those replaced by larger ones.  It synchronises each
  * device first.  The caller guarantees that no graph captured from a library call will

@@ -10,6 +10,8 @@
 
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -374,6 +376,56 @@ int get_scratch(int64_t bytes, hipStream_t stream, void** out) {
   return AWQ_OK;
 }
 
+// Allocation-free workspace for awq_gemm_noalloc: one file-scope device array per GPU
+// (each device that runs the library holds its own copy until the process ends).  The
+// first kScratchWordBytes hold fixed-point words and their side words, zero between
+// calls like the workspace above (a fill kernel clears them on the device's first call);
+// the rest holds fp32 partials, fully written before they are read in each call.  The
+// two regions never trade places, so neither kind of plan can break the other's
+// invariant.  In host code `scratch` only names the symbol: kernels get the address
+// hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchWordBytes = int64_t(2) << 20;
+constexpr int64_t kScratchPartialBytes = int64_t(62) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchWordBytes + kScratchPartialBytes];
+
+__global__ void zero_words_kernel(u32x4_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;  // device -> address of `scratch` on that device
+
+int get_static_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return AWQ_ERR_HIP;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<u32x4_t*>(ptr),
+                       kScratchWordBytes / 16);
+    if (hipGetLastError() != hipSuccess) return AWQ_ERR_HIP;
+    it = g_scratch.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return AWQ_OK;
+}
+
+// The split-K buffers of plan p: the stream's grown workspace, or (noalloc) the static
+// scratch, AWQ_ERR_UNSUPPORTED when the plan needs more than it holds.
+int workspace_for(const Plan& p, hipStream_t stream, bool noalloc, uint64_t** accum, float** partial) {
+  if (!noalloc) return get_workspace(p, stream, accum, partial);
+  if (p.accum_bytes > kScratchWordBytes || p.partial_bytes > kScratchPartialBytes) return AWQ_ERR_UNSUPPORTED;
+  void* base = nullptr;
+  const int st = get_static_scratch(stream, &base);
+  if (st != AWQ_OK) return st;
+  *accum = static_cast<uint64_t*>(base);
+  *partial = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + kScratchWordBytes);
+  return AWQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -515,7 +567,7 @@ int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size
 namespace {
 int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
                 const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
-                bool bf16, hipStream_t stream) {
+                bool bf16, hipStream_t stream, bool noalloc = false) {
   const int st = limits_check(M, K, N, group_size);
   if (st != AWQ_OK) return st;
   if (M == 0) return AWQ_OK;
@@ -534,7 +586,7 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
     uint64_t* accum = nullptr;
     float* partial = nullptr;
     if (p.dp.splits > 1) {
-      const int ws = get_workspace(p, stream, &accum, &partial);
+      const int ws = workspace_for(p, stream, noalloc, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
     float* side = accum ? reinterpret_cast<float*>(accum + decode_entries(p.dp)) : nullptr;
@@ -543,7 +595,7 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
     uint64_t* accum = nullptr;
     float* partial = nullptr;
     if (p.sk.splits > 1) {
-      const int ws = get_workspace(p, stream, &accum, &partial);
+      const int ws = workspace_for(p, stream, noalloc, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
     // Fixed-point plans: the float side words follow the accumulator words.
@@ -555,7 +607,7 @@ int gemm_common(const void* x_f16, const int32_t* qweight, const int32_t* qzeros
     uint64_t* accum = nullptr;
     float* partial = nullptr;
     if (p.tp.splits > 1 || p.tail.tp.splits > 1) {
-      const int ws = get_workspace(p, stream, &accum, &partial);
+      const int ws = workspace_for(p, stream, noalloc, &accum, &partial);
       if (ws != AWQ_OK) return ws;
     }
     e = awq::launch_tile(x, qweight, qzeros, sc, b, (int)p.rows1, (int)K, (int)N, g, p.tp, bf16, partial, y,
@@ -663,6 +715,12 @@ int awq_gemm(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, c
              const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
              struct ihipStream_t* stream) {
   return gemm_common(x_f16, qweight, qzeros, scales_f16, bias_f16, M, K, N, group_size, y_f16, false, stream);
+}
+
+int awq_gemm_noalloc(const void* x_f16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
+                     const void* bias_f16, int64_t M, int64_t K, int64_t N, int64_t group_size, void* y_f16,
+                     struct ihipStream_t* stream) {
+  return gemm_common(x_f16, qweight, qzeros, scales_f16, bias_f16, M, K, N, group_size, y_f16, false, stream, true);
 }
 
 int awq_gemm_bf16(const void* x_bf16, const int32_t* qweight, const int32_t* qzeros, const void* scales_f16,
