@@ -77,7 +77,12 @@ int awq_validate_pack(int64_t K, int64_t N, int64_t group_size,
 /*
  * Kernel limits on top of the format rules (AWQ_ERR_UNSUPPORTED otherwise):
  *   K % 32 == 0, N % 32 == 0, group_size == -1 or group_size % 32 == 0,
- *   K, N <= 2^24, M <= 2^24.
+ *   K, N <= 2^24, M <= 2^24,
+ * and every launch of awq_gemm's plan for the shape within the hardware's grid limits
+ * (under 2^32 work-items along x, 2^16 workgroups along y) and the kernels' 32-bit
+ * offsets (256-row tiles, taken above 128 rows, address a tile's x rows with 32-bit
+ * byte offsets: K < 2^23 there).  Plans assume the current device's compute units
+ * (256 when no device is visible).
  * Host-only check; returns AWQ_OK, AWQ_ERR_SHAPE, AWQ_ERR_GROUP or AWQ_ERR_UNSUPPORTED.
  */
 int awq_check_limits(int64_t M, int64_t K, int64_t N, int64_t group_size);
@@ -290,7 +295,7 @@ int awq_quantize_rtn(const void* w_f16, int64_t K, int64_t N, int64_t group_size
 
 /*
  * The launch plan awq_gemm would use for this shape (host-only, no device work).
- *   family   0 = skinny split-K family, 1 = MFMA tile family
+ *   family   0 = skinny split-K family, 1 = MFMA tile family, 2 = decode family
  *   splits   number of K splits across workgroups (1 = none)
  *   grid_x, grid_y, block   launch geometry of the main kernel (tile family: of the
  *                           first launch, over rows 0 .. M - rows of awq_gemm_plan_tail)

@@ -81,6 +81,11 @@ def test_kernel_limits(lib):
     assert lib.awq_check_limits(1, 4112, 4096, -1) == _lib.AWQ_ERR_UNSUPPORTED  # K % 32
     assert lib.awq_check_limits(1, 4096, 4096, 16) == _lib.AWQ_ERR_UNSUPPORTED  # group 16
     assert lib.awq_check_limits(1, 1 << 25, 4096, -1) == _lib.AWQ_ERR_UNSUPPORTED
+    # 256-row tiles address x rows with 32-bit byte offsets: K below 2^23 above 128 rows
+    assert lib.awq_check_limits(200, 1 << 23, 4096, -1) == _lib.AWQ_ERR_UNSUPPORTED
+    assert lib.awq_check_limits(100, (1 << 23) + 1024, 4096, -1) == _lib.AWQ_OK
+    assert lib.awq_moe_tiles(1 << 40, 8, 64) == -1
+    assert lib.awq_moe_tiles(100, 8, 64) == 2 + 8
 
 
 def test_plan_families():

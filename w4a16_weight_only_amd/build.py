@@ -21,6 +21,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libawq_w4a16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 PROBE_PATH = os.path.join(HERE, "libawq_probe.so")
+# Host-only planning code, compiled by the host C++ compiler (it also builds on its own
+# for the sanitizer sweep of the planner).
+HOST_SOURCES = ["awq_plan.cpp"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 SOURCES = ["awq_api.hip", "awq_decode.hip", "awq_dequant.hip", "awq_moe.hip", "awq_quant.hip", "awq_skinny.hip", "awq_tile.hip"]
 ARCH = "gfx950"
 
@@ -30,6 +34,13 @@ def hipcc() -> str:
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
+
+
+def host_cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand:
+            return cand
+    raise RuntimeError("no host C++ compiler (g++) found")
 
 
 COMPILE_FLAGS = [
@@ -60,6 +71,10 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *COMPILE_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".host.o"))
+        objs.append(obj)
+        cmds.append([host_cxx(), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for cmd, r in zip(cmds, ex.map(_run, cmds)):
             if verbose:

@@ -4,69 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "awq_plan.h"
+
 namespace awq {
 
-// Skinny (small-M) family geometry: a workgroup owns 32 packed word-columns
-// (256 output columns) and a contiguous run of 32-row k-steps.
-constexpr int kSkinnyThreads = 256;
-constexpr int kSkinnyWordCols = 32;
-constexpr int kSkinnyCols = 8 * kSkinnyWordCols;
-constexpr int kKStep = 32;
-constexpr int kSkinnyMaxM = 16;
-constexpr int kSkinnyMaxGroups = 16;  // quantization groups one workgroup may touch
-constexpr int kFxMaxSplits = 127;     // arrivals a fixed-point split-K word can count
-constexpr int kSkinnyMaxSplits = kFxMaxSplits;
-
-// Launch plan of the skinny family (chosen on the host, see awq_api.hip).
-struct SkinnyPlan {
-  int n_tiles;       // column tiles of kSkinnyCols
-  int splits;        // K splits across workgroups (grid y)
-  int L;             // k-steps per wave
-  int waves;         // 4 or 8 waves per workgroup (8 only for 16-row plans)
-  int mrows;         // rows kept per tile: 4, 8 or 16 (8 only on 4 waves)
-  bool single_group; // every wave's k-steps lie in one quantization group
-  bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
-};
-
-// Decode family (fp16 activations, 1 <= M <= 2): a workgroup of `waves` waves owns a
-// column tile of 64 packed word-columns (512 output columns, 256 contiguous bytes of a
-// row) and waves * ks k-steps of 32 rows, all of one wave's ks k-steps in one
-// quantization group.  The K splits meet in fixed-point accumulators: n_tiles * 512 * mp
-// 64-bit words, then as many float side words, zero before the call and left zero by it.
-constexpr int kDecodeWords = 64;
-constexpr int kDecodeCols = 8 * kDecodeWords;
-constexpr int kDecodeMaxM = 2;
-struct DecodePlan {
-  int n_tiles;  // column tiles of kDecodeCols
-  int splits;   // K splits (grid y), at most kFxMaxSplits
-  int ks;       // k-steps per wave: 1 or 2
-  int waves;    // waves per workgroup: 4 or 8
-  int mp;       // rows: 1 or 2
-  bool late;    // the workgroup's rows lie in one group: scale after the wave reduction
-};
 hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                          const uint16_t* bias, int M, int K, int N, int g, const DecodePlan& p, uint64_t* accum,
                          float* side, uint16_t* y, hipStream_t stream);
-
-// MFMA tile family.  Variants (rows x columns per workgroup, threads):
-// 0: 256 x 128 (512: two k-groups of 4 waves), 1: 64 x 128 (256), 2: 32 x 128 (256).
-// With splits > 1 each workgroup covers kps k-tiles of 64 and
-// writes fp32 sums to partial, [splits][M][N]; a second kernel adds the splits and
-// the bias.
-constexpr int kTileVariants = 3;
-constexpr int kTileBM[kTileVariants] = {256, 64, 32};
-constexpr int kTileBN[kTileVariants] = {128, 128, 128};
-constexpr int kTileThreads[kTileVariants] = {512, 256, 256};
-constexpr int kTileBK = 64;
-// Blocks of a tile grid with row_units row tiles (or table entries): whole runs of
-// 8 * (256 / bn) blocks, so that the column tiles sharing 128-byte weight lines
-// fall on one XCD (the block order of tile_kernel); padding blocks exit at once.
-int64_t tile_blocks(int64_t row_units, int64_t N, int bn);
-struct TilePlan {
-  int variant;
-  int splits;  // K splits (1: direct fp16 output)
-  int kps;     // k-tiles of kTileBK per split
-};
 
 // Routed experts: the tile kernel's grouped mode.  Each workgroup takes one table
 // entry and one column tile (in the block order of tile_kernel, with entries
@@ -88,9 +32,6 @@ struct MoeTiles {
   int sub = 1;
   int lo = 0, hi = 1 << 30;
 };
-// Tile rows of the grouped variant picked for an average of `avg_rows` slots per
-// expert, and the variant itself.
-int moe_tile_variant(int64_t avg_rows, int* block_rows);
 // Counting sort of S slots by expert into offsets [E + 1], sorted_slots [S] and the
 // tile table [tiles][4] (tiles = ceil(S / block_rows) + E), one workgroup.
 hipError_t launch_moe_align(const int32_t* expert_ids, int S, int E, int block_rows, int tiles,
@@ -103,17 +44,6 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
 hipError_t launch_dequant(const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                           int K, int N, int g, void* out, bool f16, hipStream_t stream);
 
-// RTN writer: fp16 w [K, N] -> qweight [K, N/8], qzeros [K/g, N/8], scales fp16 [K/g, N].
-// Groups of up to 256 rows take one fused pass (cache = rows per thread); longer
-// groups take two passes over chunks of 128 rows (cpg chunks per group) and need
-// scratch_bytes of device scratch for the chunks' min / max, fully written by the
-// first pass before the second reads it.  grid = workgroups per launch.
-struct RtnPlan {
-  int cache = 1, block = 0, cols = 0, cpg = 1;
-  bool two_pass = false;
-  int64_t grid = 0, scratch_bytes = 0;
-};
-RtnPlan rtn_plan(int64_t K, int64_t N, int g);
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
                                int32_t* qzeros, uint16_t* scales, void* scratch, hipStream_t stream);
 
@@ -130,7 +60,6 @@ hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym,
 // of its token t with ids[t * topk + j] == e.  A block without rows exits before any
 // load.  Expert e's weights start e * w_stride words into qweight (likewise qzeros
 // and scales).  Accumulators and partials are per block.
-constexpr int kSkinnyExpertsMaxT = 64;
 struct SkinnyExperts {
   const int32_t* ids;  // [T * topk]
   int topk;

@@ -259,35 +259,9 @@ __global__ __launch_bounds__(64 * WAVES) void rtn_kernel(const u32x4* __restrict
 }
 
 namespace {
-// 4 waves of 4 row slices x 16 word columns: every row load is a 256-byte run.
-constexpr int kCL = 16, kWaves = 4;
-constexpr int kS = kWaves * (64 / kCL);  // row slices per workgroup
-constexpr int kMaxFusedCache = 16;       // fused pass for groups of up to 256 rows
-constexpr int kChunkCache = 8;           // longer groups: chunks of 128 rows
+constexpr int kCL = kRtnWordCols, kWaves = kRtnWaves;
+constexpr int kChunkCache = kRtnChunkCache;
 }  // namespace
-
-RtnPlan rtn_plan(int64_t K, int64_t N, int g) {
-  RtnPlan p;
-  p.block = 64 * kWaves;
-  p.cols = 8 * kCL;
-  const int64_t ncb = (N + p.cols - 1) / p.cols;
-  const int64_t G = K / g;
-  if (g <= kS * kMaxFusedCache) {
-    int cache = 1;
-    while (kS * cache < g) cache *= 2;
-    p.cache = cache;
-    p.two_pass = false;
-    p.cpg = 1;
-    p.scratch_bytes = 0;
-  } else {
-    p.cache = kChunkCache;
-    p.two_pass = true;
-    p.cpg = (g + kS * kChunkCache - 1) / (kS * kChunkCache);
-    p.scratch_bytes = G * p.cpg * 2 * (N / 8) * 16;
-  }
-  p.grid = G * p.cpg * ncb;
-  return p;
-}
 
 hipError_t launch_quantize_rtn(const uint16_t* w, int K, int N, int g, bool sym, int32_t* qweight,
                                int32_t* qzeros, uint16_t* scales, void* scratch, hipStream_t stream) {

@@ -632,15 +632,6 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restric
   *reinterpret_cast<u32x2_t*>(y + e) = u32x2_t{pack_act2<BF16>(a[0], a[1]), pack_act2<BF16>(a[2], a[3])};
 }
 
-// Blocks of the tile grid (see the block order in tile_kernel): row_units units per
-// run of 256 / bn column tiles, in whole runs of 8 (256 / bn) blocks.
-int64_t tile_blocks(int64_t row_units, int64_t N, int bn) {
-  const int64_t ct = 256 / bn;
-  const int64_t n_tiles = (N + bn - 1) / bn;
-  const int64_t units = row_units * ((n_tiles + ct - 1) / ct);
-  return 8 * ct * ((units + 7) / 8);
-}
-
 template <bool BF16>
 static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
                                 const uint16_t* scales, const uint16_t* bias, int M, int K, int N, int g,
@@ -665,17 +656,6 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   hipLaunchKernelGGL(tile_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N,
                      p.splits, y);
   return hipGetLastError();
-}
-
-// Grouped variants by slots per expert: 256 x 128 from 192, 64 x 128 above 32, and
-// 32 x 128 for the few rows per expert of decode-sized batches, where the weights
-// dominate and a smaller x tile lets four workgroups share a CU.  Below 192 rows two
-// or three 64 x 128 row tiles beat one 256 x 128 tile that leaves rows idle; from
-// 192 the larger tile wins (768 tokens over 8 experts, top-2: 300 against 390 us).
-int moe_tile_variant(int64_t avg_rows, int* block_rows) {
-  const int v = avg_rows >= 192 ? 0 : (avg_rows > 32 ? 1 : 2);
-  *block_rows = kTileBM[v];
-  return v;
 }
 
 hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const int32_t* qzeros,
