@@ -17,7 +17,9 @@ for the bandwidth-bound workloads or TFLOP/s for the compute-bound prefill
 workload, over the whole timed region.  `roofline` prices the kernel's average
 launch duration (HIP events on the launch stream over the timed region) against
 MI355X's peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.  `read_ceiling` times a plain streaming read of the same byte count;
+same workload (`cores`: the BLAS threads it used; `host_cores`: the cores this process
+may run on).  `read_ceiling` times a plain streaming read of the same byte count (for the
+headline and for every other bandwidth-bound workload);
 `secondary` repeats the timing (not the CPU leg) for every other workload, and for
 the large-M (tile family) ones also times the dequantize-then-dense alternative
 (awq_dequant_f16 + torch's fp16 GEMM) under the same protocol.
@@ -79,6 +81,25 @@ def load_traffic(workload: str, digest: str):
     return t.get("hbm_bytes_per_launch")
 
 
+SETTLE_S = 0.25  # untimed graph replays before a timed one: clocks and caches settle
+
+
+def settle(graph, stream, torch, seconds=SETTLE_S):
+    """Replay `graph` untimed until `seconds` have passed (at least once), so that a short
+    timed region (a few steps) measures the steady state rather than the GPU's clock ramp
+    after idling.  Returns the number of replays."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        with torch.cuda.stream(stream):
+            for _ in range(4):
+                graph.replay()
+        n += 4
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def time_workload(name, steps, warmup, torch, awq, synth, bf16=False):
     """awq_gemm on workload `name`; bf16=True takes bfloat16 x, bias and y (awq_gemm_bf16)."""
     w = synth.WORKLOADS[name]
@@ -122,6 +143,7 @@ def time_workload(name, steps, warmup, torch, awq, synth, bf16=False):
     with torch.cuda.stream(stream):
         graph.replay()  # untimed replay: graph upload and first-touch
     torch.cuda.synchronize()
+    warm_replays = settle(graph, stream, torch)
 
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
@@ -137,7 +159,7 @@ def time_workload(name, steps, warmup, torch, awq, synth, bf16=False):
         raise RuntimeError("graph replay output differs from the eager call")
     del weights
     torch.cuda.empty_cache()
-    return dict(workload=w, wall_s=wall_s, event_s=event_s, copies=copies,
+    return dict(workload=w, wall_s=wall_s, event_s=event_s, copies=copies, warm_replays=warm_replays,
                 plan=awq.plan(w.M, w.K, w.N, w.group_size))
 
 
@@ -178,6 +200,8 @@ def time_dequant_dense(name, steps, torch, awq, synth):
     with torch.cuda.stream(stream):
         graph.replay()
         stream.synchronize()
+    settle(graph, stream, torch)
+    with torch.cuda.stream(stream):
         ev0.record(stream)
         graph.replay()
         ev1.record(stream)
@@ -219,6 +243,8 @@ def time_quantize_rtn(K, N, g, sym, steps, torch, awq, synth):
     with torch.cuda.stream(stream):
         graph.replay()
         stream.synchronize()
+    settle(graph, stream, torch)
+    with torch.cuda.stream(stream):
         ev0.record(stream)
         graph.replay()
         ev1.record(stream)
@@ -267,6 +293,8 @@ def time_moe(name, steps, torch, awq, synth):
     with torch.cuda.stream(stream):
         graph.replay()
         stream.synchronize()
+    settle(graph, stream, torch)
+    with torch.cuda.stream(stream):
         ev0.record(stream)
         graph.replay()
         ev1.record(stream)
@@ -319,6 +347,8 @@ def read_ceiling(nbytes, torch, steps=400):
     with torch.cuda.stream(stream):
         graph.replay()
         stream.synchronize()
+    settle(graph, stream, torch)
+    with torch.cuda.stream(stream):
         ev0.record(stream)
         graph.replay()
         ev1.record(stream)
@@ -374,9 +404,11 @@ def cpu_baseline(name, synth):
         value, unit = w.flops() / per / 1e12, "TFLOP/s"
     else:
         value, unit = w.algorithmic_bytes() / per / 1e9, "GB/s"
-    return dict(value=round(value, 4), unit=unit, cores=int(blas_threads), kind="oracle",
+    host_cores = len(os.sched_getaffinity(0))
+    return dict(value=round(value, 4), unit=unit, cores=int(blas_threads), host_cores=host_cores, kind="oracle",
                 sample=f"{reps} full calls of the {name} layer (unpack, fp32 dequant, fp64 matmul), "
-                       f"{per:.2f} s each; numpy elementwise on 1 thread, BLAS on {blas_threads}")
+                       f"{per:.2f} s each; numpy elementwise on 1 thread, BLAS on {blas_threads} of the "
+                       f"{host_cores} host cores this process may use")
 
 
 def main():
@@ -422,7 +454,8 @@ def main():
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "group_size": w.group_size,
                    "bias": w.bias, "algorithmic_bytes": w.algorithmic_bytes(), "flops": w.flops(),
                    "plan": r["plan"], "weight_copies_rotated": r["copies"],
-                   "timing": "HIP graph of all steps, wall clock over one replay"},
+                   "timing": "HIP graph of all steps, wall clock over one replay, after "
+                             f"{r['warm_replays']} untimed replays ({SETTLE_S} s) that let clocks settle"},
         "roofline": roof,
         "kernel_avg_us": round(per_launch_s * 1e6, 3),
         "source_digest": digest,
@@ -439,6 +472,8 @@ def main():
             v, u, rf, pl = summarize(rs, n_steps)
             entry = dict(workload=name, value=round(v, 2), unit=u, kernel_avg_us=round(pl * 1e6, 3),
                          plan=rs["plan"], roofline=rf)
+            if rf["bound"] == "hbm":
+                entry["read_ceiling"] = read_ceiling(rs["workload"].algorithmic_bytes(), torch, steps=n_steps)
             if rs["plan"]["family"] == "tile":
                 dd = time_dequant_dense(name, n_steps, torch, awq, synth)
                 entry["dequant_then_dense_us"] = dd  # awq_dequant_f16 + hipBLASLt fp16 GEMM
