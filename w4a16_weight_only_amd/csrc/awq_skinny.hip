@@ -301,16 +301,30 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     if (kb + j < ke) issue(ring[j], kb + j);
   if constexpr (!SINGLE) {
     const int ng = (s1 > s0) ? (s1 - 1) / gsteps - g0 + 1 : 0;  // <= kSkinnyMaxGroups (host)
-    for (int i = tid; i < ng * 256; i += THREADS) {
+    // Every table entry's loads are issued before any is used (one round trip to
+    // memory, not one per entry a thread fills); entries past the tables load entry 0.
+    constexpr int TAB_IT = (kSkinnyMaxGroups * 256 + THREADS - 1) / THREADS;
+    uint32_t zr[TAB_IT];
+    uint16_t sr[TAB_IT];
+    const uint16_t* sbits = reinterpret_cast<const uint16_t*>(scales);
+#pragma unroll
+    for (int it = 0; it < TAB_IT; ++it) {
+      const int i = tid + it * THREADS;
+      const int gl = i >> 8, cc = (i >> 4) & 15, v = i & 15;
+      const int wcol = tile * kSkinnyWordCols + 2 * cc + (v >> 3);
+      const bool ok = i < ng * 256 && wcol < NW;
+      zr[it] = qzeros[ok ? (int64_t)(g0 + gl) * NW + wcol : 0];
+      sr[it] = sbits[ok ? (int64_t)(g0 + gl) * N + 8 * wcol + tab_col(v) : 0];
+    }
+#pragma unroll
+    for (int it = 0; it < TAB_IT; ++it) {
+      const int i = tid + it * THREADS;
+      if (i >= ng * 256) break;
       const int gl = i >> 8, cc = (i >> 4) & 15, v = i & 15;
       const int wcol = tile * kSkinnyWordCols + 2 * cc + (v >> 3);
       const int col = tab_col(v);
-      uint32_t zw = 0u;
-      float sv = 0.f;
-      if (wcol < NW) {
-        zw = qzeros[(int64_t)(g0 + gl) * NW + wcol];
-        sv = (float)scales[(int64_t)(g0 + gl) * N + 8 * wcol + col];
-      }
+      const uint32_t zw = wcol < NW ? zr[it] : 0u;
+      const float sv = wcol < NW ? (float)__builtin_bit_cast(_Float16, sr[it]) : 0.f;
       const uint32_t z = zero_code(zw, col);
       if constexpr (BF16) {
         sh.u.meta.zsplat[gl][cc][v] = __builtin_bit_cast(uint32_t, 128.0f + (float)z);  // 128 + z, fp32
