@@ -195,20 +195,30 @@ __device__ __forceinline__ void fx_clear(uint64_t* word) {
 }
 
 // Sum over s < splits of the 4 floats at p + s * stride, added in split order (the
-// same order, so the same bits, for every call).  The loads go out 8 splits at a
-// time so that their round trips overlap; a batch past the last split re-reads the
-// last one (in bounds) and does not add it.
+// same order, so the same bits, for every call).  The loads of the first B splits go
+// out together (with B >= splits, one round trip to memory), the rest 8 at a time; a
+// load past the last split re-reads the last one (in bounds) and is not added.
+template <int B>
 __device__ __forceinline__ floatx4 sum_splits(const float* __restrict__ p, int64_t stride, int splits) {
-  floatx4 a = *reinterpret_cast<const floatx4*>(p);
-  for (int s = 1; s < splits; s += 8) {
-    floatx4 v[8];
+  floatx4 v[B];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const floatx4*>(p + (int64_t)min(s + j, splits - 1) * stride);
+  for (int j = 0; j < B; ++j) v[j] = *reinterpret_cast<const floatx4*>(p + (int64_t)min(j, splits - 1) * stride);
+  floatx4 a = v[0];
+#pragma unroll
+  for (int j = 1; j < B; ++j)
+    if (j < splits) a += v[j];
+  for (int s = B; s < splits; s += 8) {
+    floatx4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const floatx4*>(p + (int64_t)min(s + j, splits - 1) * stride);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s + j < splits) a += v[j];
+      if (s + j < splits) a += w[j];
   }
   return a;
 }
+
+// Loads in the first batch of sum_splits for a given split count.
+constexpr int split_batch(int splits) { return splits <= 4 ? 4 : (splits <= 8 ? 8 : 16); }
 
 }  // namespace awq

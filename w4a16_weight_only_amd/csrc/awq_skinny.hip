@@ -543,7 +543,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 // chunk's tokens routed to the expert in token order (row m = routed token
 // 16 chunk + m); row m goes to that token's slots of the expert.  Blocks without
 // rows wrote no partials and store nothing.
-template <bool BF16, bool EXPERTS = false>
+template <bool BF16, bool EXPERTS = false, int B = 8>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             const uint16_t* __restrict__ bias, int M, int N,
                                                             int splits, int tile_entries, uint16_t* __restrict__ y,
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
   const int slot = q * 256 + t;
-  const floatx4 a = sum_splits(partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot, TILE_ENTRIES, splits);
+  const floatx4 a = sum_splits<B>(partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot, TILE_ENTRIES, splits);
   const int sv = (t >> 4) & 15, sc = t & 15;
   const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
   const int n = tile * kSkinnyCols + ct;
@@ -619,8 +619,14 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
   if (p.splits > 1 && !(p.mrows == 4 && p.atomic && !BF16)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(skinny_reduce_kernel<BF16>, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N,
-                       p.splits, p.mrows * kSkinnyCols, y, SkinnyExperts{});
+    auto red = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(p.n_tiles * 4), dim3(256), 0, stream, partial, bias, M, N, p.splits,
+                         p.mrows * kSkinnyCols, y, SkinnyExperts{});
+    };
+    const int b = split_batch(p.splits);
+    if (b == 4) red(skinny_reduce_kernel<BF16, false, 4>);
+    else if (b == 8) red(skinny_reduce_kernel<BF16, false, 8>);
+    else red(skinny_reduce_kernel<BF16, false, 16>);
   }
   return hipGetLastError();
 }

@@ -616,13 +616,13 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
 
 // y = round(sum over splits of partial[s] + bias) to fp16 or (BF16) bfloat16, 4
 // columns per thread, splits summed in order (deterministic).
-template <bool BF16>
+template <bool BF16, int B>
 __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restrict__ partial,
                                                           const uint16_t* __restrict__ bias, int64_t MN,
                                                           int N, int splits, uint16_t* __restrict__ y) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= MN) return;
-  floatx4 a = sum_splits(partial + e, MN, splits);
+  floatx4 a = sum_splits<B>(partial + e, MN, splits);
   if (bias != nullptr) {
     const int n = (int)(e % N);
 #pragma unroll
@@ -653,8 +653,13 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
   if (e != hipSuccess || !split) return e;
   const int64_t MN = (int64_t)M * N;
   const int64_t blocks = (MN / 4 + 255) / 256;
-  hipLaunchKernelGGL(tile_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N,
-                     p.splits, y);
+  auto red = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, partial, bias, MN, N, p.splits, y);
+  };
+  const int b = split_batch(p.splits);
+  if (b == 4) red(tile_reduce_kernel<BF16, 4>);
+  else if (b == 8) red(tile_reduce_kernel<BF16, 8>);
+  else red(tile_reduce_kernel<BF16, 16>);
   return hipGetLastError();
 }
 
