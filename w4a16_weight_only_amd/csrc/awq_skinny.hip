@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int q = lane >> 4;
   const int c = lane & 15;
   const int NW = N >> 3;
@@ -226,6 +226,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const int split = blockIdx.y;
   uint64_t tokens = 0;  // EXPERTS: the routed-token mask of this block's expert
   const int row0 = kSkinnyMaxM * eb.chunk;  // EXPERTS: first routed token of the chunk
+  const uint32_t x_bytes = (uint32_t)M * (uint32_t)K * 2u;  // x rows (tokens with EXPERTS)
   if constexpr (EXPERTS) {
     tokens = routed_tokens(ex, M, expert, lane);
     M = min(__builtin_popcountll(tokens) - row0, kSkinnyMaxM);
@@ -266,16 +267,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   const uint32_t x_off = ((uint32_t)xrow * (uint32_t)K + 8u * q) * 2u;
   const uint32_t w_off = ((uint32_t)(8 * q) * (uint32_t)NW + (uint32_t)(col_ok ? wc : 0)) * 4u;
   const uint32_t row_bytes = (uint32_t)NW * 4u;
-  const char* xb = reinterpret_cast<const char*>(x);
-  const char* wb = reinterpret_cast<const char*>(qweight);
+  // Buffer loads: the lane's offset stays in one VGPR and the row moves in the scalar
+  // offset, so the loads cost no vector address arithmetic.
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(qweight), (short)0, (int)(row_bytes * (uint32_t)K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, (int)x_bytes, 0x00020000);
 
   // Loads of k-step ks (ks < ke, uniform across the wave).
   auto issue = [&](Step& st, int ks) {
-    const uint32_t o = w_off + (uint32_t)ks * (uint32_t)kKStep * row_bytes;
+    const uint32_t r0 = (uint32_t)ks * (uint32_t)kKStep;
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      st.v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wb + (o + (uint32_t)r * row_bytes)));
-    st.a = *reinterpret_cast<const half8v*>(xb + (x_off + (uint32_t)ks * (uint32_t)(kKStep * 2)));
+      st.v[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, w_off, (r0 + r) * row_bytes, 2));
+    st.a = __builtin_bit_cast(half8v, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off, r0 * 2u, 0));
   };
 
   // 1. Group data and weight loads.
