@@ -70,6 +70,8 @@ void check_skinny(const SkinnyPlan& s, int64_t M, int64_t K, int64_t N, int64_t 
   CHECK(s.splits >= 1 && s.splits <= 127);
   CHECK(K * (N / 2) < k2p32 - 4096);  // qweight byte offsets
   CHECK(s.atomic == (M <= 2));
+  CHECK(!s.fused || s.splits > 1);
+  CHECK((int64_t)s.splits * s.mrows * 256 * 4 < k2p32);  // a tile's partials: 32-bit buffer offsets
   if (s.single_group) {
     CHECK(gsteps >= T || gsteps % s.L == 0);  // waves start at multiples of L
   } else {
@@ -135,7 +137,9 @@ void check_gemm(int64_t M, int64_t K, int64_t N, int64_t gs, int cus, bool bf16)
     CHECK(p.block == 64 * s.waves);
     CHECK(p.grid_x == s.n_tiles && p.grid_y == s.splits);
     check_grid(p.grid_x, p.grid_y, p.block);
-    const int64_t acc = (s.splits > 1 && s.atomic && !bf16) ? (int64_t)s.n_tiles * s.mrows * 256 * 12 : 0;
+    const int64_t acc = s.splits == 1 ? 0
+                        : (s.atomic && !bf16) ? (int64_t)s.n_tiles * s.mrows * 256 * 12
+                                              : (s.fused ? (int64_t)s.n_tiles * 4 : 0);  // arrival counters
     const int64_t part = (s.splits > 1 && !(s.atomic && !bf16)) ? (int64_t)s.n_tiles * s.splits * s.mrows * 256 * 4 : 0;
     CHECK(p.accum_bytes == acc && p.partial_bytes == part);
   } else {

@@ -165,6 +165,72 @@ def test_gemm_layer_sampled_entries(M, K, N, g):
     tol_check(y[:, cols], yref, f"layer M{M}K{K}N{N}")
 
 
+def is_fused_skinny(p):
+    """A skinny plan whose K splits are summed by each tile's last workgroup: its
+    workspace is the fp32 partials plus one 4-byte arrival counter per column tile."""
+    gx, gy = p["grid"]
+    extra = p["workspace_bytes"] - 4 * gx
+    return p["family"] == "skinny" and gy > 1 and extra > 0 and extra % (gx * gy * 1024) == 0
+
+
+FUSED = [  # (M, K, N, g): skinny plans on grids of several rounds, splits summed in-kernel
+    (4, 2048, 65536, 64),    # 4-row plan, 256 x 8 workgroups
+    (8, 1024, 131072, 64),   # 8-row plan, 512 x 4
+    (3, 8192, 16384, 64),    # 4-row plan, 32 splits: a first batch of 16 loads, then two of 8
+]
+
+
+@pytest.mark.parametrize("M,K,N,g", FUSED)
+def test_fused_split_sum(M, K, N, g):
+    """Sampled entries against the oracle, bit-identical repeats, and the same bits
+    again after a decode call (fixed-point words in the same zero-kept region as the
+    arrival counters) on the same stream: every call leaves its counters at zero."""
+    p = awq.plan(M, K, N, g)
+    print(f"fused M={M} K={K} N={N} g={g} plan={p}", flush=True)
+    assert is_fused_skinny(p)
+    d = synth.make_custom(M, K, N, g, bias=True, seed=M + K + N)
+    t = dev(d)
+    other = dev(synth.make_custom(1, 4096, 4096, 128, seed=7))
+    ys = []
+    for _ in range(3):
+        ys.append(awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g).clone())
+        awq.awq_gemm(other["x"], other["qweight"], other["qzeros"], other["scales"], other["bias"], 128)
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    y = ys[0].cpu().numpy()
+    cols = np.unique(np.concatenate([np.linspace(0, N - 1, 512).astype(np.int64), np.arange(N - 8, N)]))
+    rows = np.repeat(np.arange(M), len(cols))
+    yref = oracle.gemm_ref_entries(d["x"], d["qweight"], d["qzeros"], d["scales"], d["bias"], g,
+                                   rows, np.tile(cols, M)).reshape(M, len(cols))
+    tol_check(y[:, cols], yref, f"fused M{M}K{K}N{N}")
+
+
+def test_fused_split_sum_graph_replays():
+    """A fused plan captured in a graph and replayed three times, with eager calls of an
+    unfused skinny plan and a decode plan in between: every replay equals the eager call."""
+    M, K, N, g = FUSED[0]
+    t = dev(synth.make_custom(M, K, N, g, seed=21))
+    o1 = dev(synth.make_custom(16, 4096, 2048, 128, seed=22))
+    o2 = dev(synth.make_custom(1, 4096, 4096, 128, seed=23))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g).clone()
+        y = torch.empty_like(eager)
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g, out=y)
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            y.zero_()  # on the replay stream, ordered before the replay
+            graph.replay()
+            awq.awq_gemm(o1["x"], o1["qweight"], o1["qzeros"], o1["scales"], o1["bias"], 128)
+            awq.awq_gemm(o2["x"], o2["qweight"], o2["qzeros"], o2["scales"], o2["bias"], 128)
+        s.synchronize()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,K,N,g", [(5, 352, 800, 32), (2, 11008, 32, -1)])
 def test_dequant_ragged_negative_scales(M, K, N, g):
     """Negative scales make (q - z) == 0 a negative zero: bits must still agree."""
@@ -309,8 +375,8 @@ def test_graph_replays_match_eager(M, K, N, g):
     with torch.cuda.graph(graph, stream=s):
         awq.awq_gemm(t["x"], t["qweight"], t["qzeros"], t["scales"], t["bias"], g, out=y)
     for rep in range(3):
-        y.zero_()
         with torch.cuda.stream(s):
+            y.zero_()  # on the replay stream, ordered before the replay
             graph.replay()
             awq.awq_gemm(other["x"], other["qweight"], other["qzeros"], other["scales"], other["bias"], 64)
         s.synchronize()
@@ -357,8 +423,8 @@ def test_graph_replay_survives_workspace_growth():
     assert awq.plan(16, 4096, 8192, 128)["workspace_bytes"] > 4 * awq.plan(1, 1024, 512, 128)["workspace_bytes"]
     yb_ref = oracle.gemm_ref(big["x"], big["qweight"], big["qzeros"], big["scales"], big["bias"], 128)
     for rep in range(3):
-        y.zero_()
         with torch.cuda.stream(s):
+            y.zero_()  # on the replay stream, ordered before the replay
             graph.replay()
             yb = awq.awq_gemm(tb["x"], tb["qweight"], tb["qzeros"], tb["scales"], tb["bias"], 128)
         s.synchronize()

@@ -221,4 +221,10 @@ __device__ __forceinline__ floatx4 sum_splits(const float* __restrict__ p, int64
 // Loads in the first batch of sum_splits for a given split count.
 constexpr int split_batch(int splits) { return splits <= 4 ? 4 : (splits <= 8 ? 8 : 16); }
 
+// Cache policy (sc1) of loads and stores that every XCD must see alike: each XCD has its
+// own L2, so partial sums exchanged between workgroups inside one kernel are written
+// through to, and read back from, the device-wide point of coherence, which is what
+// agent-scope atomic stores and loads compile to.
+constexpr int kCpolDevice = 16;
+
 }  // namespace awq

@@ -122,6 +122,18 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, SkinnyPlan
   if (splits_of(L) > kSkinnyMaxSplits) return false;
   s.L = (int)L;
   s.splits = (int)splits_of(L);
+  // fp32 partials: the workgroup of a tile that arrives last sums them when the grid takes
+  // two or more rounds of resident workgroups (its tail then overlaps the next round's
+  // loads), and for 16-row plans only from five rounds (their partials are twice the
+  // 8-row plans'); otherwise a reduce kernel does.  Measured, µs per call: 4 x 8192 x
+  // 28672 34.2 -> 31.5, 3 / 8 / 16 x 4096 x 114688 61.3 / 67.4 / 77.9 -> 56.0 / 60.8 /
+  // 75.0; 16 x 8192 x 28672 (four rounds) 43.9 -> 44.5; one-round grids 2-15% slower
+  // fused (16 x 4096 x 11008 13.2 -> 13.6, 8 x 11008 x 4096 14.0 -> 16.3), where the
+  // write-through of the partials, the arrival and the partial loads sit on the
+  // critical path instead of the reduce launch.
+  const int64_t per_cu = s.waves == 8 ? 1 : (s.mrows == 16 ? 2 : 3);
+  const int64_t rounds = ((int64_t)s.n_tiles * s.splits + per_cu * cus - 1) / (per_cu * cus);
+  s.fused = s.splits > 1 && rounds >= 2 && (s.mrows <= 8 || rounds >= 5);
   return true;
 }
 
@@ -227,8 +239,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int64_t g, int cus, bool bf16) {
     // 4-row fp16 plans: 64-bit fixed-point accumulators per tile entry; 16-row
     // plans and every bfloat16 plan: fp32 partials per (tile, split, entry).
     if (p.sk.splits > 1) {
-      if (p.sk.atomic && !bf16) p.accum_bytes = skinny_accum_entries(p.sk) * 12;
-      else p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * kSkinnyCols * 4;
+      if (p.sk.atomic && !bf16) {
+        p.accum_bytes = skinny_accum_entries(p.sk) * 12;
+      } else {
+        p.partial_bytes = (int64_t)p.sk.n_tiles * p.sk.splits * p.sk.mrows * kSkinnyCols * 4;
+        if (p.sk.fused) p.accum_bytes = (int64_t)p.sk.n_tiles * 4;  // one arrival counter per column tile
+      }
     }
   } else {
     p.family = 1;

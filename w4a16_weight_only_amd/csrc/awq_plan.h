@@ -31,6 +31,7 @@ struct SkinnyPlan {
   int mrows;         // rows kept per tile: 4, 8 or 16 (8 only on 4 waves)
   bool single_group; // every wave's k-steps lie in one quantization group
   bool atomic;       // 4-row fp16 plans: splits meet in fixed-point atomics (else fp32 partials)
+  bool fused;        // fp32 partials summed by each tile's last workgroup (else a reduce kernel)
 };
 
 // Decode family (fp16 activations, 1 <= M <= 2): a workgroup of `waves` waves owns a

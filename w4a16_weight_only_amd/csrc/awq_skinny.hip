@@ -32,8 +32,9 @@
 // sum is scaled by s in fp32 (exact dequant, no fp16 weight rounding).
 // Reduction: the waves' accumulators meet in LDS in register order (conflict-free
 // 16-byte accesses) and are summed in wave order.  With S > 1 splits, the plans of
-// three or more rows (and bfloat16) store fp32 partials that a second kernel sums in
-// split order; in fp16 plans of one or two rows (ATOMIC) the splits of an output
+// three or more rows (and bfloat16) store fp32 partials that are summed in split order,
+// by a second kernel or, on grids of several rounds (`fused`), by the workgroup of each
+// tile that arrives last; in fp16 plans of one or two rows (ATOMIC) the splits of an output
 // element meet in one 64-bit accumulator in the workspace: each workgroup
 // adds, with one relaxed atomic fetch-add, its partial as a fixed-point integer
 // (24 fractional bits) plus 2^56, i.e. one arrival in the top byte.  Integer
@@ -47,6 +48,8 @@
 // 2^-24 absolute, finer than fp32's rounding for |partial| > 1.  Partials are
 // clamped to +-2^23 so up to 128 splits can never carry into the count byte; a
 // partial that large would already exceed fp16's range by a factor of 128.
+#include <type_traits>
+
 #include "awq_device.h"
 #include "awq_kernels.h"
 
@@ -153,6 +156,7 @@ struct SkinnyLds {
       float scale[kSkinnyMaxGroups][16][kTabStride];
     } meta;
     floatx4 red[WAVES][16][RL];  // [wave][accumulator][lane]
+    uint16_t ys[16][kSkinnyCols + 8];  // rounded outputs of the last split, in output order
   } u;
 };
 
@@ -198,7 +202,7 @@ template <int WAVES, int MROWS, bool SINGLE, bool BF16, bool EXPERTS = false, bo
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const uint16_t* __restrict__ bias, int M, int K, int N, int g, int L, int splits,
+    const uint16_t* __restrict__ bias, int M, int K, int N, int g, int L, int splits, int fused,
     uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y, SkinnyExperts ex) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
@@ -478,7 +482,99 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   }
 
   if (!ATOMIC) {
-    // 3'. Plain fp32 partial stores [tile][split][entry]; skinny_reduce_kernel sums
+    if constexpr (!EXPERTS) {
+      if (fused) {
+        // 3'. fp32 partials [tile][split][entry], summed in split order by whichever
+        // workgroup of the tile arrives last.  Partials are stored and read at device
+        // scope (each XCD has its own L2); every wave waits for its stores to complete
+        // before the workgroup's single arrival on the tile's counter, so the workgroup
+        // that brings the count to `splits` reads complete partials.  It resets the
+        // counter for the next call.
+        const uint32_t entry_bytes = (uint32_t)TILE_ENTRIES * 4u;
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            partial + (int64_t)blockIdx.x * splits * TILE_ENTRIES, (short)0, (int)((uint32_t)splits * entry_bytes),
+            0x00020000);
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+          const int s = tid + k * THREADS;
+          if (s < nslots)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum[k]), prs,
+                                                   (uint32_t)split * entry_bytes + 16u * (uint32_t)s, 0, kCpolDevice);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        __shared__ uint32_t last_arrival;
+        if (tid == 0) {
+          uint32_t* ctr = reinterpret_cast<uint32_t*>(accum) + blockIdx.x;
+          const bool last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                            (uint32_t)splits - 1u;
+          if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last_arrival = last;
+        }
+        __syncthreads();
+        if (!last_arrival) return;
+        // Every slot's loads of a batch are issued before any is added (a slot whose
+        // entries lie past the live rows reads slot tid's, in bounds, and is dropped).
+        floatx4 tot[SLOTS];
+        auto gather = [&](auto bc) {
+          constexpr int B = decltype(bc)::value;
+          auto ld = [&](int k, int sp) {
+            const int sl = tid + k * THREADS < nslots ? tid + k * THREADS : tid;
+            const uint32_t off = (uint32_t)min(sp, splits - 1) * entry_bytes + 16u * (uint32_t)sl;
+            return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, kCpolDevice));
+          };
+          floatx4 v[SLOTS][B];
+#pragma unroll
+          for (int k = 0; k < SLOTS; ++k)
+#pragma unroll
+            for (int j = 0; j < B; ++j) v[k][j] = ld(k, j);
+#pragma unroll
+          for (int k = 0; k < SLOTS; ++k) {
+            tot[k] = v[k][0];
+#pragma unroll
+            for (int j = 1; j < B; ++j)
+              if (j < splits) tot[k] += v[k][j];
+          }
+          for (int s0 = B; s0 < splits; s0 += 8) {
+            floatx4 w[SLOTS][8];
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) w[k][j] = ld(k, s0 + j);
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k)
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (s0 + j < splits) tot[k] += w[k][j];
+          }
+        };
+        if (splits <= 4) gather(std::integral_constant<int, 4>{});
+        else if (splits <= 8) gather(std::integral_constant<int, 8>{});
+        else gather(std::integral_constant<int, 16>{});
+        // Rounded outputs meet in LDS in output order; y is written as 16-byte row pieces.
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+          const int s = tid + k * THREADS;
+          if (s >= nslots) continue;
+          const int sv = (s >> 4) & 15, sc = s & 15;
+          const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
+          const int n = tile * kSkinnyCols + ct;
+          const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sh.u.ys[4 * (s >> 8) + i][ct] = float_to_act<BF16>(tot[k][i] + b);
+        }
+        __syncthreads();
+        for (int i = tid; i < rows * (kSkinnyCols / 8); i += THREADS) {
+          const int row = i / (kSkinnyCols / 8), pc = i % (kSkinnyCols / 8);
+          const int n0 = tile * kSkinnyCols + 8 * pc;
+          if (n0 < N)
+            *reinterpret_cast<u32x4*>(y + (int64_t)row * N + n0) =
+                *reinterpret_cast<const u32x4*>(&sh.u.ys[row][8 * pc]);
+        }
+        return;
+      }
+    }
+    // 3'. Plain fp32 partial stores [block][split][entry]; skinny_reduce_kernel sums
     // them in split order after this kernel completes.
     float* tile_part = partial + ((int64_t)blockIdx.x * splits + split) * TILE_ENTRIES;
 #pragma unroll
@@ -602,7 +698,7 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, x, reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), bias,
-                       M, K, N, g, p.L, p.splits, accum, partial, y, SkinnyExperts{});
+                       M, K, N, g, p.L, p.splits, (int)p.fused, accum, partial, y, SkinnyExperts{});
   };
   if (p.mrows == 4 && p.atomic && !BF16) {
     if (p.single_group) go(skinny_kernel<4, 4, true, false, false, true>, 256);
@@ -620,8 +716,8 @@ static hipError_t launch_skinny_t(const uint16_t* x, const int32_t* qweight, con
     if (p.single_group) go(skinny_kernel<8, 16, true, BF16>, 512);
     else go(skinny_kernel<8, 16, false, BF16>, 512);
   }
-  // Partials (every plan but the atomic ones) are summed by the reduce kernel.
-  if (p.splits > 1 && !(p.mrows == 4 && p.atomic && !BF16)) {
+  // Partials of unfused plans (all but the atomic ones) are summed by the reduce kernel.
+  if (p.splits > 1 && !p.fused && !(p.mrows == 4 && p.atomic && !BF16)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     auto red = [&](auto kern) {
@@ -645,7 +741,7 @@ hipError_t launch_skinny_experts(const uint16_t* x, const int32_t* qweight, cons
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, x, reinterpret_cast<const uint32_t*>(qweight),
                        reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
-                       T, K, N, g, p.L, p.splits, accum, partial, y, ex);
+                       T, K, N, g, p.L, p.splits, 0, accum, partial, y, ex);
   };
   if (p.mrows == 4 && p.atomic) {
     if (p.single_group) go(skinny_kernel<4, 4, true, false, true, true>, 256);
