@@ -206,12 +206,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     uint64_t* __restrict__ accum, float* __restrict__ partial, uint16_t* __restrict__ y, SkinnyExperts ex) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int TILE_ENTRIES = MROWS * kSkinnyCols;  // (slot, row) entries of a tile
-  // k-steps in flight per wave, and how K splits meet: ATOMIC (4-row fp16 plans of
-  // one or two rows) combines splits with fixed-point atomics; the other plans (the
-  // atomic count M * N * S gets large) store fp32 partials for skinny_reduce_kernel.
-  // bfloat16 always takes the partials: the fixed-point format relies on fp16's
-  // range and resolution (every fp16 value a multiple of 2^-24, |x| < 2^16).
-  constexpr int PF = (WAVES == 8 && SINGLE) ? 4 : 2;
+  // k-steps in flight per wave: two, so a wave multiplies one k-step while the next is
+  // in flight.  Deeper rings issue more loads before the first multiply, and on a
+  // saturated memory system issuing itself stalls: up_proj 16 x 4096 x 11008 13.3 ->
+  // 12.9 us and down_proj 8 x 11008 x 4096 12.4 -> 12.2 us with two instead of four on
+  // 8-wave one-group plans.  How K splits meet: ATOMIC (4-row fp16 plans of one or two
+  // rows) combines splits with fixed-point atomics; the other plans (the atomic count
+  // M * N * S gets large) store fp32 partials.  bfloat16 always takes the partials: the
+  // fixed-point format relies on fp16's range and resolution (every fp16 value a
+  // multiple of 2^-24, |x| < 2^16).
+  constexpr int PF = 2;
   static_assert(!ATOMIC || (MROWS == 4 && !BF16), "fixed-point atomics: 4-row fp16 plans only");
   static_assert(MROWS == 4 || MROWS == 8 || MROWS == 16, "4, 8 or 16 rows");
   __shared__ SkinnyLds<WAVES, 4 * MROWS> sh;
