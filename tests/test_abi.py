@@ -91,16 +91,19 @@ def test_kernel_limits(lib):
 def test_plan_families():
     p1 = awq.plan(1, 4096, 4096, 128)
     assert p1["family"] == "decode" and p1["splits"] > 1 and p1["workspace_bytes"] > 0
-    # 512-column tiles, four 32-row k-steps per workgroup: 8 x 32 workgroups
-    assert p1["grid"] == (8, 32) and p1["block"] == 256
+    # 256-column tiles, eight 32-row k-steps per workgroup: 16 x 16 workgroups
+    assert p1["grid"] == (16, 16) and p1["block"] == 256
     p16 = awq.plan(16, 4096, 11008, 128)
     assert p16["family"] == "skinny"
     assert awq.plan(2, 4096, 4096, 128)["family"] == "decode"
     assert awq.plan(3, 4096, 4096, 128)["family"] == "skinny"
-    # Long K: two k-steps per wave on eight waves; beyond the split limit (127) the
-    # older skinny family takes small M.
-    assert awq.plan(1, 11008, 4096, 64)["grid"] == (8, 22) and awq.plan(1, 11008, 4096, 64)["block"] == 512
-    assert awq.plan(1, 16384, 4096, 128)["grid"] == (8, 32)
+    # g = 64: one k-step per wave on 256-column tiles; g = 32: 512-column tiles; past 127
+    # splits of the half-width plan, 512-column tiles with two k-steps per wave on eight
+    # waves; beyond the split limit (127) the older skinny family takes small M.
+    assert awq.plan(1, 11008, 4096, 64)["grid"] == (16, 86) and awq.plan(1, 11008, 4096, 64)["block"] == 256
+    assert awq.plan(1, 11008, 4096, 32)["grid"] == (8, 86) and awq.plan(1, 11008, 4096, 32)["block"] == 256
+    assert awq.plan(1, 28672, 8192, 64)["grid"] == (16, 56) and awq.plan(1, 28672, 8192, 64)["block"] == 512
+    assert awq.plan(1, 16384, 4096, 128)["grid"] == (16, 64)
     assert awq.plan(1, 131072, 64, -1)["family"] == "skinny"
     assert awq.plan(2, 98304, 128, 64)["family"] == "skinny"
     assert awq.plan(17, 4096, 4096, 128)["family"] == "tile"

@@ -106,6 +106,8 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (30, 96, 256, 32, True),     # 32 x 128 tiles: last k-tile partial
     (160, 1024, 512, 128, True),  # 129-192 rows on a short K: three 64 x 128 row tiles, split over K
     (24, 4128, 96, 32, True),    # 32 x 128 tiles split over K, last split ends in a half k-tile
+    (1, 3072, 544, 384, True),   # decode, 256-column tiles (last one partial), each half of a
+    (2, 3072, 544, 384, False),  # workgroup's waves scaled apart, the halves in one or two groups
 ]
 
 

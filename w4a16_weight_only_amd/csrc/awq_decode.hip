@@ -7,13 +7,13 @@
 // expanded only in registers, and the arithmetic hides under the stream).
 //
 // Work split.  A workgroup of WAVES waves owns a column tile of 64 packed word-columns
-// (256 contiguous bytes of every qweight row, 512 output columns) and WAVES * KS k-steps
-// of 32 rows; wave w takes KS consecutive k-steps, all in one quantization group (the
-// host guarantees it).  The K splits of a tile meet in 64-bit fixed-point accumulators
-// (awq_device.h): one returning atomic per output element and split, and the add that
-// completes an element writes y.
+// (256 contiguous bytes of every qweight row, 512 output columns), or 32 (HALF: 128
+// bytes, 256 columns), and WAVES * KS k-steps of 32 rows; wave w takes KS consecutive
+// k-steps, all in one quantization group (the host guarantees it).  The K splits of a
+// tile meet in 64-bit fixed-point accumulators (awq_device.h): one returning atomic per
+// output element and split, and the add that completes an element writes y.
 //
-// Per wave and k-step, on v_mfma_f32_16x16x32_f16 (x rows padded to 16):
+// Per wave and k-step, on v_mfma_f32_16x16x16_f16 (x rows padded to 16), for full tiles:
 //   lane l: c = l % 16 picks the 16-byte chunk (words 4c .. 4c+3) of the tile's 256-byte
 //   row segment, q = l / 16 picks rows 8q .. 8q+7 of the k-step; one 16-byte load per
 //   row (16 lanes cover a row's 256 bytes, one wave instruction covers 4 rows).  Every
@@ -21,12 +21,16 @@
 //   v_perm_b32 interleaves byte t of both words, the 0x6400 mantissa trick makes each
 //   nibble pair an exact fp16 pair (1024 + code, or 1024 + 16 code), and one packed add
 //   (or fma by 1/16) with the column's -(1024 + z) (or -(64 + z)) leaves the exact
-//   integers (q - z) of rows (r, r + 1).  Four pairs are one B operand: 8 consecutive k
-//   of one column.  The 32 (word, byte, nibble) choices of the lane's chunk give 32
-//   MFMAs per k-step; MFMA column c is chunk c.  The A operand is x[m = l % 16][8q ..
-//   8q+7] of the k-step, one contiguous 16-byte load.  fp16 x times a small integer is
+//   integers (q - z) of rows (r, r + 1).  Two pairs are one B operand: 4 consecutive k
+//   of one column, rows 8q .. 8q+3 or 8q+4 .. 8q+7 (the two halves of the k-step).  The
+//   32 (word, byte, nibble) choices of the lane's chunk give 32 MFMAs per half; MFMA
+//   column c is chunk c.  The A operand is x[m = l % 16][8q .. 8q+7] of the k-step, one
+//   contiguous 16-byte load.  fp16 x times a small integer is
 //   exact in fp32 and the MFMA accumulates in fp32; the wave's group sum is then scaled
 //   by s in fp32, so the weight is never rounded.
+// HALF tiles: lane l takes chunk l % 8 of the 128-byte segment and only nibble half
+// (l / 8) % 2 of each byte, so MFMA column l % 16 is (nibble half, chunk) and a k-step is
+// 16 MFMAs; the two lanes of a chunk load the same 16 bytes.
 // Reduction: the waves' sums meet in LDS (in rounds of 32 KB), each thread sums a few
 // (row block, column) entries over the waves in wave order, then adds them to the
 // fixed-point words.
@@ -45,6 +49,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Column within a word of MFMA entry u = 2 t + h (byte t, nibble h of the byte).
 __device__ __forceinline__ constexpr int entry_col(int u) { return (u & 1) ? hi_col(u >> 1) : lo_col(u >> 1); }
 
+// Column within the tile of MFMA entry v in lane l (output column l % 16 of the MFMA).
+template <bool HALF>
+__device__ __forceinline__ int out_col(int v, int l) {
+  if constexpr (HALF) {
+    const int c = l & 7, h = (l >> 3) & 1, t = v & 3;
+    return 8 * (4 * c + (v >> 2)) + (h ? hi_col(t) : lo_col(t));
+  } else {
+    return 8 * (4 * (l & 15) + (v >> 3)) + entry_col(v & 7);
+  }
+}
+
 // Byte t of each 16-bit half of a word, replicated: [b.t, 0, b.t, 0].
 template <int t>
 __device__ __forceinline__ uint32_t splat_byte(uint32_t b) {
@@ -56,8 +71,16 @@ __device__ __forceinline__ uint32_t splat_byte(uint32_t b) {
 // MP: rows padded to 1, 2, 4, 8 or 16; KS: k-steps per wave; WAVES: 4 or 8 waves per
 // workgroup (two waves per SIMD either way).  LATE: the workgroup's rows lie in one
 // quantization group, so the scales are applied once, to the sums reduced over the
-// waves (one 2-byte scale per output entry instead of 64 bytes per lane and wave).
-template <int MP, int KS, int WAVES, bool LATE>
+// waves (one 2-byte scale per output entry instead of 64 bytes per lane and wave);
+// LATE2: they lie in two, one per half of the waves, whose sums are reduced and scaled
+// apart (two 2-byte scales per output entry).
+// HALF: a column tile of 32 word-columns (256 outputs, 128 bytes of a row): lane l
+// takes chunk c = l % 8 and nibble half h = (l / 8) % 2 of every byte (MFMA column
+// l % 16 is the pair (h, c)), the lanes of both halves load the same 16 bytes, and a
+// k-step is 16 MFMAs (word w, byte t) instead of 32.  Half the columns per workgroup
+// means half the K splits for the same grid, so half the fixed-point adds, and half
+// as many of them meet at each address.
+template <int MP, int KS, int WAVES, bool LATE, bool HALF = false, bool LATE2 = false>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uint16_t* __restrict__ x,
                                                         const uint32_t* __restrict__ qweight,
                                                         const uint32_t* __restrict__ qzeros,
@@ -70,17 +93,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   constexpr int LIVE = MP <= 4 ? 16 : 16 * (MP / 4);
   constexpr int RREG = MP < 4 ? MP : 4;
   constexpr int THREADS = 64 * WAVES;
-  constexpr int ROUNDS = LIVE / 16;      // LDS rounds of the wave reduction (WAVES * 8 KB each)
-  constexpr int VR = 32 / ROUNDS;        // MFMA entries per round
-  constexpr int EPR = 512 / THREADS;     // reduced (entry, lane) pairs per thread and round
+  constexpr int WORDS = HALF ? kDecodeWords / 2 : kDecodeWords;  // packed words of a column tile
+  constexpr int COLS = 8 * WORDS;
+  constexpr int NV = HALF ? 16 : 32;     // MFMA entries (accumulators) per k-step
+  constexpr int ROUNDS = LIVE / 16;      // LDS rounds of the wave reduction
+  constexpr int VR = NV / ROUNDS;        // MFMA entries per round
+  constexpr int PAIRS = VR * LIVE;       // (entry, lane) pairs per round: the tile's columns
+  constexpr int EPR = PAIRS / THREADS;   // reduced pairs per thread and round
   constexpr int EPT = EPR * ROUNDS;      // reduced pairs per thread
-  static_assert(VR * LIVE == 512, "one round is 512 (entry, lane) pairs");
+  static_assert(PAIRS == COLS && EPR * THREADS == PAIRS, "one round is one (entry, lane) pair per column");
   __shared__ floatx4 red[WAVES][VR][LIVE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane & 15;
+  const int c = HALF ? (lane & 7) : (lane & 15);
+  const int hsel = HALF ? ((lane >> 3) & 1) : 0;  // HALF: this lane's nibble of each byte
   const int q = lane >> 4;
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
@@ -88,7 +116,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   const int T = K >> 5;
   // Lanes of a partial last tile read the last valid chunk (N % 32 == 0, so NW % 4 == 0)
   // and never store.
-  const int wc_raw = tile * kDecodeWords + 4 * c;
+  const int wc_raw = tile * WORDS + 4 * c;
   const int wc = wc_raw < NW ? wc_raw : NW - 4;
   const int kb = (split * WAVES + wave) * KS;  // first k-step of this wave
   const int nks = min(max(T - kb, 0), KS);      // k-steps this wave multiplies (uniform)
@@ -128,40 +156,53 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   // bias every lane reads x[0] and selects 0.
   const bool has_bias = bias != nullptr;
   const uint16_t* bsrc = has_bias ? bias : x;
-  uint16_t braw[EPT], sraw[EPT];
+  // LATE2: the groups of the first and the second half of the waves (a second half
+  // past K reads the last group; its sums are zero).
+  const int g_first = (min(split * WAVES * KS, T - 1) * kKStep) / g;
+  const int g_second = (min(split * WAVES * KS + WAVES / 2 * KS, T - 1) * kKStep) / g;
+  uint16_t braw[EPT], sraw[EPT], sraw2[LATE2 ? EPT : 1];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int le = tid + THREADS * (k % EPR);
     const int v = (k / EPR) * VR + le / LIVE, l = le % LIVE;
-    const int n = min(tile * kDecodeCols + 8 * (4 * (l & 15) + (v >> 3)) + entry_col(v & 7), N - 1);
+    const int n = min(tile * COLS + out_col<HALF>(v, l), N - 1);
     braw[k] = bsrc[has_bias ? n : 0];
-    if constexpr (LATE) sraw[k] = scales[(int64_t)gi * N + n];  // the workgroup's group
+    if constexpr (LATE) sraw[k] = scales[(int64_t)(LATE2 ? g_first : gi) * N + n];  // the workgroup's group
+    if constexpr (LATE2) sraw2[k] = scales[(int64_t)g_second * N + n];
   }
   // Every load is issued before any arithmetic waits on one.
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- Zero splats of the group: entry v = 8 w + 2 t + h holds -(1024 + z) (h = 0) or
   // -(64 + z) (h = 1) in both fp16 halves.
+  // HALF: entry v = 4 w + t holds the lane's own nibble half: -(1024 + z) or -(64 + z).
   const UnpackConsts uk = unpack_consts();
   uint32_t zneg_lo = 0xE400E400u, zneg_hi = 0xD400D400u;
   asm volatile("" : "+v"(zneg_lo), "+v"(zneg_hi));
-  uint32_t zs[32];
+  const uint32_t hmask = hsel ? uk.mhi : uk.mlo;           // HALF: the lane's nibble mask
+  const uint32_t zneg_h = hsel ? zneg_hi : zneg_lo;
+  const half2v hmult = hsel ? half2v{(_Float16)0.0625f, (_Float16)0.0625f} : half2v{(_Float16)1.f, (_Float16)1.f};
+  uint32_t zs[HALF ? 16 : 32];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t b[4] = {splat_byte<0>(zw[w]), splat_byte<1>(zw[w]), splat_byte<2>(zw[w]), splat_byte<3>(zw[w])};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      zs[8 * w + 2 * t] = (b[t] & uk.mlo) | zneg_lo;
-      zs[8 * w + 2 * t + 1] = (b[t] & uk.mhi) | zneg_hi;
+      if constexpr (HALF) {
+        zs[4 * w + t] = (b[t] & hmask) | zneg_h;
+      } else {
+        zs[8 * w + 2 * t] = (b[t] & uk.mlo) | zneg_lo;
+        zs[8 * w + 2 * t + 1] = (b[t] & uk.mhi) | zneg_hi;
+      }
     }
   }
 
   // ---- Multiply, in halves of a k-step (rows 8q .. 8q+3, then 8q+4 .. 8q+7) on
   // v_mfma_f32_16x16x16_f16, so the first half runs while the second half's loads are
   // still arriving.
-  floatx4 acc[32];
+  floatx4 acc[NV];
 #pragma unroll
-  for (int v = 0; v < 32; ++v) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int v = 0; v < NV; ++v) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
   const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -187,15 +228,25 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
               else if (t == 1) pb = pair_byte<1>(ra, rb);
               else if (t == 2) pb = pair_byte<2>(ra, rb);
               else pb = pair_byte<3>(ra, rb);
-              lo[p] = as_u32(as_h2((pb & uk.mlo) | uk.magic) + as_h2(zs[8 * w + 2 * t]));
-              hi[p] = as_u32(__builtin_elementwise_fma(as_h2((pb & uk.mhi) | uk.magic), sixteenth,
-                                                       as_h2(zs[8 * w + 2 * t + 1])));
+              if constexpr (HALF) {
+                lo[p] = as_u32(__builtin_elementwise_fma(as_h2((pb & hmask) | uk.magic), hmult, as_h2(zs[4 * w + t])));
+              } else {
+                lo[p] = as_u32(as_h2((pb & uk.mlo) | uk.magic) + as_h2(zs[8 * w + 2 * t]));
+                hi[p] = as_u32(__builtin_elementwise_fma(as_h2((pb & uk.mhi) | uk.magic), sixteenth,
+                                                         as_h2(zs[8 * w + 2 * t + 1])));
+              }
             }
-            const int vl = 8 * w + 2 * t;
-            acc[vl] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, __builtin_bit_cast(half4v, u32x2{lo[0], lo[1]}),
-                                                            acc[vl], 0, 0, 0);
-            acc[vl + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, __builtin_bit_cast(half4v, u32x2{hi[0], hi[1]}),
-                                                                acc[vl + 1], 0, 0, 0);
+            if constexpr (HALF) {
+              const int vl = 4 * w + t;
+              acc[vl] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, __builtin_bit_cast(half4v, u32x2{lo[0], lo[1]}),
+                                                              acc[vl], 0, 0, 0);
+            } else {
+              const int vl = 8 * w + 2 * t;
+              acc[vl] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, __builtin_bit_cast(half4v, u32x2{lo[0], lo[1]}),
+                                                              acc[vl], 0, 0, 0);
+              acc[vl + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                  ah, __builtin_bit_cast(half4v, u32x2{hi[0], hi[1]}), acc[vl + 1], 0, 0, 0);
+            }
           }
         }
       }
@@ -209,15 +260,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   if constexpr (!LATE) {
     const _Float16* sh = reinterpret_cast<const _Float16*>(sv);
 #pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      const float sc = (float)sh[8 * (v >> 3) + entry_col(v & 7)];
+    for (int v = 0; v < NV; ++v) {
+      const float sc = HALF ? (float)sh[8 * (v >> 2) + (hsel ? hi_col(v & 3) : lo_col(v & 3))]
+                            : (float)sh[8 * (v >> 3) + entry_col(v & 7)];
 #pragma unroll
       for (int r = 0; r < RREG; ++r) acc[v][r] *= sc;
     }
   }
 
   // ---- Waves -> LDS, in rounds; each thread sums EPR (entry, lane) pairs per round.
-  floatx4 ent[EPT];
+  floatx4 ent[EPT], ent2[LATE2 ? EPT : 1];
 #pragma unroll
   for (int b = 0; b < ROUNDS; ++b) {
     if (b > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous round read
@@ -229,10 +281,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
 #pragma unroll
     for (int k = 0; k < EPR; ++k) {
       const int le = tid + THREADS * k;
+      constexpr int W1 = LATE2 ? WAVES / 2 : WAVES;  // waves of the first group
       floatx4 sum = red[0][le / LIVE][le % LIVE];
 #pragma unroll
-      for (int wv2 = 1; wv2 < WAVES; ++wv2) sum += red[wv2][le / LIVE][le % LIVE];
+      for (int wv2 = 1; wv2 < W1; ++wv2) sum += red[wv2][le / LIVE][le % LIVE];
       ent[EPR * b + k] = sum;
+      if constexpr (LATE2) {
+        floatx4 sum2 = red[W1][le / LIVE][le % LIVE];
+#pragma unroll
+        for (int wv2 = W1 + 1; wv2 < WAVES; ++wv2) sum2 += red[wv2][le / LIVE][le % LIVE];
+        ent2[EPR * b + k] = sum2;
+      }
     }
   }
 
@@ -240,8 +299,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
       const float sc = (float)__builtin_bit_cast(_Float16, sraw[k]);
+      if constexpr (LATE2) {
+        const float sc2 = (float)__builtin_bit_cast(_Float16, sraw2[k]);
 #pragma unroll
-      for (int r = 0; r < RREG; ++r) ent[k][r] *= sc;
+        for (int r = 0; r < RREG; ++r) ent[k][r] = ent[k][r] * sc + ent2[k][r] * sc2;
+      } else {
+#pragma unroll
+        for (int r = 0; r < RREG; ++r) ent[k][r] *= sc;
+      }
     }
   }
 
@@ -256,10 +321,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   for (int k = 0; k < EPT; ++k) {
     const int le = tid + THREADS * (k % EPR);
     const int v = (k / EPR) * VR + le / LIVE, l = le % LIVE;
-    const int cl = 8 * (4 * (l & 15) + (v >> 3)) + entry_col(v & 7);
     row0[k] = 4 * (l >> 4);
-    ncol[k] = tile * kDecodeCols + cl;
-    e0[k] = (tile * 32 + v) * RREG * LIVE + l;
+    ncol[k] = tile * COLS + out_col<HALF>(v, l);
+    e0[k] = (tile * NV + v) * RREG * LIVE + l;
     nrow[k] = ncol[k] < N ? min(max(M - row0[k], 0), RREG) : 0;
   }
   if (splits == 1) {  // K <= 128: the workgroup holds the whole sum
@@ -313,7 +377,15 @@ hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_
   };
   auto by_shape = [&](auto mp) {
     constexpr int MP = decltype(mp)::value;
-    if (p.waves == 8) {
+    if (p.words != kDecodeWords) {  // half-width tiles: 4 waves
+      if (p.ks == 2) {
+        if (p.late == 2) go(decode_kernel<MP, 2, 4, true, true, true>, 256);
+        else p.late ? go(decode_kernel<MP, 2, 4, true, true>, 256) : go(decode_kernel<MP, 2, 4, false, true>, 256);
+      } else {
+        if (p.late == 2) go(decode_kernel<MP, 1, 4, true, true, true>, 256);
+        else p.late ? go(decode_kernel<MP, 1, 4, true, true>, 256) : go(decode_kernel<MP, 1, 4, false, true>, 256);
+      }
+    } else if (p.waves == 8) {
       if (p.ks == 2) p.late ? go(decode_kernel<MP, 2, 8, true>, 512) : go(decode_kernel<MP, 2, 8, false>, 512);
       else p.late ? go(decode_kernel<MP, 1, 8, true>, 512) : go(decode_kernel<MP, 1, 8, false>, 512);
     } else {

@@ -149,31 +149,50 @@ bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, DecodePlan& d) {
   if (M < 1 || M > kDecodeMaxM) return false;
   if (K * (N / 2) >= (int64_t(1) << 32) - 4096) return false;
   const int64_t T = K / kKStep;
-  d.n_tiles = (int)((N / 8 + kDecodeWords - 1) / kDecodeWords);
   d.mp = (int)M;
   auto splits_of = [&](int ks, int waves) { return (T + (int64_t)ks * waves - 1) / ((int64_t)ks * waves); };
   auto ok = [&](int ks, int waves) {
     return (g == K || g % (kKStep * ks) == 0) && splits_of(ks, waves) <= kFxMaxSplits;
   };
-  // Up to 128 k-steps (K <= 4096): one k-step per wave, 4 waves (4096 x 4096: 6.2 us
-  // against 6.6-8.2 for the other shapes).  Longer K: two k-steps per wave on 8-wave
-  // workgroups (11008 x 4096: 8.9 us against 9.7-12.8).
-  const int pref_ks = T <= 128 ? 1 : 2, pref_w = T <= 128 ? 4 : 8;
-  const int cand[4][2] = {{pref_ks, pref_w}, {1, 4}, {1, 8}, {2, 8}};
-  d.ks = 0;
-  for (const auto& c : cand)
-    if (ok(c[0], c[1])) {
-      d.ks = c[0];
-      d.waves = c[1];
-      break;
-    }
-  if (d.ks == 0) return false;
+  // Half-width tiles (256 columns, 4 waves) whenever each half of a workgroup's waves
+  // stays inside one quantization group, so the sums are scaled after the wave reduction:
+  // two k-steps per wave when g is K or a multiple of 128, one when a multiple of 64.
+  // Half the columns per workgroup halves the K splits for the same grid, and with them
+  // the fixed-point adds and how many meet at each address.  Measured, us per call, full
+  // tiles -> half: 1 x 4096 x 4096 g128 6.38 -> 5.39, g64 6.88 -> 5.52; 2 x 4096 x 4096
+  // g128 8.00 -> 6.04; 1 x 4096 x 11008 g128 10.15 -> 8.33; 1 x 11008 x 4096 g-1 9.02 ->
+  // 8.25, g64 9.80 -> 9.10; 1 x 8192 x 28672 g128 35.9 -> 27.6.  Half tiles whose waves
+  // scale their own sums (g = 32, or g = 64 with two k-steps) measured slower (1 x 4096 x
+  // 4096 g32 6.86 -> 7.82; 1 x 11008 x 4096 g64 9.5 -> 11.5), so other layers keep full
+  // tiles: up to 128 k-steps one k-step per wave on 4 waves, longer K two k-steps per
+  // wave on 8 waves (11008 x 4096: 8.9 us against 9.7-12.8).
+  const int hks = (g == K || g % (4 * kKStep) == 0) ? 2 : (g % (2 * kKStep) == 0 ? 1 : 0);
+  if (hks > 0 && splits_of(hks, 4) <= kFxMaxSplits) {
+    d.words = kDecodeWords / 2;
+    d.ks = hks;
+    d.waves = 4;
+  } else {
+    d.words = kDecodeWords;
+    const int pref_ks = T <= 128 ? 1 : 2, pref_w = T <= 128 ? 4 : 8;
+    const int cand[4][2] = {{pref_ks, pref_w}, {1, 4}, {1, 8}, {2, 8}};
+    d.ks = 0;
+    for (const auto& c : cand)
+      if (ok(c[0], c[1])) {
+        d.ks = c[0];
+        d.waves = c[1];
+        break;
+      }
+    if (d.ks == 0) return false;
+  }
+  d.n_tiles = (int)((N / 8 + d.words - 1) / d.words);
   d.splits = (int)splits_of(d.ks, d.waves);
-  d.late = g == K || g % ((int64_t)kKStep * d.ks * d.waves) == 0;
+  d.late = (g == K || g % ((int64_t)kKStep * d.ks * d.waves) == 0) ? 1
+           : (d.words != kDecodeWords && g % ((int64_t)kKStep * d.ks * d.waves / 2) == 0) ? 2
+                                                                                         : 0;
   return true;
 }
 
-int64_t decode_entries(const DecodePlan& d) { return (int64_t)d.n_tiles * kDecodeCols * d.mp; }
+int64_t decode_entries(const DecodePlan& d) { return (int64_t)d.n_tiles * 8 * d.words * d.mp; }
 
 int64_t skinny_accum_entries(const SkinnyPlan& s) { return (int64_t)s.n_tiles * s.mrows * kSkinnyCols; }
 

@@ -35,20 +35,22 @@ struct SkinnyPlan {
 };
 
 // Decode family (fp16 activations, 1 <= M <= 2): a workgroup of `waves` waves owns a
-// column tile of 64 packed word-columns (512 output columns, 256 contiguous bytes of a
-// row) and waves * ks k-steps of 32 rows, all of one wave's ks k-steps in one
-// quantization group.  The K splits meet in fixed-point accumulators: n_tiles * 512 * mp
-// 64-bit words, then as many float side words, zero before the call and left zero by it.
+// column tile of `words` packed word-columns (64: 512 output columns, 256 contiguous
+// bytes of a row; 32: 256 columns, 128 bytes, 4 waves only) and waves * ks k-steps of 32
+// rows, all of one wave's ks k-steps in one quantization group.  The K splits meet in
+// fixed-point accumulators: n_tiles * 8 * words * mp 64-bit words, then as many float
+// side words, zero before the call and left zero by it.
 constexpr int kDecodeWords = 64;
-constexpr int kDecodeCols = 8 * kDecodeWords;
 constexpr int kDecodeMaxM = 2;
 struct DecodePlan {
-  int n_tiles;  // column tiles of kDecodeCols
+  int n_tiles;  // column tiles of 8 * words columns
+  int words;    // packed word-columns per tile: 64, or 32 (half-width tiles)
   int splits;   // K splits (grid y), at most kFxMaxSplits
   int ks;       // k-steps per wave: 1 or 2
   int waves;    // waves per workgroup: 4 or 8
   int mp;       // rows: 1 or 2
-  bool late;    // the workgroup's rows lie in one group: scale after the wave reduction
+  int late;     // the workgroup's rows lie in one group (1) or two, one per half of its
+                // waves (2): scale after the wave reduction; 0: each wave scales its sums
 };
 // MFMA tile family.  Variants (rows x columns per workgroup, threads):
 // 0: 256 x 128 (512: two k-groups of 4 waves), 1: 64 x 128 (256), 2: 32 x 128 (256).
