@@ -124,11 +124,12 @@ void check_gemm(int64_t M, int64_t K, int64_t N, int64_t gs, int cus, bool bf16)
     CHECK(d.splits == cdiv(T, span));
     CHECK(d.splits >= 1 && d.splits <= 127);
     CHECK(g == K || (g / 32) % d.ks == 0);             // a wave's k-steps in one group
-    CHECK(d.late >= 0 && d.late <= 2);
-    CHECK(d.late != 1 || g == K || (g / 32) % span == 0);  // a workgroup's k-steps in one group
-    // two groups: each half of the waves' k-steps in one group (half-width tiles only)
-    CHECK(d.late != 2 || (d.words == 32 && d.waves % 2 == 0 && (g / 32) % (span / 2) == 0));
+    CHECK(d.late == 0 || d.late == 1 || d.late == 2 || d.late == 4);
+    // late > 0: the workgroup's waves form `late` equal parts, each inside one group
+    CHECK(d.late == 0 || g == K || (g / 32) % (span / d.late) == 0);
+    CHECK(d.late <= 1 || d.words == 32);
     CHECK(d.words == 64 || (d.words == 32 && d.waves == 4 && d.late >= 1));
+    CHECK(d.words == 32 || d.splits > 0);
     CHECK(d.n_tiles == cdiv(N / 8, d.words));
     CHECK(p.grid_x == d.n_tiles && p.grid_y == d.splits);
     CHECK(K * (N / 2) < k2p32 - 4096);

@@ -97,12 +97,12 @@ def test_plan_families():
     assert p16["family"] == "skinny"
     assert awq.plan(2, 4096, 4096, 128)["family"] == "decode"
     assert awq.plan(3, 4096, 4096, 128)["family"] == "skinny"
-    # g = 64: one k-step per wave on 256-column tiles; g = 32: 512-column tiles; past 127
-    # splits of the half-width plan, 512-column tiles with two k-steps per wave on eight
-    # waves; beyond the split limit (127) the older skinny family takes small M.
-    assert awq.plan(1, 11008, 4096, 64)["grid"] == (16, 86) and awq.plan(1, 11008, 4096, 64)["block"] == 256
-    assert awq.plan(1, 11008, 4096, 32)["grid"] == (8, 86) and awq.plan(1, 11008, 4096, 32)["block"] == 256
-    assert awq.plan(1, 28672, 8192, 64)["grid"] == (16, 56) and awq.plan(1, 28672, 8192, 64)["block"] == 512
+    # 256-column tiles: two k-steps per wave for g = 64, one for g = 32; past 127 splits
+    # of those, 512-column tiles with two k-steps per wave on eight waves; beyond the
+    # split limit (127) the older skinny family takes small M.
+    assert awq.plan(1, 11008, 4096, 64)["grid"] == (16, 43) and awq.plan(1, 11008, 4096, 64)["block"] == 256
+    assert awq.plan(1, 11008, 4096, 32)["grid"] == (16, 86) and awq.plan(1, 11008, 4096, 32)["block"] == 256
+    assert awq.plan(1, 40960, 4096, 64)["grid"] == (8, 80) and awq.plan(1, 40960, 4096, 64)["block"] == 512
     assert awq.plan(1, 16384, 4096, 128)["grid"] == (16, 64)
     assert awq.plan(1, 131072, 64, -1)["family"] == "skinny"
     assert awq.plan(2, 98304, 128, 64)["family"] == "skinny"

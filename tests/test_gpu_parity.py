@@ -108,6 +108,9 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (24, 4128, 96, 32, True),    # 32 x 128 tiles split over K, last split ends in a half k-tile
     (1, 3072, 544, 384, True),   # decode, 256-column tiles (last one partial), each half of a
     (2, 3072, 544, 384, False),  # workgroup's waves scaled apart, the halves in one or two groups
+    (1, 3072, 544, 96, True),    # decode, one k-step per wave, each wave's sums scaled apart
+    (2, 2048, 800, 32, True),    # the same with g = 32
+    (1, 40960, 96, 64, True),    # decode past 127 half-width splits: 512-column tiles, 8 waves
 ]
 
 

@@ -69,18 +69,18 @@ __device__ __forceinline__ uint32_t splat_byte(uint32_t b) {
 }  // namespace
 
 // MP: rows padded to 1, 2, 4, 8 or 16; KS: k-steps per wave; WAVES: 4 or 8 waves per
-// workgroup (two waves per SIMD either way).  LATE: the workgroup's rows lie in one
-// quantization group, so the scales are applied once, to the sums reduced over the
-// waves (one 2-byte scale per output entry instead of 64 bytes per lane and wave);
-// LATE2: they lie in two, one per half of the waves, whose sums are reduced and scaled
-// apart (two 2-byte scales per output entry).
+// workgroup (two waves per SIMD either way).  LG: how the group scales are applied.
+// LG = 0: each wave scales its own sums (the 32 scales of its lane's chunk, 64 bytes per
+// lane).  LG = 1, 2, 4: the workgroup's waves form LG equal parts, each inside one
+// quantization group; the wave reduction sums each part apart and scales it once (LG
+// 2-byte scales per output entry).
 // HALF: a column tile of 32 word-columns (256 outputs, 128 bytes of a row): lane l
 // takes chunk c = l % 8 and nibble half h = (l / 8) % 2 of every byte (MFMA column
 // l % 16 is the pair (h, c)), the lanes of both halves load the same 16 bytes, and a
 // k-step is 16 MFMAs (word w, byte t) instead of 32.  Half the columns per workgroup
 // means half the K splits for the same grid, so half the fixed-point adds, and half
 // as many of them meet at each address.
-template <int MP, int KS, int WAVES, bool LATE, bool HALF = false, bool LATE2 = false>
+template <int MP, int KS, int WAVES, int LG, bool HALF = false>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uint16_t* __restrict__ x,
                                                         const uint32_t* __restrict__ qweight,
                                                         const uint32_t* __restrict__ qzeros,
@@ -145,6 +145,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
       wv[s][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voff, (r0 + j) * row_bytes, 2));
   }
   // Scales of the lane's 32 columns (8 wc .. 8 wc + 31), when each wave scales its own sums.
+  constexpr bool LATE = LG > 0;
+  static_assert(LG == 0 || LG == 1 || (LG == 2 && WAVES % 2 == 0) || (LG == 4 && WAVES % 4 == 0), "parts");
   u32x4 sv[LATE ? 1 : 4];
   if constexpr (!LATE) {
 #pragma unroll
@@ -156,19 +158,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   // bias every lane reads x[0] and selects 0.
   const bool has_bias = bias != nullptr;
   const uint16_t* bsrc = has_bias ? bias : x;
-  // LATE2: the groups of the first and the second half of the waves (a second half
-  // past K reads the last group; its sums are zero).
-  const int g_first = (min(split * WAVES * KS, T - 1) * kKStep) / g;
-  const int g_second = (min(split * WAVES * KS + WAVES / 2 * KS, T - 1) * kKStep) / g;
-  uint16_t braw[EPT], sraw[EPT], sraw2[LATE2 ? EPT : 1];
+  // The group of each part of the waves (a part past K reads the last group; its sums
+  // are zero).
+  constexpr int LGN = LG > 0 ? LG : 1;
+  int gpart[LGN];
+#pragma unroll
+  for (int j = 0; j < LGN; ++j) gpart[j] = (min((split * WAVES + j * (WAVES / LGN)) * KS, T - 1) * kKStep) / g;
+  uint16_t braw[EPT], sraw[LGN][EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int le = tid + THREADS * (k % EPR);
     const int v = (k / EPR) * VR + le / LIVE, l = le % LIVE;
     const int n = min(tile * COLS + out_col<HALF>(v, l), N - 1);
     braw[k] = bsrc[has_bias ? n : 0];
-    if constexpr (LATE) sraw[k] = scales[(int64_t)(LATE2 ? g_first : gi) * N + n];  // the workgroup's group
-    if constexpr (LATE2) sraw2[k] = scales[(int64_t)g_second * N + n];
+    if constexpr (LATE) {
+#pragma unroll
+      for (int j = 0; j < LG; ++j) sraw[j][k] = scales[(int64_t)gpart[j] * N + n];
+    }
   }
   // Every load is issued before any arithmetic waits on one.
   __builtin_amdgcn_sched_barrier(0);
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   }
 
   // ---- Waves -> LDS, in rounds; each thread sums EPR (entry, lane) pairs per round.
-  floatx4 ent[EPT], ent2[LATE2 ? EPT : 1];
+  floatx4 ent[LGN][EPT];
 #pragma unroll
   for (int b = 0; b < ROUNDS; ++b) {
     if (b > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous round read
@@ -281,16 +287,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
 #pragma unroll
     for (int k = 0; k < EPR; ++k) {
       const int le = tid + THREADS * k;
-      constexpr int W1 = LATE2 ? WAVES / 2 : WAVES;  // waves of the first group
-      floatx4 sum = red[0][le / LIVE][le % LIVE];
+      constexpr int WP = WAVES / LGN;  // waves per part
 #pragma unroll
-      for (int wv2 = 1; wv2 < W1; ++wv2) sum += red[wv2][le / LIVE][le % LIVE];
-      ent[EPR * b + k] = sum;
-      if constexpr (LATE2) {
-        floatx4 sum2 = red[W1][le / LIVE][le % LIVE];
+      for (int j = 0; j < LGN; ++j) {
+        floatx4 sum = red[j * WP][le / LIVE][le % LIVE];
 #pragma unroll
-        for (int wv2 = W1 + 1; wv2 < WAVES; ++wv2) sum2 += red[wv2][le / LIVE][le % LIVE];
-        ent2[EPR * b + k] = sum2;
+        for (int wv2 = j * WP + 1; wv2 < (j + 1) * WP; ++wv2) sum += red[wv2][le / LIVE][le % LIVE];
+        ent[j][EPR * b + k] = sum;
       }
     }
   }
@@ -298,14 +301,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   if constexpr (LATE) {
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const float sc = (float)__builtin_bit_cast(_Float16, sraw[k]);
-      if constexpr (LATE2) {
-        const float sc2 = (float)__builtin_bit_cast(_Float16, sraw2[k]);
 #pragma unroll
-        for (int r = 0; r < RREG; ++r) ent[k][r] = ent[k][r] * sc + ent2[k][r] * sc2;
-      } else {
+      for (int r = 0; r < RREG; ++r) {
+        float v = ent[0][k][r] * (float)__builtin_bit_cast(_Float16, sraw[0][k]);
 #pragma unroll
-        for (int r = 0; r < RREG; ++r) ent[k][r] *= sc;
+        for (int j = 1; j < LG; ++j) v += ent[j][k][r] * (float)__builtin_bit_cast(_Float16, sraw[j][k]);
+        ent[0][k][r] = v;
       }
     }
   }
@@ -332,27 +333,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
 #pragma unroll
       for (int r = 0; r < RREG; ++r)
         if (r < nrow[k])
-          y[(int64_t)(row0[k] + r) * N + ncol[k]] = __builtin_bit_cast(uint16_t, (_Float16)(ent[k][r] + bb[k]));
+          y[(int64_t)(row0[k] + r) * N + ncol[k]] = __builtin_bit_cast(uint16_t, (_Float16)(ent[0][k][r] + bb[k]));
     return;
   }
   bool exc = false;
 #pragma unroll
   for (int k = 0; k < EPT; ++k)
 #pragma unroll
-    for (int r = 0; r < RREG; ++r) exc |= r < nrow[k] && !fx_normal(ent[k][r]);
+    for (int r = 0; r < RREG; ++r) exc |= r < nrow[k] && !fx_normal(ent[0][k][r]);
   if (__builtin_amdgcn_ballot_w64(exc) != 0) {  // rare: NaN, +-inf or huge partials
 #pragma unroll
     for (int k = 0; k < EPT; ++k)
 #pragma unroll
       for (int r = 0; r < RREG; ++r)
-        if (r < nrow[k] && !fx_normal(ent[k][r])) fx_side_add(side + e0[k] + r * LIVE, ent[k][r]);
+        if (r < nrow[k] && !fx_normal(ent[0][k][r])) fx_side_add(side + e0[k] + r * LIVE, ent[0][k][r]);
     fx_release();
   }
   uint64_t ret[EPT][RREG];
 #pragma unroll
   for (int k = 0; k < EPT; ++k)
 #pragma unroll
-    for (int r = 0; r < RREG; ++r) ret[k][r] = fx_add(accum + e0[k] + r * LIVE, r < nrow[k] ? fx_word(ent[k][r]) : 0ull);
+    for (int r = 0; r < RREG; ++r) ret[k][r] = fx_add(accum + e0[k] + r * LIVE, r < nrow[k] ? fx_word(ent[0][k][r]) : 0ull);
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
 #pragma unroll
@@ -377,20 +378,21 @@ hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_
   };
   auto by_shape = [&](auto mp) {
     constexpr int MP = decltype(mp)::value;
-    if (p.words != kDecodeWords) {  // half-width tiles: 4 waves
-      if (p.ks == 2) {
-        if (p.late == 2) go(decode_kernel<MP, 2, 4, true, true, true>, 256);
-        else p.late ? go(decode_kernel<MP, 2, 4, true, true>, 256) : go(decode_kernel<MP, 2, 4, false, true>, 256);
-      } else {
-        if (p.late == 2) go(decode_kernel<MP, 1, 4, true, true, true>, 256);
-        else p.late ? go(decode_kernel<MP, 1, 4, true, true>, 256) : go(decode_kernel<MP, 1, 4, false, true>, 256);
-      }
+    if (p.words != kDecodeWords) {  // half-width tiles: 4 waves, scaled after the reduction
+      auto by_lg = [&](auto ks) {
+        constexpr int KS = decltype(ks)::value;
+        if (p.late == 1) go(decode_kernel<MP, KS, 4, 1, true>, 256);
+        else if (p.late == 2) go(decode_kernel<MP, KS, 4, 2, true>, 256);
+        else go(decode_kernel<MP, KS, 4, 4, true>, 256);
+      };
+      if (p.ks == 2) by_lg(std::integral_constant<int, 2>{});
+      else by_lg(std::integral_constant<int, 1>{});
     } else if (p.waves == 8) {
-      if (p.ks == 2) p.late ? go(decode_kernel<MP, 2, 8, true>, 512) : go(decode_kernel<MP, 2, 8, false>, 512);
-      else p.late ? go(decode_kernel<MP, 1, 8, true>, 512) : go(decode_kernel<MP, 1, 8, false>, 512);
+      if (p.ks == 2) p.late ? go(decode_kernel<MP, 2, 8, 1>, 512) : go(decode_kernel<MP, 2, 8, 0>, 512);
+      else p.late ? go(decode_kernel<MP, 1, 8, 1>, 512) : go(decode_kernel<MP, 1, 8, 0>, 512);
     } else {
-      if (p.ks == 2) p.late ? go(decode_kernel<MP, 2, 4, true>, 256) : go(decode_kernel<MP, 2, 4, false>, 256);
-      else p.late ? go(decode_kernel<MP, 1, 4, true>, 256) : go(decode_kernel<MP, 1, 4, false>, 256);
+      if (p.ks == 2) p.late ? go(decode_kernel<MP, 2, 4, 1>, 256) : go(decode_kernel<MP, 2, 4, 0>, 256);
+      else p.late ? go(decode_kernel<MP, 1, 4, 1>, 256) : go(decode_kernel<MP, 1, 4, 0>, 256);
     }
   };
   if (p.mp == 1) by_shape(std::integral_constant<int, 1>{});

@@ -154,20 +154,19 @@ bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, DecodePlan& d) {
   auto ok = [&](int ks, int waves) {
     return (g == K || g % (kKStep * ks) == 0) && splits_of(ks, waves) <= kFxMaxSplits;
   };
-  // Half-width tiles (256 columns, 4 waves) whenever each half of a workgroup's waves
-  // stays inside one quantization group, so the sums are scaled after the wave reduction:
-  // two k-steps per wave when g is K or a multiple of 128, one when a multiple of 64.
+  // Half-width tiles (256 columns, 4 waves): two k-steps per wave when g is K or a
+  // multiple of 64, else one; the workgroup's waves then form 1, 2 or 4 parts that each
+  // lie in one quantization group, summed and scaled apart after the wave reduction.
   // Half the columns per workgroup halves the K splits for the same grid, and with them
   // the fixed-point adds and how many meet at each address.  Measured, us per call, full
-  // tiles -> half: 1 x 4096 x 4096 g128 6.38 -> 5.39, g64 6.88 -> 5.52; 2 x 4096 x 4096
-  // g128 8.00 -> 6.04; 1 x 4096 x 11008 g128 10.15 -> 8.33; 1 x 11008 x 4096 g-1 9.02 ->
-  // 8.25, g64 9.80 -> 9.10; 1 x 8192 x 28672 g128 35.9 -> 27.6.  Half tiles whose waves
-  // scale their own sums (g = 32, or g = 64 with two k-steps) measured slower (1 x 4096 x
-  // 4096 g32 6.86 -> 7.82; 1 x 11008 x 4096 g64 9.5 -> 11.5), so other layers keep full
-  // tiles: up to 128 k-steps one k-step per wave on 4 waves, longer K two k-steps per
-  // wave on 8 waves (11008 x 4096: 8.9 us against 9.7-12.8).
-  const int hks = (g == K || g % (4 * kKStep) == 0) ? 2 : (g % (2 * kKStep) == 0 ? 1 : 0);
-  if (hks > 0 && splits_of(hks, 4) <= kFxMaxSplits) {
+  // tiles -> half: 1 x 4096 x 4096 g128 6.38 -> 5.39, g64 6.88 -> 5.49, g32 6.97 -> 5.61;
+  // 2 x 4096 x 4096 g128 8.00 -> 6.04; 1 x 4096 x 11008 g128 10.15 -> 8.33; 1 x 11008 x
+  // 4096 g-1 9.02 -> 8.25, g32 11.18 -> 9.90; 2 x 11008 x 4096 g64 10.48 -> 9.42; 1 x 8192
+  // x 28672 g128 35.9 -> 27.6.  Beyond 127 splits, full tiles: two k-steps per wave on 8
+  // waves (one on 4 waves up to 128 k-steps), each wave scaling its own sums unless the
+  // workgroup lies in one group.
+  const int hks = (g == K || g % (2 * kKStep) == 0) ? 2 : 1;
+  if (splits_of(hks, 4) <= kFxMaxSplits) {
     d.words = kDecodeWords / 2;
     d.ks = hks;
     d.waves = 4;
@@ -186,9 +185,8 @@ bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, DecodePlan& d) {
   }
   d.n_tiles = (int)((N / 8 + d.words - 1) / d.words);
   d.splits = (int)splits_of(d.ks, d.waves);
-  d.late = (g == K || g % ((int64_t)kKStep * d.ks * d.waves) == 0) ? 1
-           : (d.words != kDecodeWords && g % ((int64_t)kKStep * d.ks * d.waves / 2) == 0) ? 2
-                                                                                         : 0;
+  const int64_t span = (int64_t)kKStep * d.ks * d.waves;
+  d.late = (g == K || g % span == 0) ? 1 : d.words == kDecodeWords ? 0 : (g % (span / 2) == 0 ? 2 : 4);
   return true;
 }
 

@@ -49,8 +49,8 @@ struct DecodePlan {
   int ks;       // k-steps per wave: 1 or 2
   int waves;    // waves per workgroup: 4 or 8
   int mp;       // rows: 1 or 2
-  int late;     // the workgroup's rows lie in one group (1) or two, one per half of its
-                // waves (2): scale after the wave reduction; 0: each wave scales its sums
+  int late;     // 1, 2 or 4: the workgroup's waves form that many equal parts, each in
+                // one group, scaled after the wave reduction; 0: each wave scales its sums
 };
 // MFMA tile family.  Variants (rows x columns per workgroup, threads):
 // 0: 256 x 128 (512: two k-groups of 4 waves), 1: 64 x 128 (256), 2: 32 x 128 (256).
