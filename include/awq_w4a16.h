@@ -131,7 +131,7 @@ int awq_dequant_f16(const int32_t* qweight, const int32_t* qzeros, const void* s
  *   y_f16       device fp16 [M, N], written in full
  * M == 0 returns AWQ_OK and enqueues nothing (GPTQModel wiki, "Native GEMM": empty
  * input launches no kernel).  Kernel families are chosen by M: bandwidth-bound
- * streaming kernels for small M (the decode family for one or two rows, the skinny
+ * streaming kernels for small M (the decode family for one to four rows, the skinny
  * family up to 16 rows and where the decode family's limits do not fit) and an MFMA
  * tile family above (awq_gemm_plan reports the choice).  In the tile family a partly filled last 256-row
  * tile that would take one more round of the compute units runs as a second launch

@@ -116,7 +116,9 @@ void check_gemm(int64_t M, int64_t K, int64_t N, int64_t gs, int cus, bool bf16)
   CHECK(p.accum_bytes >= 0 && p.partial_bytes >= 0);
   if (p.family == 2) {
     const DecodePlan& d = p.dp;
-    CHECK(!bf16 && M <= 2 && d.mp == M);
+    CHECK(!bf16 && M <= 4 && d.mp == (M <= 2 ? M : 4));
+    // three or four rows: grids of up to two rounds of three workgroups per CU, or N <= 8192
+    CHECK(M <= 2 || (N <= 32768 && (d.n_tiles * d.splits <= 1536 || N <= 8192)));
     CHECK(d.ks == 1 || d.ks == 2);
     CHECK(d.waves == 4 || d.waves == 8);
     CHECK(p.block == 64 * d.waves);
@@ -133,7 +135,7 @@ void check_gemm(int64_t M, int64_t K, int64_t N, int64_t gs, int cus, bool bf16)
     CHECK(d.n_tiles == cdiv(N / 8, d.words));
     CHECK(p.grid_x == d.n_tiles && p.grid_y == d.splits);
     CHECK(K * (N / 2) < k2p32 - 4096);
-    CHECK(p.accum_bytes == (d.splits > 1 ? (int64_t)d.n_tiles * 8 * d.words * M * 12 : 0));
+    CHECK(p.accum_bytes == (d.splits > 1 ? (int64_t)d.n_tiles * 8 * d.words * d.mp * 12 : 0));
     CHECK(p.partial_bytes == 0);
     check_grid(p.grid_x, p.grid_y, p.block);
   } else if (p.family == 0) {

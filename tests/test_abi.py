@@ -96,7 +96,10 @@ def test_plan_families():
     p16 = awq.plan(16, 4096, 11008, 128)
     assert p16["family"] == "skinny"
     assert awq.plan(2, 4096, 4096, 128)["family"] == "decode"
-    assert awq.plan(3, 4096, 4096, 128)["family"] == "skinny"
+    assert awq.plan(4, 4096, 4096, 128)["family"] == "decode"
+    assert awq.plan(5, 4096, 4096, 128)["family"] == "skinny"
+    assert awq.plan(3, 8192, 16384, 128)["family"] == "skinny"   # wide and large: the skinny family
+    assert awq.plan(4, 28672, 8192, 128)["family"] == "decode"
     # 256-column tiles: two k-steps per wave for g = 64, one for g = 32; past 127 splits
     # of those, 512-column tiles with two k-steps per wave on eight waves; beyond the
     # split limit (127) the older skinny family takes small M.

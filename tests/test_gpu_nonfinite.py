@@ -63,7 +63,8 @@ def compare(y, yref, label):
 SHAPES = [  # (M, K, N, g, family): reaching each reduction path
     (1, 4096, 512, 128, "decode"),
     (2, 4096, 544, 64, "decode"),      # partial last 512-column tile
-    (3, 2048, 512, 128, "skinny"),     # fp32 partials and the reduce kernel
+    (3, 2048, 512, 128, "decode"),     # three rows, four kept per lane: fixed point with side words
+    (5, 2048, 512, 128, "skinny"),     # fp32 partials and the reduce kernel
     (16, 4096, 512, -1, "skinny"),
     (1, 131072, 64, -1, "skinny"),     # beyond the decode family's split limit: fixed point, one group per wave
     (2, 98304, 128, 64, "skinny"),     # the same with waves over several groups (LDS tables)

@@ -111,6 +111,9 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (1, 3072, 544, 96, True),    # decode, one k-step per wave, each wave's sums scaled apart
     (2, 2048, 800, 32, True),    # the same with g = 32
     (1, 40960, 96, 64, True),    # decode past 127 half-width splits: 512-column tiles, 8 waves
+    (3, 3072, 544, 384, True),   # decode, three rows (four kept), two groups per workgroup
+    (4, 2048, 800, 32, False),   # decode, four rows, each wave's sums scaled apart
+    (4, 40960, 96, 64, True),    # decode, four rows on 512-column tiles
 ]
 
 

@@ -1,4 +1,4 @@
-// Decode family of awq_gemm (fp16 activations, 1 <= M <= 2): bandwidth-bound streaming
+// Decode family of awq_gemm (fp16 activations, 1 <= M <= 4): bandwidth-bound streaming
 // of the packed weight.
 //
 // What it computes: y[m, n] = sum_k x[m, k] * (q[k, n] - z[k/g, n]) * s[k/g, n] + bias[n]
@@ -396,7 +396,8 @@ hipError_t launch_decode(const uint16_t* x, const int32_t* qweight, const int32_
     }
   };
   if (p.mp == 1) by_shape(std::integral_constant<int, 1>{});
-  else by_shape(std::integral_constant<int, 2>{});
+  else if (p.mp == 2) by_shape(std::integral_constant<int, 2>{});
+  else by_shape(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 

@@ -142,14 +142,13 @@ bool plan_skinny(int64_t M, int64_t K, int64_t N, int64_t g, int cus, SkinnyPlan
 // format, and qweight stays below 4 GiB (32-bit buffer offsets).  One workgroup per
 // (512-column tile, K split) of waves * ks k-steps.
 bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, DecodePlan& d) {
-  // One or two rows: the returning fixed-point adds (M x N x splits of them) stay cheap.
-  // From three rows they cost more than the older skinny family's fp32 partials (M = 16
-  // on 4096 x 11008: 27.6 us at best against 13.9; M = 8 on 11008 x 4096: 17.2 against
-  // 12.9), which keeps those.
+  // Up to four rows: the returning fixed-point adds (M x N x splits of them) stay cheap
+  // enough.  From five rows they cost more than the skinny family's fp32 partials (M = 8
+  // on 11008 x 4096: 15.6 / 17.9 us for g-1 / g64 against 12.3 / 14.2), which keeps those.
   if (M < 1 || M > kDecodeMaxM) return false;
   if (K * (N / 2) >= (int64_t(1) << 32) - 4096) return false;
   const int64_t T = K / kKStep;
-  d.mp = (int)M;
+  d.mp = M <= 2 ? (int)M : 4;
   auto splits_of = [&](int ks, int waves) { return (T + (int64_t)ks * waves - 1) / ((int64_t)ks * waves); };
   auto ok = [&](int ks, int waves) {
     return (g == K || g % (kKStep * ks) == 0) && splits_of(ks, waves) <= kFxMaxSplits;
@@ -185,6 +184,17 @@ bool plan_decode(int64_t M, int64_t K, int64_t N, int64_t g, DecodePlan& d) {
   }
   d.n_tiles = (int)((N / 8 + d.words - 1) / d.words);
   d.splits = (int)splits_of(d.ks, d.waves);
+  // Three or four rows: only while the grid stays within two rounds of three workgroups
+  // per CU (1536 workgroups) or N <= 8192, and N <= 32768 (the adds' words stay under
+  // 1.5 MB).  Measured against the skinny family, us per call: 3 x 2048 x 4096 8.90 ->
+  // 5.91, 3 x 4096 x 4096 9.49 -> 6.95, 4 x 4096 x 4096 9.36 -> 7.39, 4 x 11008 x 4096
+  // g64 13.68 -> 10.93, 4 x 4096 x 22016 17.46 -> 16.01, 4 x 28672 x 8192 35.8 -> 32.9;
+  // kept on the skinny family: 3 x 8192 x 16384 20.5 (21.2 here), 4 x 8192 x 28672 32.3
+  // (34.6), 3 x 4096 x 114688 56.0 (60.1).
+  if (M > 2) {
+    const int64_t grid = (int64_t)d.n_tiles * d.splits;
+    if (N > 32768 || (grid > 1536 && N > 8192)) return false;
+  }
   const int64_t span = (int64_t)kKStep * d.ks * d.waves;
   d.late = (g == K || g % span == 0) ? 1 : d.words == kDecodeWords ? 0 : (g % (span / 2) == 0 ? 2 : 4);
   return true;

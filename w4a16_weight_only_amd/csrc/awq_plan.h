@@ -34,21 +34,21 @@ struct SkinnyPlan {
   bool fused;        // fp32 partials summed by each tile's last workgroup (else a reduce kernel)
 };
 
-// Decode family (fp16 activations, 1 <= M <= 2): a workgroup of `waves` waves owns a
+// Decode family (fp16 activations, 1 <= M <= 4): a workgroup of `waves` waves owns a
 // column tile of `words` packed word-columns (64: 512 output columns, 256 contiguous
 // bytes of a row; 32: 256 columns, 128 bytes, 4 waves only) and waves * ks k-steps of 32
 // rows, all of one wave's ks k-steps in one quantization group.  The K splits meet in
 // fixed-point accumulators: n_tiles * 8 * words * mp 64-bit words, then as many float
 // side words, zero before the call and left zero by it.
 constexpr int kDecodeWords = 64;
-constexpr int kDecodeMaxM = 2;
+constexpr int kDecodeMaxM = 4;
 struct DecodePlan {
   int n_tiles;  // column tiles of 8 * words columns
   int words;    // packed word-columns per tile: 64, or 32 (half-width tiles)
   int splits;   // K splits (grid y), at most kFxMaxSplits
   int ks;       // k-steps per wave: 1 or 2
   int waves;    // waves per workgroup: 4 or 8
-  int mp;       // rows: 1 or 2
+  int mp;       // rows kept: 1, 2 or 4 (three rows padded to 4)
   int late;     // 1, 2 or 4: the workgroup's waves form that many equal parts, each in
                 // one group, scaled after the wave reduction; 0: each wave scales its sums
 };
