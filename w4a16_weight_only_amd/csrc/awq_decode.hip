@@ -30,10 +30,11 @@
 //   by s in fp32, so the weight is never rounded.
 // HALF tiles: lane l takes chunk l % 8 of the 128-byte segment and only nibble half
 // (l / 8) % 2 of each byte, so MFMA column l % 16 is (nibble half, chunk) and a k-step is
-// 16 MFMAs; the two lanes of a chunk load the same 16 bytes.
-// Reduction: the waves' sums meet in LDS (in rounds of 32 KB), each thread sums a few
-// (row block, column) entries over the waves in wave order, then adds them to the
-// fixed-point words.
+// 16 MFMAs.  Lanes l and l ^ 8 load the two rows of each row pair (every 16-byte chunk is
+// loaded once) and trade words with a DPP row rotation, so each holds both rows.
+// Reduction: the waves' sums meet in LDS (only the live rows of each MFMA entry, in
+// rounds), each thread sums a few (row block, column) entries over the waves in wave
+// order, then adds them to the fixed-point words.
 #include <type_traits>
 
 #include "awq_device.h"
@@ -42,6 +43,8 @@
 namespace awq {
 
 namespace {
+
+constexpr int kDppRowRor8 = 0x128;  // DPP row_ror:8: lane l reads lane l ^ 8 of its 16-lane row
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -76,8 +79,8 @@ __device__ __forceinline__ uint32_t splat_byte(uint32_t b) {
 // 2-byte scales per output entry).
 // HALF: a column tile of 32 word-columns (256 outputs, 128 bytes of a row): lane l
 // takes chunk c = l % 8 and nibble half h = (l / 8) % 2 of every byte (MFMA column
-// l % 16 is the pair (h, c)), the lanes of both halves load the same 16 bytes, and a
-// k-step is 16 MFMAs (word w, byte t) instead of 32.  Half the columns per workgroup
+// l % 16 is the pair (h, c)), the two lanes of a chunk load one row each of every row
+// pair and trade words, and a k-step is 16 MFMAs (word w, byte t) instead of 32.  Half the columns per workgroup
 // means half the K splits for the same grid, so half the fixed-point adds, and half
 // as many of them meet at each address.
 template <int MP, int KS, int WAVES, int LG, bool HALF = false>
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   constexpr int EPR = PAIRS / THREADS;   // reduced pairs per thread and round
   constexpr int EPT = EPR * ROUNDS;      // reduced pairs per thread
   static_assert(PAIRS == COLS && EPR * THREADS == PAIRS, "one round is one (entry, lane) pair per column");
-  __shared__ floatx4 red[WAVES][VR][LIVE];
+  __shared__ float red[WAVES][VR][LIVE][RREG];  // only the live rows of each entry
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,14 +138,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   const uint32_t row_bytes = (uint32_t)NW * 4u;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(qweight), (short)0, (int)(row_bytes * (uint32_t)K), 0x00020000);
-  const uint32_t voff = ((uint32_t)(8 * q) * (uint32_t)NW + (uint32_t)wc) * 4u;
-  u32x4 wv[KS][8];
+  // Full tiles: rows 8q + j, j = 0..7.  HALF: rows 8q + 2j + hsel, j = 0..3 (lanes l and
+  // l ^ 8 take the two rows of each pair; every 16-byte chunk is loaded once).
+  constexpr int LPS = HALF ? 4 : 8;  // weight loads per lane and k-step
+  const uint32_t voff = ((uint32_t)(8 * q + hsel) * (uint32_t)NW + (uint32_t)wc) * 4u;
+  u32x4 wv[KS][LPS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const uint32_t r0 = (uint32_t)min(kb + s, T - 1) * kKStep;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wv[s][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voff, (r0 + j) * row_bytes, 2));
+    for (int j = 0; j < LPS; ++j)
+      wv[s][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voff, (r0 + (HALF ? 2 * j : j)) * row_bytes, 2));
   }
   // Scales of the lane's 32 columns (8 wc .. 8 wc + 31), when each wave scales its own sums.
   constexpr bool LATE = LG > 0;
@@ -178,6 +185,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   }
   // Every load is issued before any arithmetic waits on one.
   __builtin_amdgcn_sched_barrier(0);
+  // The kernel arguments past the preloaded ones are fetched here, under the loads, not
+  // when the split sum first needs them.
+  asm volatile("" ::"s"(splits), "s"(accum), "s"(side), "s"(y));
 
   // ---- Zero splats of the group: entry v = 8 w + 2 t + h holds -(1024 + z) (h = 0) or
   // -(64 + z) (h = 1) in both fp16 halves.
@@ -188,6 +198,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
   const uint32_t hmask = hsel ? uk.mhi : uk.mlo;           // HALF: the lane's nibble mask
   const uint32_t zneg_h = hsel ? zneg_hi : zneg_lo;
   const half2v hmult = hsel ? half2v{(_Float16)0.0625f, (_Float16)0.0625f} : half2v{(_Float16)1.f, (_Float16)1.f};
+  // HALF: v_perm_b32 selectors that put byte t of row 8q + 2j in the low half and of row
+  // 8q + 2j + 1 in the high half, from (the partner lane's word, this lane's word): the
+  // lane holding the odd row takes the even row from its partner.
+  const uint32_t psel0 = 0x0C000C00u | (hsel ? 0x00000004u : 0x00040000u);
   uint32_t zs[HALF ? 16 : 32];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -221,6 +235,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
         // A k-step past K (the last split's idle waves) multiplies zeros: (q - z) is finite.
         const half8v as = s < nks ? a[s] : half8v{};
         const half4v ah = half4v{as[4 * hh], as[4 * hh + 1], as[4 * hh + 2], as[4 * hh + 3]};
+        // HALF: the partner lane's (l ^ 8) words of this half's two row pairs.
+        uint32_t oth[2][4];
+        if constexpr (HALF) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              oth[p][w] = (uint32_t)__builtin_amdgcn_mov_dpp((int)wv[s][2 * hh + p][w], kDppRowRor8, 0xF, 0xF, false);
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
 #pragma unroll
@@ -228,12 +251,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
             uint32_t lo[2], hi[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const uint32_t ra = wv[s][4 * hh + 2 * p][w], rb = wv[s][4 * hh + 2 * p + 1][w];
               uint32_t pb;
-              if (t == 0) pb = pair_byte<0>(ra, rb);
-              else if (t == 1) pb = pair_byte<1>(ra, rb);
-              else if (t == 2) pb = pair_byte<2>(ra, rb);
-              else pb = pair_byte<3>(ra, rb);
+              if constexpr (HALF) {
+                pb = __builtin_amdgcn_perm(oth[p][w], wv[s][2 * hh + p][w], psel0 + 0x00010001u * (uint32_t)t);
+              } else {
+                const uint32_t ra = wv[s][4 * hh + 2 * p][w], rb = wv[s][4 * hh + 2 * p + 1][w];
+                if (t == 0) pb = pair_byte<0>(ra, rb);
+                else if (t == 1) pb = pair_byte<1>(ra, rb);
+                else if (t == 2) pb = pair_byte<2>(ra, rb);
+                else pb = pair_byte<3>(ra, rb);
+              }
               if constexpr (HALF) {
                 lo[p] = as_u32(__builtin_elementwise_fma(as_h2((pb & hmask) | uk.magic), hmult, as_h2(zs[4 * w + t])));
               } else {
@@ -281,7 +308,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
     if (b > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous round read
     if (lane < LIVE) {
 #pragma unroll
-      for (int vl = 0; vl < VR; ++vl) red[wave][vl][lane] = acc[b * VR + vl];
+      for (int vl = 0; vl < VR; ++vl)
+#pragma unroll
+        for (int r = 0; r < RREG; ++r) red[wave][vl][lane][r] = acc[b * VR + vl][r];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
@@ -290,9 +319,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void decode_kernel(const uin
       constexpr int WP = WAVES / LGN;  // waves per part
 #pragma unroll
       for (int j = 0; j < LGN; ++j) {
-        floatx4 sum = red[j * WP][le / LIVE][le % LIVE];
+        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int wv2 = j * WP + 1; wv2 < (j + 1) * WP; ++wv2) sum += red[wv2][le / LIVE][le % LIVE];
+        for (int wv2 = j * WP; wv2 < (j + 1) * WP; ++wv2)
+#pragma unroll
+          for (int r = 0; r < RREG; ++r) sum[r] += red[wv2][le / LIVE][le % LIVE][r];
         ent[j][EPR * b + k] = sum;
       }
     }
