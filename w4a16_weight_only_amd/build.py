@@ -50,9 +50,13 @@ COMPILE_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The decode kernel is short enough that fetching its arguments
-# from memory shows up in every call: have the dispatcher preload them into SGPRs.
-EXTRA_FLAGS = {"awq_decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# Per-source extra flags.  Have the dispatcher preload kernel arguments into SGPRs: a
+# scalar load of an argument from memory is a cache miss at the start of every call (two
+# in a row where a branch on the first guards the second), which shows in the short
+# kernels (decode, skinny, the split-sum kernels): up_proj 16x4096x11008 12.98 -> 12.76 us,
+# down_proj 8x11008x4096 g64 14.50 -> 14.09 us.
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+EXTRA_FLAGS = {"awq_decode.hip": _PRELOAD, "awq_skinny.hip": _PRELOAD, "awq_tile.hip": _PRELOAD}
 
 
 def _run(cmd):
