@@ -237,7 +237,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   constexpr int DPW = IPW + XPW;               // direct loads per wave per k-tile
   const char* wb = reinterpret_cast<const char*>(qweight);
   const char* sb = reinterpret_cast<const char*>(scales);
-  const int64_t to_z = reinterpret_cast<const char*>(qzeros) - sb;
   // Weight load: lane l covers row l / NG of the load's RPI rows and position l % NG,
   // which holds word group (l % NG) ^ swz(row).
   auto swz = [](int r) { return ((r >> 3) & 1) * (NG / 2); };
@@ -256,6 +255,16 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const int g_lane = lane < 2 * GP ? lane : 0;
   const int g_half = g_lane < GP ? 0 : 1;
   const int g_u = g_lane - g_half * GP;
+  // The piece of group gi sits at g_base + gi * g_stride: four zero words of a qzeros
+  // row (NW words long) or eight scales of a scales row (N halves long).
+  const bool g_zero = g_u < ZP;
+  const char* g_base = g_zero ? reinterpret_cast<const char*>(qzeros) + 4 * (int64_t)min(wc0 + 4 * g_u, NW - 4)
+                              : sb + 2 * (int64_t)min(n0 + 8 * (g_u - ZP), N - 8);
+  const uint32_t g_stride = g_zero ? 4u * (uint32_t)NW : 2u * (uint32_t)N;
+  // Group of the 32-row block u: floor(u / gk), gk = g / 32, as floor((u + 0.5) * (1 / gk))
+  // in fp32.  (u + 0.5) / gk lies at least 0.5 / gk from an integer; for u < 2^19 (K <=
+  // 2^24) the two roundings move it by less than 2^-4 / gk, so the floor is exact.
+  const float g_rcp = 1.0f / (float)(g >> 5);
   // First row loaded for the k-tile starting at k0 (see above).
   auto tile_row = [&](int k0) { return (K - k0 < kBK && K >= kBK) ? k0 - kBK / 2 : k0; };
   auto load_tile = [&](int buf, int k0) {
@@ -271,13 +280,9 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
       } else if (e == NB) {
         // Groups of the two 32-row halves; g is a multiple of 32, so a group boundary
         // inside the k-tile can only fall between the halves.
-        const int gi = min(kl + g_half * (kBK / 2), K - 1) / g;
-        // Blended operands (z = 0 / 1) rather than selected pointers; offsets from the
-        // scales pointer keep the address a global one.
-        const int64_t z = g_u < ZP;
-        const int64_t zcol = min(wc0 + 4 * g_u, NW - 4), scol = min(n0 + 8 * (g_u - ZP), N - 8);
-        const int64_t zoff = ((int64_t)gi * NW + zcol) << 2, soff = ((int64_t)gi * N + scol) << 1;
-        load_lds16(sb + (soff + z * (zoff + to_z - soff)), &Gs[buf][0]);
+        const uint32_t u = (uint32_t)min(kl + g_half * (kBK / 2), K - 1) >> 5;
+        const uint32_t gi = (uint32_t)(((float)u + 0.5f) * g_rcp);
+        load_lds16(g_base + (uint64_t)gi * g_stride, &Gs[buf][0]);
       } else {
         load_lds16_s(xb + ((int64_t)a_row0[0] * K + kl) * 2, a_off[0], &stg.sink[0]);
       }
