@@ -18,6 +18,10 @@
 // straight into LDS (global_load_lds_dwordx4, no register round trip), kStages - 1
 // k-tiles ahead of the multiply; layouts are XOR-swizzled so that both the direct
 // loads and the fragment reads are conflict-free.
+// k loop: software-pipelined (the B operand of the next k16 step dequantised while the
+// MFMAs of the current one run, across the k-tile barrier too) for the 256-row and the
+// 32-row tiles; the 64-row tiles, two workgroups per CU whose waves already overlap
+// each other, go step by step (pipelining them measured 2-4% slower).
 // B operand, dequantised in registers: in a 32x32x16 B operand lane l supplies 8
 // consecutive k of column n = l % 32.  A wave's 32 FN columns are its packed word
 // columns x nibble positions: lane l takes word column l % 8 (FN = 2) or l % 4
@@ -514,7 +518,81 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     };
     for (int kt = 0; kt < KT - 1; ++kt) body(kt, true);
     body(KT - 1, keep_of(KT - 1));
+  } else if constexpr (FM == 1) {
+    // 32-row tiles: a software-pipelined k loop of one k-group (four k16 steps per k-tile, both halves):
+    // the B operand of step s + 1 is read and dequantised while the MFMAs of step s run,
+    // and the barrier sits before the last step of a k-tile, whose MFMAs overlap the
+    // dequant of the next k-tile's first step (the buffer a barrier releases only has to
+    // stay intact until its fragments are in registers).  Steps of the unused half of a
+    // partial last k-tile are read and dequantised but not multiplied; after the last
+    // k-tile the reads of "k-tile KT" hit the clamped re-load of the last one (valid
+    // data) and what is dequantised from them is never multiplied.
+    auto part_of = [&](int t) { return kt0 + t == KT_all - 1 && K % kBK != 0; };
+    auto mul_of = [&](int t, int st) { return !part_of(t) || (st >> 1) == part_half; };
+    auto dequant1 = [&](const Frag& f, half8v(&bf)[2]) {
+      const uint32_t w[8] = {f.wlo[0], f.wlo[1], f.wlo[2], f.wlo[3], f.whi[0], f.whi[1], f.whi[2], f.whi[3]};
+      u32x4 b0w, b1w;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t pb = __builtin_amdgcn_perm(w[2 * pr + 1], w[2 * pr], sel);
+        b0w[pr] = b_pair<BF16>((pb & mask) | uk.magic, mult, off0, sc0);
+        if constexpr (FN == 2) b1w[pr] = b_pair<BF16>(((pb >> 8) & mask) | uk.magic, mult, off1, sc1);
+      }
+      bf[0] = __builtin_bit_cast(half8v, b0w);
+      if constexpr (FN == 2) bf[1] = __builtin_bit_cast(half8v, b1w);
+    };
+    auto mfma1 = [&](const Frag& f, const half8v(&bf)[2]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma32<BF16>(f.a[i], bf[j], acc[i][j]);
+      }
+    };
+    // One MFMA, then a share of the dequant's VALU instructions, FM * FN times.
+    auto interleave1 = [] {
+#pragma unroll
+      for (int i = 0; i < FM * FN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 20 / (FM * FN), 0);  // VALU
+      }
+    };
+    // Step st (0..3) of buffer buf: fragments f; half st / 2's group data.
+    auto read_step = [&](Frag& f, int buf, int st) { read_frag(f, buf, st & 1, st >> 1); };
+    Frag fa, fb;
+    half8v ba[2], bb[2];
+    read_step(fa, 0, 0);
+    apply_group(0, 0, true);
+    dequant1(fa, ba);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt % kStages, nbuf = (kt + 1) % kStages;
+      load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
+      // step 0 (fa, ba) | dequant step 1 -> (fb, bb)
+      read_step(fb, buf, 1);
+      if (mul_of(kt, 0)) mfma1(fa, ba);
+      dequant1(fb, bb);
+      interleave1();
+      // step 1 (fb, bb) | dequant step 2 -> (fa, ba), with half 1's group data
+      read_step(fa, buf, 2);
+      if (mul_of(kt, 1)) mfma1(fb, bb);
+      apply_group(buf, 1, true);
+      dequant1(fa, ba);
+      interleave1();
+      // step 2 (fa, ba) | dequant step 3 -> (fb, bb)
+      read_step(fb, buf, 3);
+      if (mul_of(kt, 2)) mfma1(fa, ba);
+      dequant1(fb, bb);
+      interleave1();
+      barrier_keep_last();
+      // step 3 (fb, bb) | dequant step 0 of k-tile kt + 1 -> (fa, ba)
+      read_step(fa, nbuf, 0);
+      if (mul_of(kt, 3)) mfma1(fb, bb);
+      apply_group(nbuf, 0, true);
+      dequant1(fa, ba);
+      interleave1();
+    }
   } else {
+    // 64-row tiles (two workgroups per CU, whose waves overlap each other): step by step.
     for (int kt = 0; kt < KT; ++kt) {
       load_tile((kt + kStages - 1) % kStages, kofs(kt + kStages - 1));
       run(kt % kStages, kt0 + kt == KT_all - 1 && K % kBK != 0);
