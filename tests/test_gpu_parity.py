@@ -114,6 +114,13 @@ RAGGED = [  # (M, K, N, g, bias): tails in M, N and in the K split
     (3, 3072, 544, 384, True),   # decode, three rows (four kept), two groups per workgroup
     (4, 2048, 800, 32, False),   # decode, four rows, each wave's sums scaled apart
     (4, 40960, 96, 64, True),    # decode, four rows on 512-column tiles
+    (4, 2048, 544, -1, True),    # decode, four rows, one group: the workgroup scaled once
+    (3, 3072, 800, 64, False),   # decode, three rows, each wave's group scaled apart (4 parts)
+    (1, 40960, 96, -1, True),    # decode, 512-column tiles in one group (scaled once)
+    (1, 20480, 64, 160, True),   # decode, 512-column tiles of one k-step per wave on 8 waves
+    (2, 20480, 64, 160, False),  # the same, two rows
+    (4, 20480, 64, 160, True),   # the same, four rows
+    (2, 40960, 96, -1, False),   # decode, two rows on 512-column tiles in one group
 ]
 
 
