@@ -310,7 +310,15 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   const half2v mult = hi_nib ? half2v{(_Float16)0.0625f, (_Float16)0.0625f} : half2v{(_Float16)1.f, (_Float16)1.f};
   const int c0 = 8 * wloc + order_of(p0);      // column within the workgroup tile, N-tile 0
   const int c1 = 8 * wloc + order_of(p0 + 4);  // N-tile 1 (FN = 2)
-  const _Float16 zbase = hi_nib ? (_Float16)64.f : (_Float16)1024.f;
+  // -(1024 + z) (low nibble) and -(64 + z) (high nibble) as fp16 bit patterns: 1024 + z
+  // and 64 + z (z <= 15) are exact, with z in the low mantissa bits (ulp 1) or above them
+  // (ulp 1/16).
+  const uint32_t zpat = hi_nib ? 0xD400u : 0xE400u;
+  const uint32_t zsh = hi_nib ? 4u : 0u;
+  auto zsplat = [&](uint32_t z) {
+    const uint32_t h = zpat | (z << zsh);
+    return __builtin_bit_cast(half2v, h | (h << 16));
+  };
 
   half2v off0, off1, sc0, sc1;
   // Group data of half h of k-tile buf.  keep = false zeroes the scales (the unused half
@@ -321,11 +329,11 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint32_t zw = gz[wloc];
     // Loads first, then a select: a conditional load would split the loop body.
     const _Float16 s0v = gs[c0];
-    off0 = splat(-(zbase + (_Float16)(float)((zw >> (4 * p0)) & 0xFu)));
+    off0 = zsplat((zw >> (4 * p0)) & 0xFu);
     sc0 = splat(keep ? s0v : (_Float16)0.f);
     if (FN == 2) {
       const _Float16 s1v = gs[c1];
-      off1 = splat(-(zbase + (_Float16)(float)((zw >> (4 * (p0 + 4))) & 0xFu)));
+      off1 = zsplat((zw >> (4 * (p0 + 4))) & 0xFu);
       sc1 = splat(keep ? s1v : (_Float16)0.f);
     }
   };
