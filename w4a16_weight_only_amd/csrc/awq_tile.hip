@@ -650,10 +650,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // c0, c0 + 1).
   if (partial != nullptr) {
     // Split K: this split's fp32 sums, no bias, to partial[split][M][N]; rows >= M
-    // and columns >= N are not stored.  Written through past the XCD's L2 (agent-scope
-    // stores, sc1): the partials are read once, by the split-sum kernel on every XCD, so
-    // keeping them dirty in this XCD's L2 buys nothing (measured: M = 64 on 11008 x
-    // 4096 23.2 -> 22.2 us per call, M = 512 g64 61.5 -> 60.2).
+    // and columns >= N are not stored.
     float* pout = partial + (int64_t)blockIdx.y * M * N;
     const int n = n0 + c0;
     if (owner && n < N) {
@@ -666,8 +663,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
             if (FN == 2)
               *reinterpret_cast<floatx2*>(&pout[(int64_t)row * N + n]) = floatx2{acc[i][0][r], acc[i][FN - 1][r]};
             else
-              __hip_atomic_store(&pout[(int64_t)row * N + n], acc[i][0][r], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+              pout[(int64_t)row * N + n] = acc[i][0][r];
           }
         }
     }
