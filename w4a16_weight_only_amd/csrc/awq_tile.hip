@@ -650,7 +650,11 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   // c0, c0 + 1).
   if (partial != nullptr) {
     // Split K: this split's fp32 sums, no bias, to partial[split][M][N]; rows >= M
-    // and columns >= N are not stored.
+    // and columns >= N are not stored.  Written through past the XCD's L2 (agent-scope
+    // stores, sc1): the split-sum kernel reads each partial once, from any XCD, so
+    // keeping it dirty in this XCD's L2 buys nothing (measured: M = 512 on 11008 x 4096
+    // g64 61.5 -> 60.2 and 63.1 -> 60.9 us per call on two boxes; M = 64 23.2 -> 22.2
+    // on one, unchanged on the other).
     float* pout = partial + (int64_t)blockIdx.y * M * N;
     const int n = n0 + c0;
     if (owner && n < N) {
@@ -663,7 +667,8 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
             if (FN == 2)
               *reinterpret_cast<floatx2*>(&pout[(int64_t)row * N + n]) = floatx2{acc[i][0][r], acc[i][FN - 1][r]};
             else
-              pout[(int64_t)row * N + n] = acc[i][0][r];
+              __hip_atomic_store(&pout[(int64_t)row * N + n], acc[i][0][r], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
           }
         }
     }
