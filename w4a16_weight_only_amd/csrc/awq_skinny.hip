@@ -440,6 +440,22 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     __syncthreads();  // the tables are dead; their LDS becomes the reduction buffer
   }
 
+  // Output column of a slot.
+  auto slot_n = [&](int s) {
+    const int sv = (s >> 4) & 15, sc = s & 15;
+    return tile * kSkinnyCols + 8 * (2 * sc + (sv >> 3)) + tab_col(sv);
+  };
+  constexpr int SLOTS = 1024 / THREADS;  // slots per thread when all 16 rows are live
+  // The bias of this thread's slots, requested now so that it arrives under the wave
+  // reduction: each epilogue below would otherwise wait for it after its own memory round
+  // trip (partials or fixed-point adds).  Without a bias the loads read x and are unused.
+  uint16_t braw[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    const int n = slot_n(tid + k * THREADS);
+    braw[k] = (bias != nullptr ? bias : x)[bias != nullptr ? min(n, N - 1) : 0];
+  }
+
   // 2. Waves -> LDS in register order, then sums over waves per slot.  Only the
   // lanes q < MROWS / 4 (rows 0 .. MROWS - 1) hold rows that are ever stored.
   if (q < MROWS / 4) {
@@ -451,7 +467,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
   // Slots in q-major order so that M <= 4 touches only q = 0 (one slot per thread).
   const int rows = M < MROWS ? M : MROWS;
   const int nslots = 256 * ((rows + 3) / 4);
-  constexpr int SLOTS = 1024 / THREADS;  // slots per thread when all 16 rows are live
   floatx4 sum[SLOTS];
 #pragma unroll
   for (int k = 0; k < SLOTS; ++k) {
@@ -462,19 +477,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       for (int wv = 0; wv < WAVES; ++wv) sum[k] += sh.u.red[wv][(s >> 4) & 15][(s >> 8) * 16 + (s & 15)];
     }
   }
-  // Output column of a slot.
-  auto slot_n = [&](int s) {
-    const int sv = (s >> 4) & 15, sc = s & 15;
-    return tile * kSkinnyCols + 8 * (2 * sc + (sv >> 3)) + tab_col(sv);
-  };
-
   if (splits == 1) {
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int s = tid + k * THREADS;
       const int n = slot_n(s);
       if (s < nslots && n < N) {
-        const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
+        const float b = bias ? act_to_float<BF16>(braw[k]) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * (s >> 8) + i;
@@ -563,7 +572,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
           const int sv = (s >> 4) & 15, sc = s & 15;
           const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
           const int n = tile * kSkinnyCols + ct;
-          const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
+          const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(braw[k]) : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) sh.u.ys[4 * (s >> 8) + i][ct] = float_to_act<BF16>(tot[k][i] + b);
         }
@@ -630,7 +639,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
       const int row = 4 * (s >> 8) + i;
       const FxSum fs = fx_decode(ret[i]);
       if (n < N && row < rows && fs.arrivals == (uint32_t)splits) {
-        const float b = bias ? act_to_float<BF16>(bias[n]) : 0.f;
+        const float b = bias ? act_to_float<BF16>(braw[k]) : 0.f;
         const float v = fx_total(fs, tile_side + 4 * s + i) + b;
         fx_clear(tile_acc + 4 * s + i);
         put(row, n, v);
@@ -668,11 +677,16 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   if (4 * q >= M) return;  // whole workgroup: rows beyond M
   const int t = threadIdx.x;
   const int slot = q * 256 + t;
-  const floatx4 a = sum_splits<B>(partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot, TILE_ENTRIES, splits);
   const int sv = (t >> 4) & 15, sc = t & 15;
   const int ct = 8 * (2 * sc + (sv >> 3)) + tab_col(sv);  // column within the tile
   const int n = tile * kSkinnyCols + ct;
-  const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
+  // The bias is requested first, so that it arrives with the partials: one memory round
+  // trip, not two (without a bias the load reads the first partial and is not used).
+  const uint16_t* bsrc = bias != nullptr ? bias : reinterpret_cast<const uint16_t*>(partial);
+  const uint16_t braw = bsrc[bias != nullptr ? min(n, N - 1) : 0];
+  __builtin_amdgcn_sched_barrier(0);
+  const floatx4 a = sum_splits<B>(partial + (int64_t)block * splits * TILE_ENTRIES + 4 * slot, TILE_ENTRIES, splits);
+  const float b = (bias != nullptr && n < N) ? act_to_float<BF16>(braw) : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) ys[i][ct] = float_to_act<BF16>(a[i] + b);
   __syncthreads();

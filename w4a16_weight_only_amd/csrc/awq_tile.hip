@@ -320,6 +320,16 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     return __builtin_bit_cast(half2v, h | (h << 16));
   };
 
+  // Bias of this lane's output column(s) for the unsplit epilogue, requested before the k
+  // loop (the epilogue would otherwise wait a memory round trip for it after the last
+  // k-tile).  Without a bias, or with split partials, the loads read x and are unused.
+  uint16_t braw[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const bool use = bias != nullptr && partial == nullptr;
+    braw[j] = (use ? bias : x)[use ? min(n0 + (j == 0 ? c0 : c1), N - 1) : 0];
+  }
+
   half2v off0, off1, sc0, sc1;
   // Group data of half h of k-tile buf.  keep = false zeroes the scales (the unused half
   // of a partial last k-tile, whose MFMAs are skipped anyway).
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + (j == 0 ? c0 : c1);
-      bj[j] = (bias != nullptr && n < N) ? act_to_float<BF16>(bias[n]) : 0.f;
+      bj[j] = (bias != nullptr && n < N) ? act_to_float<BF16>(braw[j]) : 0.f;
     }
   #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -718,13 +728,20 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float* __restric
                                                           int N, int splits, uint16_t* __restrict__ y) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= MN) return;
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  // The four bias values (n % 4 == 0: N is a multiple of 32) are requested first, so that
+  // they arrive with the partials: one memory round trip, not two.  Without a bias the
+  // load reads the first partial and is not used.
+  const int n = (int)(e % N);
+  const uint16_t* bsrc = bias != nullptr ? bias + n : reinterpret_cast<const uint16_t*>(partial);
+  const u32x2_t braw = *reinterpret_cast<const u32x2_t*>(bsrc);
+  __builtin_amdgcn_sched_barrier(0);
   floatx4 a = sum_splits<B>(partial + e, MN, splits);
   if (bias != nullptr) {
-    const int n = (int)(e % N);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] += act_to_float<BF16>(bias[n + j]);
+    for (int j = 0; j < 4; ++j)
+      a[j] += act_to_float<BF16>((uint16_t)(braw[j >> 1] >> (16 * (j & 1))));
   }
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   *reinterpret_cast<u32x2_t*>(y + e) = u32x2_t{pack_act2<BF16>(a[0], a[1]), pack_act2<BF16>(a[2], a[3])};
 }
 
