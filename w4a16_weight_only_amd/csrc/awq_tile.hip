@@ -100,9 +100,11 @@ __device__ __forceinline__ uint32_t b_pair(uint32_t magic_pair, half2v mult, hal
 template <int FM, int FN, int WM, int KG, bool BF16, bool GROUPED = false>
 __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales,
-    const uint16_t* __restrict__ bias, int M, int K, int N, int g, int m_tiles, int kps,
-    float* __restrict__ partial, uint16_t* __restrict__ y, MoeTiles moe) {
+    const uint32_t* __restrict__ qzeros, const _Float16* __restrict__ scales, int M, int K, int N,
+    int g, int m_tiles, int kps, const uint16_t* __restrict__ bias, float* __restrict__ partial,
+    uint16_t* __restrict__ y, MoeTiles moe) {
+  // Argument order: everything the prologue needs first, so that it falls in the 14
+  // dwords the dispatcher preloads into SGPRs (the rest is fetched from memory).
   constexpr int THREADS = 256 * KG;   // KG groups of 4 waves; group kg takes k16 steps of its share
   constexpr int WN = 4 / WM;          // waves along N
   constexpr int BM = WM * 32 * FM;    // workgroup rows
@@ -320,16 +322,6 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
     return __builtin_bit_cast(half2v, h | (h << 16));
   };
 
-  // Bias of this lane's output column(s) for the unsplit epilogue, requested before the k
-  // loop (the epilogue would otherwise wait a memory round trip for it after the last
-  // k-tile).  Without a bias, or with split partials, the loads read x and are unused.
-  uint16_t braw[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const bool use = bias != nullptr && partial == nullptr;
-    braw[j] = (use ? bias : x)[use ? min(n0 + (j == 0 ? c0 : c1), N - 1) : 0];
-  }
-
   half2v off0, off1, sc0, sc1;
   // Group data of half h of k-tile buf.  keep = false zeroes the scales (the unused half
   // of a partial last k-tile, whose MFMAs are skipped anyway).
@@ -446,6 +438,16 @@ __global__ __launch_bounds__(256 * KG, 1) void tile_kernel(
   };
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) load_tile(t, kofs(t));
+  // Bias of this lane's output column(s) for the unsplit epilogue, requested once the
+  // first k-tiles' loads are out (the epilogue would otherwise wait a memory round trip
+  // for it after the last k-tile).  Without a bias, or with split partials, the load
+  // reads x and is unused.
+  uint16_t braw[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const bool use = bias != nullptr && partial == nullptr;
+    braw[j] = (use ? bias : x)[use ? min(n0 + (j == 0 ? c0 : c1), N - 1) : 0];
+  }
   barrier_keep_last();
   if constexpr (KG == 2) {
     // Software-pipelined k loop: a wave's share of a k-tile is two k16 steps of one
@@ -754,7 +756,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const int32_t* qweight, const
     const int m_tiles = (M + bm - 1) / bm;
     hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks(m_tiles, N, bn), (unsigned)p.splits), dim3(threads), 0,
                        stream, x, reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<const uint32_t*>(qzeros),
-                       reinterpret_cast<const _Float16*>(scales), bias, M, K, N, g, m_tiles, p.kps,
+                       reinterpret_cast<const _Float16*>(scales), M, K, N, g, m_tiles, p.kps, bias,
                        split ? partial : nullptr, y, MoeTiles{});
   };
   switch (p.variant) {
@@ -786,8 +788,8 @@ hipError_t launch_tile_grouped(const uint16_t* x, const int32_t* qweight, const 
     m.hi = hi;
     hipLaunchKernelGGL(kern, dim3((unsigned)tile_blocks((int64_t)moe.tiles * sub, N, bn), 1u), dim3(threads), 0,
                        stream, x, reinterpret_cast<const uint32_t*>(qweight),
-                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), nullptr,
-                       0, K, N, g, 1, (K + kBK - 1) / kBK, nullptr, y, m);
+                       reinterpret_cast<const uint32_t*>(qzeros), reinterpret_cast<const _Float16*>(scales), 0, K,
+                       N, g, 1, (K + kBK - 1) / kBK, nullptr, nullptr, y, m);
   };
   // 256-row tables: two launches over the same table, the 256 x 128 tile on the
   // entries of at least 128 rows, then the 64 x 128 tile on the smaller ones (an
