@@ -424,17 +424,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void skinny_kernel(
     }
   }
   if constexpr (SINGLE) {
-    // Scale the group's sums; a single row only needs the first element of each.
+    // Scale the group's sums (all four rows of each entry: a per-entry branch on M == 1
+    // compiled to 32 branches here, on the path to the wave reduction).
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float sv = (float)((v >> 3) ? gs1[tab_col(v)] : gs0[tab_col(v)]);
       if constexpr (BF16) {
         const float zc = __builtin_bit_cast(float, zs[v]);
-        if (M == 1) part[v][0] = (part[v][0] - zc * sx[0]) * sv;
-        else part[v] = (part[v] - zc * sx) * sv;
+        part[v] = (part[v] - zc * sx) * sv;
       } else {
-        if (M == 1) part[v][0] *= sv;
-        else part[v] *= sv;
+        part[v] *= sv;
       }
     }
   } else {
