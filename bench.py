@@ -19,7 +19,8 @@ launch duration (HIP events on the launch stream over the timed region) against
 MI355X's peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the
 same workload (`cores`: the BLAS threads it used; `host_cores`: the cores this process
 may run on).  `read_ceiling` times a plain streaming read of the same byte count (for the
-headline and for every other bandwidth-bound workload);
+headline and for every other bandwidth-bound workload), and `launch_floor` an empty kernel
+of the same grid, i.e. what each dependent launch costs before any work;
 `secondary` repeats the timing (not the CPU leg) for every other workload, and for
 the large-M (tile family) ones also times the dequantize-then-dense alternative
 (awq_dequant_f16 + torch's fp16 GEMM) under the same protocol.
@@ -391,6 +392,47 @@ def read_ceiling(nbytes, torch, steps=400):
                 how="libawq_probe.so stream read of the same byte count, rotated, graph-replayed")
 
 
+def launch_floor(blocks, threads, torch, steps=400):
+    """Per-launch time of an empty kernel with the given grid, replayed from a HIP graph
+    like the timed steps: what each dependent launch costs on this device before any work
+    (the probe library's empty kernel)."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "w4a16_weight_only_amd", "libawq_probe.so"))
+    probe.awq_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.awq_probe_empty.restype = ctypes.c_int
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def go():
+        st = probe.awq_probe_empty(blocks, threads, sink.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"awq_probe_empty failed: {st}")
+
+    with torch.cuda.stream(stream):
+        go()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            go()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        replay(graph, stream)
+        ev0.record(stream)
+        ev1.record(stream)
+        stream.synchronize()
+    settle(graph, stream, torch)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        replay(graph, stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    return dict(blocks=blocks, threads=threads, us_per_launch=round(us, 3),
+                how="libawq_probe.so empty kernel of the same grid, graph-replayed")
+
+
 def summarize(r, steps):
     w = r["workload"]
     ab = w.algorithmic_bytes()
@@ -492,6 +534,8 @@ def main():
         "source_digest": digest,
     }
     out["read_ceiling"] = read_ceiling(w.algorithmic_bytes(), torch)
+    pg = r["plan"]
+    out["launch_floor"] = launch_floor(int(pg["grid"][0]) * int(pg["grid"][1]), int(pg["block"]), torch)
     if not args.no_secondary:
         # Every other workload once, shorter: parity-test shapes, reported for context.
         sec = []
@@ -505,6 +549,9 @@ def main():
                          plan=rs["plan"], roofline=rf)
             if rf["bound"] == "hbm":
                 entry["read_ceiling"] = read_ceiling(rs["workload"].algorithmic_bytes(), torch, steps=n_steps)
+                pg = rs["plan"]
+                entry["launch_floor"] = launch_floor(int(pg["grid"][0]) * int(pg["grid"][1]), int(pg["block"]), torch,
+                                                     steps=n_steps)
             if rs["plan"]["family"] == "tile":
                 dd = time_dequant_dense(name, n_steps, torch, awq, synth)
                 entry["dequant_then_dense_us"] = dd  # awq_dequant_f16 + hipBLASLt fp16 GEMM

@@ -1,4 +1,6 @@
-// Streaming-read probe, built as its own small library (not part of the AWQ C ABI):
+// Probes, built as their own small library (not part of the AWQ C ABI).
+//
+// Streaming-read probe:
 // reads a device buffer once with 16-byte nontemporal loads, one contiguous 16 KiB
 // chunk per workgroup, and stores a word only if the XOR of all data equals a magic
 // value (practically never).  Timed by the benchmark next to awq_gemm on the same
@@ -28,6 +30,13 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// Launch-floor probe: a grid of workgroups that do nothing.  Replayed back to back from a
+// graph, its per-launch time is what every dependent launch costs on this device before
+// any work: dispatch, wave launch and retirement, the end-of-kernel release.
+__global__ void empty_kernel(uint32_t* __restrict__ sink, int never) {
+  if (never == 1 && threadIdx.x == 0) sink[blockIdx.x] = 0u;  // the host passes 0
+}
+
 }  // namespace
 
 // bytes: multiple of 16; sink: at least ceil(bytes / 16384) words of device memory.
@@ -37,5 +46,13 @@ extern "C" int awq_probe_stream_read(const void* src, int64_t bytes, uint32_t* s
   const int64_t blocks = (bytes + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// blocks x threads workgroups of the empty kernel; sink: at least `blocks` words.
+extern "C" int awq_probe_empty(int64_t blocks, int threads, uint32_t* sink, hipStream_t stream) {
+  if (sink == nullptr || blocks <= 0 || blocks >= (int64_t(1) << 31) || threads <= 0 || threads > 1024)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(empty_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, sink, 0);
   return (int)hipGetLastError();
 }
