@@ -41,6 +41,23 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_the_bench_probes():
+    # The benchmark's read ceiling and launch floor come from this separate library (not
+    # part of the AWQ ABI); bad arguments are rejected before any launch.
+    path = os.path.join(ROOT, "w4a16_weight_only_amd", "libawq_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libawq_probe.so is not built; run `python -m w4a16_weight_only_amd.build`")
+    probe = ctypes.CDLL(path)
+    probe.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    probe.awq_probe_stream_read.restype = ctypes.c_int
+    probe.awq_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.awq_probe_empty.restype = ctypes.c_int
+    assert probe.awq_probe_stream_read(None, 16, None, None) != 0
+    assert probe.awq_probe_empty(0, 256, ctypes.c_void_p(16), None) != 0
+    assert probe.awq_probe_empty(1, 2048, ctypes.c_void_p(16), None) != 0
+    assert probe.awq_probe_empty(1, 256, None, None) != 0
+
+
 def test_status_strings(lib):
     for st in range(-6, 1):
         s = _lib.status_string(st)
